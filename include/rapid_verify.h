@@ -1,0 +1,195 @@
+/*
+ * rapid_verify -- the target model's speculative verification step for
+ * long-context decoding, for AMD Instinct MI355X (gfx950).
+ *
+ * The step has two halves.
+ *
+ * 1. Attention of the verify queries (the last committed token plus the draft
+ *    tokens, or the nodes of a draft tree) over the long history KV cache and
+ *    over the draft block itself.  Following the hybrid tree attention of the
+ *    LongSpec summary (gist.science, "LongSpec", section 2.3 "Fast Tree
+ *    Attention"), it is computed in two parts and merged:
+ *      spec_attn_prefix  -- unmasked attention over the history cache, split
+ *                           along the sequence into partial results (O, LSE);
+ *      spec_attn_block   -- attention among the draft rows under the causal
+ *                           or tree mask;
+ *      lse_merge         -- log-sum-exp merge of all partials.
+ *
+ * 2. RAPID's acceptance over the vocabulary (RAPID blog post,
+ *    leeon-k.github.io, sections 2.1, 2.3, 2.4; abeam.tech RAPID article,
+ *    "Key idea 1"):
+ *      rapid_accept      -- p = softmax(z/T), q = softmax(y/T),
+ *                           p_hat = softmax(z/T + eta*(q - p)); draft t is
+ *                           kept while r_t <= min(1, p_hat_t[x_t]/q_t[x_t]);
+ *                           at the first rejection a token is drawn from
+ *                           norm(max(p_hat - q, 0)) by inverse CDF with the
+ *                           caller's uniform; if every draft is kept, a bonus
+ *                           token is drawn from the last row's p.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor arguments are caller-owned DEVICE pointers (except
+ *   parent_host, which is host memory), dense row-major in the stated
+ *   shapes.  bf16 data are IEEE bfloat16 bit patterns.  Pointers to bf16 and
+ *   fp32 tensors must be 16-byte aligned.
+ * - The library allocates nothing, frees nothing, keeps no state between
+ *   calls and never synchronises.  Work is enqueued asynchronously on
+ *   `stream` (a hipStream_t; NULL is the null stream).  Calls on different
+ *   streams may run concurrently if their outputs do not overlap.
+ * - Every scalar and pointer argument is validated on the host before any
+ *   HIP call.  On a failed check the call returns a nonzero rv_status and
+ *   writes nothing.  A failed kernel launch returns RV_ERR_HIP (the HIP error
+ *   is cleared).  No C++ exception crosses this interface.
+ * - Device data are the caller's responsibility: seq_lens values are clamped
+ *   to [0, L_max]; a draft id outside [0, V) makes rapid_accept report
+ *   n_accept = -1 for that sequence; non-finite logits give unspecified
+ *   tokens but never an out-of-bounds access.
+ * - Results are bit-deterministic: no atomics, fixed reduction orders.
+ *
+ * Notation: B batch, Hq query heads, Hkv kv heads (Hq % Hkv == 0, query head
+ * h reads kv head h / (Hq/Hkv)), n block rows (gamma+1 for a chain, the node
+ * count for a tree), d head dim, L_max cache capacity per sequence, S number
+ * of history splits, gamma draft tokens, V vocabulary size.
+ */
+#ifndef RAPID_VERIFY_H
+#define RAPID_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RV_OK = 0,
+  RV_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  RV_ERR_SHAPE = 2,       /* a size is out of range or inconsistent           */
+  RV_ERR_UNSUPPORTED = 3, /* valid but not implemented (e.g. d not 64 or 128) */
+  RV_ERR_VALUE = 4,       /* a scalar is out of range (T <= 0, NaN eta, tree) */
+  RV_ERR_WORKSPACE = 5,   /* workspace too small                              */
+  RV_ERR_HIP = 6,         /* a HIP launch failed                              */
+  RV_ERR_ALIGNMENT = 7    /* a tensor pointer is not 16-byte aligned          */
+} rv_status;
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* rv_status_string(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int rv_version(void);
+
+/* Largest supported block size n, and largest (Hq/Hkv)*n rows per kv head. */
+#define RV_MAX_BLOCK_ROWS 64
+#define RV_MAX_GROUP_ROWS 256
+
+/*
+ * Choose the history split for spec_attn_prefix on this device class:
+ * writes *split_len (tokens per split, a multiple of 128) and *num_splits
+ * (S = ceil(max_seq_len / split_len), at least 1) so that the launch fills the
+ * MI355X's 256 compute units.  Pure host arithmetic, no HIP call.
+ */
+rv_status rv_prefix_default_split(int64_t max_seq_len, int B, int Hq, int Hkv, int n,
+                                  int d, int64_t* split_len, int* num_splits);
+
+/*
+ * spec_attn_prefix -- unmasked attention of every block row over the history
+ * cache, one normalised partial result per split (LongSpec summary, section
+ * 2.3: the history part needs no mask; the partials are merged by
+ * log-sum-exp).
+ *
+ *   q         bf16 [B, Hq, n, d]       block-row queries
+ *   k_cache   bf16 [B, Hkv, L_max, d]  history keys
+ *   v_cache   bf16 [B, Hkv, L_max, d]  history values
+ *   seq_lens  int32 [B] (device)       history length of each sequence
+ *   max_seq_len  host bound >= every seq_lens[b]; sizes the grid
+ *   sm_scale  score scale: s_j = sm_scale * <q, k_j>
+ *   split_len tokens per split (a positive multiple of 128)
+ *   num_splits S >= ceil(max_seq_len / split_len): capacity of the partials
+ *   o_part    fp32 [B, Hq, n, S, d]  out: sum_j softmax_split(s)_j v_j
+ *   lse_part  fp32 [B, Hq, n, S]     out: natural-log sum_j exp(s_j) over the
+ *                                    split; -inf (and o_part = 0) for a split
+ *                                    that holds no history token
+ * Split s of sequence b covers tokens [s*split_len, min((s+1)*split_len,
+ * seq_lens[b])).  Supports d in {64, 128}, n <= 64, (Hq/Hkv)*n <= 256.
+ */
+rv_status spec_attn_prefix(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* seq_lens, int64_t max_seq_len, int B, int Hq,
+                           int Hkv, int n, int d, int64_t L_max, float sm_scale,
+                           int64_t split_len, int num_splits, float* o_part, float* lse_part,
+                           void* stream);
+
+/*
+ * spec_attn_block -- attention of the block rows over the block's own keys
+ * under the speculative mask (LongSpec summary, section 2.3: only the few
+ * speculative tokens need a mask).
+ *
+ *   q            bf16 [B, Hq, n, d]
+ *   k_blk, v_blk bf16 [B, Hkv, n, d]   keys/values of the block rows
+ *   parent_host  HOST int32 [n] or NULL.  NULL: causal chain, row i sees
+ *                block rows j <= i.  Otherwise a tree shared by the batch:
+ *                parent_host[0] == -1 and 0 <= parent_host[i] < i; row i sees
+ *                itself and its ancestors.  Invalid trees -> RV_ERR_VALUE.
+ *   o_blk        fp32 [B, Hq, n, d]   out: normalised over the visible rows
+ *   lse_blk      fp32 [B, Hq, n]      out: natural-log sum exp of the scores
+ * Supports d in {64, 128}, 1 <= n <= 64.
+ */
+rv_status spec_attn_block(const void* q, const void* k_blk, const void* v_blk,
+                          const int32_t* parent_host, int B, int Hq, int Hkv, int n, int d,
+                          float sm_scale, float* o_blk, float* lse_blk, void* stream);
+
+/*
+ * lse_merge -- log-sum-exp merge of the S history partials and the block
+ * partial (LongSpec summary, section 2.3: the two parts' outputs are combined
+ * with the log-sum-exp trick).  With M = max_k LSE_k and a_k = exp(LSE_k-M):
+ *   out = sum_k a_k O_k / sum_k a_k,   lse_out = M + log sum_k a_k.
+ * Partials with LSE = -inf have weight 0.
+ *
+ *   o_part, lse_part  fp32 [B, Hq, n, S, d], [B, Hq, n, S]
+ *   o_blk, lse_blk    fp32 [B, Hq, n, d],    [B, Hq, n]
+ *   out               bf16 [B, Hq, n, d]  (round to nearest even)
+ *   lse_out           fp32 [B, Hq, n] or NULL
+ */
+rv_status lse_merge(const float* o_part, const float* lse_part, int S, const float* o_blk,
+                    const float* lse_blk, int B, int Hq, int n, int d, void* out,
+                    float* lse_out, void* stream);
+
+/* Bytes of device workspace rapid_accept needs for (B, gamma, V). */
+size_t rapid_accept_workspace_size(int B, int gamma, int V);
+
+/*
+ * rapid_accept -- RAPID's acceptance for B sequences (RAPID blog post,
+ * section 2.1 acceptance test and residual draw; section 2.3 acceptance
+ * against the full-context target; section 2.4 retrieval-augmented target
+ * p_hat used in place of p at inference).
+ *
+ *   z          fp32 [B, gamma+1, V]  target logits; row t scores the token
+ *                                    after block row t
+ *   y          fp32 [B, gamma, V]    draft logits of draft t
+ *   draft      int32 [B, gamma]      draft token ids x_t
+ *   r          fp32 [B, gamma]       acceptance uniforms in [0, 1)
+ *   u          fp32 [B, gamma+1]     sampling uniforms in [0, 1); u[b,t] is
+ *                                    used only for a draw at row t
+ *   T          temperature > 0 for both p and q;  eta  finite
+ *   n_accept   int32 [B]             out: number of leading accepted drafts
+ *                                    (-1 if a draft id is out of range)
+ *   out_tokens int32 [B, gamma+1]    out: x_0..x_{n-1}, then the drawn token,
+ *                                    then -1
+ *   ratio_out  fp32 [B, gamma] or NULL  out: min(1, p_hat_t[x_t]/q_t[x_t])
+ *   p_hat_out  fp32 [B, gamma, V] or NULL  out: p_hat for every draft row
+ *   workspace  device scratch of at least rapid_accept_workspace_size bytes
+ * The draw at row t picks the smallest id k (ascending) whose cumulative
+ * weight exceeds u_t * W, W the row's total weight; if rounding leaves no
+ * such id, the largest id of positive weight.  Supports gamma in [1, 63],
+ * V in [2, 2^22].
+ */
+rv_status rapid_accept(const float* z, const float* y, const int32_t* draft, const float* r,
+                       const float* u, int B, int gamma, int V, float T, float eta,
+                       int32_t* n_accept, int32_t* out_tokens, float* ratio_out,
+                       float* p_hat_out, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RAPID_VERIFY_H */

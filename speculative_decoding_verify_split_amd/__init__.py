@@ -1,0 +1,21 @@
+"""rapid_verify for AMD MI355X (gfx950): the target model's speculative
+verification step for long-context decoding -- split-KV history attention,
+masked draft-block attention, log-sum-exp merge, and RAPID's acceptance with
+the retrieval-augmented target -- as a C-ABI HIP library with a thin Python
+binding.  The library is loaded on first use and every call fails loudly if
+it has not been built.
+"""
+
+from .rapid_verify import (  # noqa: F401
+    LIB_PATH,
+    RapidVerifyError,
+    load_library,
+    lse_merge,
+    rapid_accept,
+    rapid_accept_workspace_size,
+    rv_prefix_default_split,
+    rv_status_string,
+    rv_version,
+    spec_attn_block,
+    spec_attn_prefix,
+)

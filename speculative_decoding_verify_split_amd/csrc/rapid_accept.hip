@@ -1,0 +1,491 @@
+// rapid_accept: RAPID's acceptance over the vocabulary (RAPID blog post,
+// leeon-k.github.io: section 2.1, the acceptance test r <= min(1, p(x)/q(x))
+// and the residual draw from norm(max(p - q, 0)); section 2.3, the test
+// against the full-context target; section 2.4, the retrieval-augmented target
+// p_hat = softmax(z/T + eta (q - p)) used in place of p at inference).
+//
+// Each row is a V-long fp32 stream (V ~ 1.3e5), so the pass is bandwidth-
+// and latency-bound; every row is cut into 4096-element chunks, one
+// 256-thread workgroup per chunk (16 contiguous elements per thread), and
+// cross-chunk results go through a small workspace:
+//   stats_kernel   (chunk, row, b): max and sum of 2^(x - max) of z/T (rows
+//                  0..gamma) and y/T (rows 0..gamma-1), base-2 units
+//   phat_kernel    (chunk, t, b):   the same for s = z/T + eta (q - p)
+//   decide_kernel  (chunk, b):      every chunk recomputes the gamma ratios
+//                  min(1, p_hat_t[x_t]/q_t[x_t]) and the first-reject cut t*;
+//                  chunk 0 writes n_accept, the accepted tokens and the
+//                  ratios; every chunk writes its share of the draw weights
+//                  (max(p_hat - q, 0) at t* < gamma, p_gamma otherwise) and,
+//                  on request, p_hat
+//   draw_kernel    (b):             inverse CDF with the caller's uniform:
+//                  chunk -> wave -> lane -> element, each level taking the
+//                  first unit whose running total exceeds the target
+// No atomics; every reduction has a fixed order, so results are bit-exact
+// run to run.
+
+#include "rv_device.h"
+#include "rv_internal.h"
+
+namespace rv {
+namespace {
+
+constexpr int TPB = kVocabThreads;
+constexpr int PER = kVocabPerThread;
+constexpr int CH = kVocabChunk;
+
+template <bool VEC>
+__device__ __forceinline__ void load_run(const float* __restrict__ row, int V, int start,
+                                         float (&x)[PER]) {
+  if (VEC && start + PER <= V) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(row + start);
+#pragma unroll
+    for (int j = 0; j < PER / 4; ++j) {
+      const f32x4 v = p[j];
+      x[4 * j + 0] = v[0];
+      x[4 * j + 1] = v[1];
+      x[4 * j + 2] = v[2];
+      x[4 * j + 3] = v[3];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) x[e] = (start + e < V) ? row[start + e] : 0.f;
+  }
+}
+
+__device__ float block_max(float v) {
+  __shared__ float sh[TPB / 64];
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float r = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
+  __syncthreads();
+  return r;
+}
+
+__device__ float block_sum(float v) {
+  __shared__ float sh[TPB / 64];
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const float r = (sh[0] + sh[1]) + (sh[2] + sh[3]);
+  __syncthreads();
+  return r;
+}
+
+// Base-2 log-sum-exp of a row from its per-chunk (max, sum) pairs, computed
+// by one wave; every lane returns the same value.
+__device__ float wave_combine(const float* __restrict__ st, int C) {
+  const int lane = threadIdx.x & 63;
+  float m = -INFINITY;
+  for (int c = lane; c < C; c += 64) m = fmaxf(m, st[2 * c]);
+  m = wave_max(m);
+  float l = 0.f;
+  for (int c = lane; c < C; c += 64) l += st[2 * c + 1] * exp2_hw(st[2 * c] - m);
+  l = wave_sum(l);
+  return m + log2_hw(l);
+}
+
+// p, q and s/ln2 of one vocabulary entry.  x2 = z/T/ln2, lz = log2 sum 2^x2,
+// likewise for y; s2 = (z/T + eta (q - p)) / ln2.
+__device__ __forceinline__ void pq_s(float zv, float yv, float invT2, float eta2, float lz,
+                                     float ly, float& p, float& q, float& s2) {
+  const float x2 = zv * invT2;
+  p = exp2_hw(x2 - lz);
+  q = exp2_hw(yv * invT2 - ly);
+  s2 = fmaf(eta2, q - p, x2);
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(TPB) void stats_kernel(const float* __restrict__ z,
+                                                    const float* __restrict__ y, int gamma, int V,
+                                                    float invT2, int C, float* __restrict__ zstat,
+                                                    float* __restrict__ ystat) {
+  const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+  const float* row;
+  float* dst;
+  if (r <= gamma) {
+    row = z + ((size_t)b * (gamma + 1) + r) * V;
+    dst = zstat + (((size_t)b * (gamma + 1) + r) * C + c) * 2;
+  } else {
+    const int t = r - gamma - 1;
+    row = y + ((size_t)b * gamma + t) * V;
+    dst = ystat + (((size_t)b * gamma + t) * C + c) * 2;
+  }
+  const int start = c * CH + threadIdx.x * PER;
+  float x[PER];
+  load_run<VEC>(row, V, start, x);
+  float tm = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    x[e] = (start + e < V) ? x[e] * invT2 : -INFINITY;
+    tm = fmaxf(tm, x[e]);
+  }
+  const float cm = block_max(tm);
+  float ts = 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) ts += exp2_hw(x[e] - cm);
+  const float cs = block_sum(ts);
+  if (threadIdx.x == 0) {
+    dst[0] = cm;
+    dst[1] = cs;
+  }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(TPB) void phat_kernel(const float* __restrict__ z,
+                                                   const float* __restrict__ y, int gamma, int V,
+                                                   float invT2, float eta2, int C,
+                                                   const float* __restrict__ zstat,
+                                                   const float* __restrict__ ystat,
+                                                   float* __restrict__ sstat) {
+  const int c = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
+  const float lz = wave_combine(zstat + ((size_t)b * (gamma + 1) + t) * C * 2, C);
+  const float ly = wave_combine(ystat + ((size_t)b * gamma + t) * C * 2, C);
+  const float* zrow = z + ((size_t)b * (gamma + 1) + t) * V;
+  const float* yrow = y + ((size_t)b * gamma + t) * V;
+  const int start = c * CH + threadIdx.x * PER;
+  float zx[PER], yx[PER];
+  load_run<VEC>(zrow, V, start, zx);
+  load_run<VEC>(yrow, V, start, yx);
+  float s2[PER];
+  float tm = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    float p, q, s;
+    pq_s(zx[e], yx[e], invT2, eta2, lz, ly, p, q, s);
+    s2[e] = (start + e < V) ? s : -INFINITY;
+    tm = fmaxf(tm, s2[e]);
+  }
+  const float cm = block_max(tm);
+  float ts = 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) ts += exp2_hw(s2[e] - cm);
+  const float cs = block_sum(ts);
+  if (threadIdx.x == 0) {
+    float* dst = sstat + (((size_t)b * gamma + t) * C + c) * 2;
+    dst[0] = cm;
+    dst[1] = cs;
+  }
+}
+
+// Row constants of one sequence, computed cooperatively into LDS.
+struct RowLse {
+  float lz[kMaxGamma + 1];
+  float ly[kMaxGamma];
+  float ls[kMaxGamma];
+};
+
+__device__ void row_constants(RowLse& rc, int b, int gamma, int C, const float* zstat,
+                              const float* ystat, const float* sstat, int only_row) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int t = wave; t <= gamma; t += TPB / 64) {
+    if (only_row >= 0 && t != only_row) continue;
+    const float vz = wave_combine(zstat + ((size_t)b * (gamma + 1) + t) * C * 2, C);
+    float vy = 0.f, vs = 0.f;
+    if (t < gamma) {
+      vy = wave_combine(ystat + ((size_t)b * gamma + t) * C * 2, C);
+      vs = wave_combine(sstat + ((size_t)b * gamma + t) * C * 2, C);
+    }
+    if (lane == 0) {
+      rc.lz[t] = vz;
+      if (t < gamma) {
+        rc.ly[t] = vy;
+        rc.ls[t] = vs;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Draw weight of one entry at row ts: max(p_hat - q, 0) (kind 0) or p_hat
+// (kind 1) for a rejected draft row, p_gamma for the bonus row.
+__device__ __forceinline__ float draw_weight(float zv, float yv, int ts, int gamma, int kind,
+                                             float invT2, float eta2, const RowLse& rc) {
+  if (ts == gamma) return exp2_hw(zv * invT2 - rc.lz[gamma]);
+  float p, q, s2;
+  pq_s(zv, yv, invT2, eta2, rc.lz[ts], rc.ly[ts], p, q, s2);
+  const float ph = exp2_hw(s2 - rc.ls[ts]);
+  return kind == 0 ? fmaxf(ph - q, 0.f) : ph;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(TPB) void decide_kernel(
+    const float* __restrict__ z, const float* __restrict__ y, const int32_t* __restrict__ draft,
+    const float* __restrict__ r, int gamma, int V, float invT2, float eta2, int C,
+    const float* __restrict__ zstat, const float* __restrict__ ystat,
+    const float* __restrict__ sstat, float* __restrict__ wsum, int32_t* __restrict__ tstar_ws,
+    int32_t* __restrict__ n_accept, int32_t* __restrict__ out_tokens,
+    float* __restrict__ ratio_out, float* __restrict__ p_hat_out) {
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ RowLse rc;
+  __shared__ int sh_ts;
+  row_constants(rc, b, gamma, C, zstat, ystat, sstat, -1);
+
+  if (wave == 0) {
+    bool bad = false, acc = true;
+    float ratio = 0.f;
+    if (lane < gamma) {
+      const int x = draft[(size_t)b * gamma + lane];
+      bad = (x < 0 || x >= V);
+      if (!bad) {
+        float p, q, s2;
+        pq_s(z[((size_t)b * (gamma + 1) + lane) * V + x], y[((size_t)b * gamma + lane) * V + x],
+             invT2, eta2, rc.lz[lane], rc.ly[lane], p, q, s2);
+        const float ph = exp2_hw(s2 - rc.ls[lane]);
+        ratio = fminf(1.0f, ph / q);
+        acc = r[(size_t)b * gamma + lane] <= ratio;
+      }
+    }
+    const uint64_t badm = __ballot(bad);
+    const uint64_t rej = __ballot(lane < gamma && !acc);
+    int ts = rej ? (int)__ffsll((long long)rej) - 1 : gamma;
+    if (badm) ts = -1;
+    if (lane == 0) sh_ts = ts;
+    if (c == 0) {
+      if (ratio_out != nullptr && lane < gamma)
+        ratio_out[(size_t)b * gamma + lane] = bad ? __builtin_nanf("") : ratio;
+      if (lane <= gamma)
+        out_tokens[(size_t)b * (gamma + 1) + lane] =
+            (lane < ts) ? draft[(size_t)b * gamma + lane] : -1;
+      if (lane == 0) {
+        n_accept[b] = ts;
+        tstar_ws[b] = ts;
+      }
+    }
+  }
+  __syncthreads();
+  const int ts = sh_ts;
+  const int start = c * CH + threadIdx.x * PER;
+
+  if (p_hat_out != nullptr) {
+    for (int t = 0; t < gamma; ++t) {
+      float zx[PER], yx[PER];
+      load_run<VEC>(z + ((size_t)b * (gamma + 1) + t) * V, V, start, zx);
+      load_run<VEC>(y + ((size_t)b * gamma + t) * V, V, start, yx);
+      float* dst = p_hat_out + ((size_t)b * gamma + t) * V;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        float p, q, s2;
+        pq_s(zx[e], yx[e], invT2, eta2, rc.lz[t], rc.ly[t], p, q, s2);
+        if (start + e < V) dst[start + e] = exp2_hw(s2 - rc.ls[t]);
+      }
+    }
+  }
+  if (ts < 0) return;  // uniform across the workgroup
+
+  float zx[PER], yx[PER];
+  load_run<VEC>(z + ((size_t)b * (gamma + 1) + ts) * V, V, start, zx);
+  if (ts < gamma)
+    load_run<VEC>(y + ((size_t)b * gamma + ts) * V, V, start, yx);
+  else
+#pragma unroll
+    for (int e = 0; e < PER; ++e) yx[e] = 0.f;
+  float w0 = 0.f, w1 = 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    if (start + e < V) {
+      w0 += draw_weight(zx[e], yx[e], ts, gamma, 0, invT2, eta2, rc);
+      w1 += draw_weight(zx[e], yx[e], ts, gamma, 1, invT2, eta2, rc);
+    }
+  }
+  const float W0 = block_sum(w0);
+  const float W1 = block_sum(w1);
+  if (threadIdx.x == 0) {
+    wsum[((size_t)b * C + c) * 2 + 0] = W0;
+    wsum[((size_t)b * C + c) * 2 + 1] = W1;
+  }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(TPB) void draw_kernel(
+    const float* __restrict__ z, const float* __restrict__ y, const float* __restrict__ u,
+    int gamma, int V, float invT2, float eta2, int C, const float* __restrict__ zstat,
+    const float* __restrict__ ystat, const float* __restrict__ sstat,
+    const float* __restrict__ wsum, const int32_t* __restrict__ tstar_ws,
+    int32_t* __restrict__ out_tokens) {
+  const int b = blockIdx.x;
+  const int ts = tstar_ws[b];
+  if (ts < 0) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ RowLse rc;
+  __shared__ int sh_chunk, sh_kind;
+  __shared__ float sh_tau;
+  __shared__ float wtot[TPB / 64];
+  row_constants(rc, b, gamma, C, zstat, ystat, sstat, ts);
+
+  if (threadIdx.x == 0) {
+    // Chunk level.  kind 1 (p_hat itself) only if a rejected row has no
+    // residual mass, which exact arithmetic rules out.
+    const float* ws = wsum + (size_t)b * C * 2;
+    float W = 0.f;
+    for (int c = 0; c < C; ++c) W += ws[2 * c];
+    int kind = 0;
+    if (!(W > 0.f)) {
+      kind = 1;
+      W = 0.f;
+      for (int c = 0; c < C; ++c) W += ws[2 * c + 1];
+    }
+    float tau = u[(size_t)b * (gamma + 1) + ts] * W;
+    float base = 0.f, last_base = 0.f;
+    int pick = -1, last = -1;
+    for (int c = 0; c < C; ++c) {
+      const float wc = ws[2 * c + kind];
+      if (wc > 0.f) {
+        if (base + wc > tau) {
+          pick = c;
+          break;
+        }
+        last = c;
+        last_base = base;
+      }
+      base += wc;
+    }
+    if (pick < 0) {  // rounding: take the last chunk with weight
+      pick = last < 0 ? 0 : last;
+      base = last_base;
+      tau = INFINITY;
+    }
+    sh_chunk = pick;
+    sh_kind = kind;
+    sh_tau = tau - base;
+  }
+  __syncthreads();
+  const int chunk = sh_chunk, kind = sh_kind;
+  const float tau_c = sh_tau;
+  const int start = chunk * CH + threadIdx.x * PER;
+  float zx[PER], yx[PER], w[PER];
+  load_run<VEC>(z + ((size_t)b * (gamma + 1) + ts) * V, V, start, zx);
+  if (ts < gamma)
+    load_run<VEC>(y + ((size_t)b * gamma + ts) * V, V, start, yx);
+  else
+#pragma unroll
+    for (int e = 0; e < PER; ++e) yx[e] = 0.f;
+  float tsum = 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    w[e] = (start + e < V) ? draw_weight(zx[e], yx[e], ts, gamma, kind, invT2, eta2, rc) : 0.f;
+    tsum += w[e];
+  }
+  // Inclusive scan of the thread totals inside each wave (fixed pattern).
+  float incl = tsum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wtot[wave] = incl;
+  __syncthreads();
+  // Wave level (same arithmetic in every thread).
+  float tau = tau_c, base = 0.f;
+  int wsel = -1, wlast = -1;
+  float wlast_base = 0.f;
+  for (int ww = 0; ww < TPB / 64; ++ww) {
+    const float wt = wtot[ww];
+    if (wt > 0.f) {
+      if (base + wt > tau) {
+        wsel = ww;
+        break;
+      }
+      wlast = ww;
+      wlast_base = base;
+    }
+    base += wt;
+  }
+  if (wsel < 0) {
+    wsel = wlast < 0 ? 0 : wlast;
+    base = wlast_base;
+    tau = INFINITY;
+  }
+  if (wave != wsel) return;
+  const float tau_w = tau - base;
+  // Lane level.
+  const uint64_t hit = __ballot(tsum > 0.f && incl > tau_w);
+  int lsel;
+  float tau_l;
+  const float excl = incl - tsum;
+  if (hit) {
+    lsel = (int)__ffsll((long long)hit) - 1;
+    tau_l = tau_w - __shfl(excl, lsel, 64);
+  } else {
+    const uint64_t pos = __ballot(tsum > 0.f);
+    lsel = pos ? 63 - (int)__builtin_clzll(pos) : 0;
+    tau_l = INFINITY;
+  }
+  if (lane != lsel) return;
+  // Element level.
+  float acc = 0.f;
+  int k = -1, klast = -1;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    if (w[e] > 0.f) {
+      if (k < 0 && acc + w[e] > tau_l) k = e;
+      klast = e;
+    }
+    acc += w[e];
+  }
+  if (k < 0) k = klast < 0 ? 0 : klast;
+  int tok = start + k;
+  if (tok >= V) tok = V - 1;
+  out_tokens[(size_t)b * (gamma + 1) + ts] = tok;
+}
+
+template <bool VEC>
+hipError_t launch_accept(const float* z, const float* y, const int32_t* draft, const float* r,
+                         const float* u, int B, int gamma, int V, float invT2, float eta2,
+                         const AcceptLayout& L, float* ws, int32_t* n_accept,
+                         int32_t* out_tokens, float* ratio_out, float* p_hat_out,
+                         hipStream_t s) {
+  const int C = L.chunks;
+  float* zstat = ws + L.zstat;
+  float* ystat = ws + L.ystat;
+  float* sstat = ws + L.sstat;
+  float* wsm = ws + L.wsum;
+  int32_t* tstar = reinterpret_cast<int32_t*>(ws + L.tstar);
+  hipLaunchKernelGGL((stats_kernel<VEC>), dim3(C, 2 * gamma + 1, B), dim3(TPB), 0, s, z, y, gamma,
+                     V, invT2, C, zstat, ystat);
+  hipLaunchKernelGGL((phat_kernel<VEC>), dim3(C, gamma, B), dim3(TPB), 0, s, z, y, gamma, V,
+                     invT2, eta2, C, zstat, ystat, sstat);
+  hipLaunchKernelGGL((decide_kernel<VEC>), dim3(C, B), dim3(TPB), 0, s, z, y, draft, r, gamma, V,
+                     invT2, eta2, C, zstat, ystat, sstat, wsm, tstar, n_accept, out_tokens,
+                     ratio_out, p_hat_out);
+  hipLaunchKernelGGL((draw_kernel<VEC>), dim3(B), dim3(TPB), 0, s, z, y, u, gamma, V, invT2, eta2,
+                     C, zstat, ystat, sstat, wsm, tstar, out_tokens);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace rv
+
+extern "C" size_t rapid_accept_workspace_size(int B, int gamma, int V) {
+  if (B < 1 || gamma < 1 || V < 2 || gamma > rv::kMaxGamma || V > rv::kMaxVocab) return 0;
+  return rv::accept_layout(B, gamma, V).words * 4;
+}
+
+extern "C" rv_status rapid_accept(const float* z, const float* y, const int32_t* draft,
+                                  const float* r, const float* u, int B, int gamma, int V,
+                                  float T, float eta, int32_t* n_accept, int32_t* out_tokens,
+                                  float* ratio_out, float* p_hat_out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  rv_status st = rv::check_accept(z, y, draft, r, u, B, gamma, V, T, eta, n_accept, out_tokens,
+                                  workspace, workspace_bytes);
+  if (st != RV_OK) return st;
+  const rv::AcceptLayout L = rv::accept_layout(B, gamma, V);
+  const double log2e = 1.4426950408889634;
+  const float invT2 = (float)(log2e / (double)T);
+  const float eta2 = (float)((double)eta * log2e);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* ws = static_cast<float*>(workspace);
+  hipError_t e;
+  if (V % 4 == 0)
+    e = rv::launch_accept<true>(z, y, draft, r, u, B, gamma, V, invT2, eta2, L, ws, n_accept,
+                                out_tokens, ratio_out, p_hat_out, s);
+  else
+    e = rv::launch_accept<false>(z, y, draft, r, u, B, gamma, V, invT2, eta2, L, ws, n_accept,
+                                 out_tokens, ratio_out, p_hat_out, s);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return RV_ERR_HIP;
+  }
+  return RV_OK;
+}

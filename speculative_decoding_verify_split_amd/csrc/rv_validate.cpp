@@ -1,0 +1,178 @@
+// Host-side argument validation and launch planning for rapid_verify.
+// This unit makes no HIP call, so every check can be exercised without a GPU.
+
+#include <math.h>
+#include <string.h>
+
+#include "rv_internal.h"
+
+namespace rv {
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+RowPlan row_plan(int Hq, int Hkv, int n) {
+  RowPlan p;
+  p.M = (Hq / Hkv) * n;
+  p.MT = ceil_div(p.M, 16);
+  p.RG = ceil_div(p.MT, kMaxTilesPerWave);
+  p.MTW = ceil_div(p.MT, p.RG);
+  return p;
+}
+
+static rv_status check_heads(int B, int Hq, int Hkv, int n, int d) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || n < 1) return RV_ERR_SHAPE;
+  if (Hq % Hkv != 0) return RV_ERR_SHAPE;
+  if (n > RV_MAX_BLOCK_ROWS) return RV_ERR_UNSUPPORTED;
+  if ((int64_t)(Hq / Hkv) * n > RV_MAX_GROUP_ROWS) return RV_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return RV_ERR_UNSUPPORTED;
+  return RV_OK;
+}
+
+rv_status check_prefix(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* seq_lens, int64_t max_seq_len, int B, int Hq, int Hkv,
+                       int n, int d, int64_t L_max, float sm_scale, int64_t split_len,
+                       int num_splits, const float* o_part, const float* lse_part) {
+  if (!q || !k_cache || !v_cache || !seq_lens || !o_part || !lse_part) return RV_ERR_NULL;
+  rv_status st = check_heads(B, Hq, Hkv, n, d);
+  if (st != RV_OK) return st;
+  if (L_max < 0 || max_seq_len < 0 || max_seq_len > L_max) return RV_ERR_SHAPE;
+  // buffer offsets inside one (sequence, kv-head) slab are 32-bit
+  if (L_max * (int64_t)d * 2 > (int64_t)0x7fffffff) return RV_ERR_UNSUPPORTED;
+  if (split_len <= 0 || split_len % kSplitQuantum != 0) return RV_ERR_SHAPE;
+  if (num_splits < 1 || num_splits > 65535) return RV_ERR_SHAPE;
+  if ((max_seq_len + split_len - 1) / split_len > num_splits) return RV_ERR_SHAPE;
+  if (!isfinite(sm_scale)) return RV_ERR_VALUE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o_part) ||
+      !aligned16(lse_part))
+    return RV_ERR_ALIGNMENT;
+  RowPlan rp = row_plan(Hq, Hkv, n);
+  if ((int64_t)Hkv * rp.RG > 65535 || B > 65535) return RV_ERR_UNSUPPORTED;
+  return RV_OK;
+}
+
+rv_status check_block(const void* q, const void* k_blk, const void* v_blk,
+                      const int32_t* parent_host, int B, int Hq, int Hkv, int n, int d,
+                      float sm_scale, const float* o_blk, const float* lse_blk, BlockMask* mask) {
+  if (!q || !k_blk || !v_blk || !o_blk || !lse_blk) return RV_ERR_NULL;
+  rv_status st = check_heads(B, Hq, Hkv, n, d);
+  if (st != RV_OK) return st;
+  if (!isfinite(sm_scale)) return RV_ERR_VALUE;
+  if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(o_blk) ||
+      !aligned16(lse_blk))
+    return RV_ERR_ALIGNMENT;
+  if ((int64_t)B * Hq > 0x7fffffff / 64) return RV_ERR_UNSUPPORTED;
+  BlockMask m;
+  memset(&m, 0, sizeof(m));
+  if (parent_host == nullptr) {
+    for (int i = 0; i < n; ++i) m.bits[i] = (i == 63) ? ~0ull : ((1ull << (i + 1)) - 1ull);
+  } else {
+    if (parent_host[0] != -1) return RV_ERR_VALUE;
+    m.bits[0] = 1ull;
+    for (int i = 1; i < n; ++i) {
+      int p = parent_host[i];
+      if (p < 0 || p >= i) return RV_ERR_VALUE;
+      // ancestors of i = ancestors of its parent (already final) plus i itself
+      m.bits[i] = m.bits[p] | (1ull << i);
+    }
+  }
+  if (mask) *mask = m;
+  return RV_OK;
+}
+
+rv_status check_merge(const float* o_part, const float* lse_part, int S, const float* o_blk,
+                      const float* lse_blk, int B, int Hq, int n, int d, const void* out) {
+  if (!o_part || !lse_part || !o_blk || !lse_blk || !out) return RV_ERR_NULL;
+  if (B < 1 || Hq < 1 || n < 1 || S < 1) return RV_ERR_SHAPE;
+  if (n > RV_MAX_BLOCK_ROWS) return RV_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return RV_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hq * n > 0x7fffffff / 4) return RV_ERR_UNSUPPORTED;
+  if (!aligned16(o_part) || !aligned16(lse_part) || !aligned16(o_blk) || !aligned16(lse_blk) ||
+      !aligned16(out))
+    return RV_ERR_ALIGNMENT;
+  return RV_OK;
+}
+
+static size_t round_words(size_t w) { return (w + 63) & ~(size_t)63; }  // 256-byte regions
+
+AcceptLayout accept_layout(int B, int gamma, int V) {
+  AcceptLayout L;
+  L.chunks = ceil_div(V, kVocabChunk);
+  size_t C = (size_t)L.chunks;
+  size_t off = 0;
+  L.zstat = off;
+  off += round_words((size_t)B * (gamma + 1) * C * 2);
+  L.ystat = off;
+  off += round_words((size_t)B * gamma * C * 2);
+  L.sstat = off;
+  off += round_words((size_t)B * gamma * C * 2);
+  L.wsum = off;
+  off += round_words((size_t)B * C * 2);
+  L.tstar = off;
+  off += round_words((size_t)B);
+  L.words = off;
+  return L;
+}
+
+rv_status check_accept(const float* z, const float* y, const int32_t* draft, const float* r,
+                       const float* u, int B, int gamma, int V, float T, float eta,
+                       const int32_t* n_accept, const int32_t* out_tokens, const void* workspace,
+                       size_t workspace_bytes) {
+  if (!z || !y || !draft || !r || !u || !n_accept || !out_tokens || !workspace)
+    return RV_ERR_NULL;
+  if (B < 1 || gamma < 1 || V < 2) return RV_ERR_SHAPE;
+  if (gamma > kMaxGamma || V > kMaxVocab || B > 65535) return RV_ERR_UNSUPPORTED;
+  if (!(T > 0.0f) || !isfinite(T) || !isfinite(eta)) return RV_ERR_VALUE;
+  if (!aligned16(z) || !aligned16(y) || !aligned16(workspace)) return RV_ERR_ALIGNMENT;
+  if (workspace_bytes < accept_layout(B, gamma, V).words * 4) return RV_ERR_WORKSPACE;
+  return RV_OK;
+}
+
+}  // namespace rv
+
+extern "C" {
+
+const char* rv_status_string(int status) {
+  switch (status) {
+    case RV_OK: return "RV_OK";
+    case RV_ERR_NULL: return "RV_ERR_NULL: a required pointer is NULL";
+    case RV_ERR_SHAPE: return "RV_ERR_SHAPE: a size is out of range or inconsistent";
+    case RV_ERR_UNSUPPORTED: return "RV_ERR_UNSUPPORTED: shape not supported by this library";
+    case RV_ERR_VALUE: return "RV_ERR_VALUE: a scalar or the tree is invalid";
+    case RV_ERR_WORKSPACE: return "RV_ERR_WORKSPACE: workspace too small";
+    case RV_ERR_HIP: return "RV_ERR_HIP: a HIP launch failed";
+    case RV_ERR_ALIGNMENT: return "RV_ERR_ALIGNMENT: a tensor pointer is not 16-byte aligned";
+    default: return "unknown rv_status";
+  }
+}
+
+int rv_version(void) { return 100; }
+
+rv_status rv_prefix_default_split(int64_t max_seq_len, int B, int Hq, int Hkv, int n, int d,
+                                  int64_t* split_len, int* num_splits) {
+  if (!split_len || !num_splits) return RV_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || n < 1 || Hq % Hkv != 0 || max_seq_len < 0)
+    return RV_ERR_SHAPE;
+  (void)d;
+  const int64_t q = rv::kSplitQuantum;
+  rv::RowPlan rp = rv::row_plan(Hq, Hkv, n);
+  const int64_t groups = (int64_t)B * Hkv * rp.RG;
+  const int64_t target_groups = 256;  // one 4-wave workgroup per compute unit
+  int64_t per = (max_seq_len * groups + target_groups - 1) / target_groups;
+  int64_t len = ((per + q - 1) / q) * q;
+  const int64_t min_len = 8 * q;  // at least 8 tiles per wave
+  if (len < min_len) len = min_len;
+  int64_t S = (max_seq_len + len - 1) / len;
+  if (S < 1) S = 1;
+  if (S > 65535) return RV_ERR_UNSUPPORTED;
+  *split_len = len;
+  *num_splits = (int)S;
+  return RV_OK;
+}
+
+}  // extern "C"

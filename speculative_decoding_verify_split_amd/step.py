@@ -1,0 +1,101 @@
+"""One verify step on the GPU: device buffers plus the four library calls.
+
+Plumbing only: torch allocates device memory and supplies the stream; every
+arithmetic step runs inside librapid_verify.so.
+"""
+
+import numpy as np
+
+from . import rapid_verify as rv
+
+
+def bf16_to_device(bits, device="cuda"):
+    """uint16 bf16 bit patterns (numpy) -> torch.bfloat16 tensor on the GPU."""
+    import torch
+    a = np.ascontiguousarray(bits).view(np.int16)
+    return torch.from_numpy(a).to(device).view(torch.bfloat16)
+
+
+def to_device(arr, device="cuda"):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+
+
+class VerifyStep:
+    """Device-resident inputs and outputs of one verify step.
+
+    attn: a workloads.AttnInputs-like object (numpy uint16 bf16 bits), or
+          None for the vocabulary pass only;
+    vocab: a workloads.VocabInputs-like object, or None for attention only.
+    split: (split_len, num_splits) or None for the library's default.
+    """
+
+    def __init__(self, attn, vocab=None, split=None, want_ratio=True, want_p_hat=False,
+                 device="cuda"):
+        import torch
+        self.device = device
+        self.attn = attn
+        f32 = torch.float32
+        if attn is not None:
+            B, Hq, n, d = attn.q.shape
+            Hkv, L_max = attn.k_cache.shape[1], attn.k_cache.shape[2]
+            self.B, self.Hq, self.Hkv, self.n, self.d, self.L_max = B, Hq, Hkv, n, d, L_max
+            self.max_seq_len = int(np.max(attn.seq_lens)) if B else 0
+            self.parent = None if attn.parent is None else [int(x) for x in attn.parent]
+            self.sm_scale = float(attn.sm_scale)
+            self.q = bf16_to_device(attn.q, device)
+            self.k_cache = bf16_to_device(attn.k_cache, device)
+            self.v_cache = bf16_to_device(attn.v_cache, device)
+            self.k_blk = bf16_to_device(attn.k_blk, device)
+            self.v_blk = bf16_to_device(attn.v_blk, device)
+            self.seq_lens = to_device(attn.seq_lens.astype(np.int32), device)
+            if split is None:
+                split = rv.rv_prefix_default_split(self.max_seq_len, B, Hq, Hkv, n, d)
+            self.split_len, self.num_splits = int(split[0]), int(split[1])
+            S = self.num_splits
+            self.o_part = torch.empty((B, Hq, n, S, d), dtype=f32, device=device)
+            self.lse_part = torch.empty((B, Hq, n, S), dtype=f32, device=device)
+            self.o_blk = torch.empty((B, Hq, n, d), dtype=f32, device=device)
+            self.lse_blk = torch.empty((B, Hq, n), dtype=f32, device=device)
+            self.out = torch.empty((B, Hq, n, d), dtype=torch.bfloat16, device=device)
+            self.lse_out = torch.empty((B, Hq, n), dtype=f32, device=device)
+        self.vocab = vocab
+        if vocab is not None:
+            Bv, g1, V = vocab.z.shape
+            self.gamma, self.V = g1 - 1, V
+            self.T, self.eta = float(vocab.T), float(vocab.eta)
+            self.z = to_device(vocab.z, device)
+            self.y = to_device(vocab.y, device)
+            self.draft = to_device(vocab.draft.astype(np.int32), device)
+            self.r = to_device(vocab.r, device)
+            self.u = to_device(vocab.u, device)
+            self.n_accept = torch.empty((Bv,), dtype=torch.int32, device=device)
+            self.out_tokens = torch.empty((Bv, g1), dtype=torch.int32, device=device)
+            ws = rv.rapid_accept_workspace_size(Bv, self.gamma, V)
+            self.workspace = torch.empty((ws,), dtype=torch.uint8, device=device)
+            self.ratio = torch.empty((Bv, self.gamma), dtype=f32, device=device) if want_ratio else None
+            self.p_hat = (torch.empty((Bv, self.gamma, V), dtype=f32, device=device)
+                          if want_p_hat else None)
+
+    def attention(self, k_cache=None, v_cache=None, stream=None):
+        """The three attention calls; k_cache/v_cache override the resident
+        cache (same shape), e.g. to rotate copies when timing."""
+        kc = self.k_cache if k_cache is None else k_cache
+        vc = self.v_cache if v_cache is None else v_cache
+        rv.spec_attn_prefix(self.q, kc, vc, self.seq_lens, self.max_seq_len, self.split_len,
+                            self.num_splits, self.o_part, self.lse_part, self.sm_scale, stream)
+        rv.spec_attn_block(self.q, self.k_blk, self.v_blk, self.parent, self.o_blk, self.lse_blk,
+                           self.sm_scale, stream)
+        rv.lse_merge(self.o_part, self.lse_part, self.o_blk, self.lse_blk, self.out, self.lse_out,
+                     stream)
+
+    def accept(self, z=None, y=None, stream=None):
+        rv.rapid_accept(self.z if z is None else z, self.y if y is None else y, self.draft, self.r,
+                        self.u, self.T, self.eta, self.n_accept, self.out_tokens, self.workspace,
+                        self.ratio, self.p_hat, stream)
+
+    def run(self, stream=None):
+        if self.attn is not None:
+            self.attention(stream=stream)
+        if self.vocab is not None:
+            self.accept(stream=stream)

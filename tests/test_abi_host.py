@@ -1,0 +1,184 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and rejects invalid arguments on the host before any HIP call
+(so no test here touches a device)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from speculative_decoding_verify_split_amd import rapid_verify as rv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rapid_verify.h")
+
+RV_OK, RV_ERR_NULL, RV_ERR_SHAPE, RV_ERR_UNSUPPORTED, RV_ERR_VALUE, RV_ERR_WORKSPACE = range(6)
+RV_ERR_HIP, RV_ERR_ALIGNMENT = 6, 7
+
+P = 0x10000  # a 16-byte aligned non-null address; never dereferenced (calls fail validation)
+MIS = 0x10004
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rv.LIB_PATH):
+        pytest.fail("librapid_verify.so is not built")
+    return rv.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:rv_status|size_t|const char\s*\*|int)\s+(\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("spec_attn_prefix", "spec_attn_block", "lse_merge", "rapid_accept",
+              "rapid_accept_workspace_size", "rv_status_string", "rv_prefix_default_split"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", rv.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = rv.rv_status_string(code)
+        assert s.startswith("RV_")
+    assert "unknown" in rv.rv_status_string(99)
+    assert rv.rv_version() >= 100
+
+
+def _prefix(lib, **kw):
+    a = dict(q=P, k=P, v=P, lens=P, max_seq_len=4096, B=1, Hq=8, Hkv=2, n=5, d=64, L_max=4096,
+             scale=1.0, split_len=1024, S=4, o=P, lse=P)
+    a.update(kw)
+    return lib.spec_attn_prefix(a["q"], a["k"], a["v"], a["lens"], a["max_seq_len"], a["B"],
+                                a["Hq"], a["Hkv"], a["n"], a["d"], a["L_max"], a["scale"],
+                                a["split_len"], a["S"], a["o"], a["lse"], None)
+
+
+def test_prefix_validation(lib):
+    assert _prefix(lib, q=None) == RV_ERR_NULL
+    assert _prefix(lib, lens=None) == RV_ERR_NULL
+    assert _prefix(lib, o=None) == RV_ERR_NULL
+    assert _prefix(lib, d=96) == RV_ERR_UNSUPPORTED
+    assert _prefix(lib, Hq=7) == RV_ERR_SHAPE
+    assert _prefix(lib, B=0) == RV_ERR_SHAPE
+    assert _prefix(lib, n=65) == RV_ERR_UNSUPPORTED
+    assert _prefix(lib, Hq=64, Hkv=1, n=5) == RV_ERR_UNSUPPORTED  # 320 rows per kv head
+    assert _prefix(lib, split_len=1000) == RV_ERR_SHAPE
+    assert _prefix(lib, split_len=0) == RV_ERR_SHAPE
+    assert _prefix(lib, S=3) == RV_ERR_SHAPE  # 4096 tokens need 4 splits of 1024
+    assert _prefix(lib, max_seq_len=5000) == RV_ERR_SHAPE  # beyond L_max
+    assert _prefix(lib, scale=float("nan")) == RV_ERR_VALUE
+    assert _prefix(lib, scale=float("inf")) == RV_ERR_VALUE
+    assert _prefix(lib, k=MIS) == RV_ERR_ALIGNMENT
+    assert _prefix(lib, lse=MIS) == RV_ERR_ALIGNMENT
+    assert _prefix(lib, L_max=1 << 24, max_seq_len=1 << 24, d=128, S=1 << 14) == RV_ERR_UNSUPPORTED
+
+
+def _block(lib, parent=None, **kw):
+    a = dict(q=P, k=P, v=P, B=1, Hq=8, Hkv=2, n=5, d=64, scale=1.0, o=P, lse=P)
+    a.update(kw)
+    par = None
+    if parent is not None:
+        arr = (ctypes.c_int32 * len(parent))(*parent)
+        par = ctypes.cast(arr, ctypes.c_void_p)
+    return lib.spec_attn_block(a["q"], a["k"], a["v"], par, a["B"], a["Hq"], a["Hkv"], a["n"],
+                               a["d"], a["scale"], a["o"], a["lse"], None)
+
+
+def test_block_validation(lib):
+    assert _block(lib, q=None) == RV_ERR_NULL
+    assert _block(lib, v=None) == RV_ERR_NULL
+    assert _block(lib, n=0) == RV_ERR_SHAPE
+    assert _block(lib, n=65) == RV_ERR_UNSUPPORTED
+    assert _block(lib, d=32) == RV_ERR_UNSUPPORTED
+    assert _block(lib, parent=[0, 0, 1, 2, 3]) == RV_ERR_VALUE      # root must be -1
+    assert _block(lib, parent=[-1, 0, 2, 1, 0]) == RV_ERR_VALUE     # parent not earlier
+    assert _block(lib, parent=[-1, 0, 1, -1, 0]) == RV_ERR_VALUE    # second root
+    assert _block(lib, o=MIS) == RV_ERR_ALIGNMENT
+    assert _block(lib, scale=float("nan")) == RV_ERR_VALUE
+
+
+def _merge(lib, **kw):
+    a = dict(o=P, l=P, S=4, ob=P, lb=P, B=1, Hq=8, n=5, d=64, out=P, lo=P)
+    a.update(kw)
+    return lib.lse_merge(a["o"], a["l"], a["S"], a["ob"], a["lb"], a["B"], a["Hq"], a["n"], a["d"],
+                         a["out"], a["lo"], None)
+
+
+def test_merge_validation(lib):
+    assert _merge(lib, o=None) == RV_ERR_NULL
+    assert _merge(lib, out=None) == RV_ERR_NULL
+    assert _merge(lib, S=0) == RV_ERR_SHAPE
+    assert _merge(lib, n=0) == RV_ERR_SHAPE
+    assert _merge(lib, d=256) == RV_ERR_UNSUPPORTED
+    assert _merge(lib, ob=MIS) == RV_ERR_ALIGNMENT
+
+
+def _accept(lib, **kw):
+    a = dict(z=P, y=P, x=P, r=P, u=P, B=1, g=4, V=32000, T=1.0, eta=0.5, n=P, tok=P, ratio=None,
+             ph=None, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return lib.rapid_accept(a["z"], a["y"], a["x"], a["r"], a["u"], a["B"], a["g"], a["V"], a["T"],
+                            a["eta"], a["n"], a["tok"], a["ratio"], a["ph"], a["ws"], a["wsb"],
+                            None)
+
+
+def test_accept_validation(lib):
+    assert _accept(lib, z=None) == RV_ERR_NULL
+    assert _accept(lib, u=None) == RV_ERR_NULL
+    assert _accept(lib, ws=None) == RV_ERR_NULL
+    assert _accept(lib, tok=None) == RV_ERR_NULL
+    assert _accept(lib, T=0.0) == RV_ERR_VALUE
+    assert _accept(lib, T=-1.0) == RV_ERR_VALUE
+    assert _accept(lib, T=float("inf")) == RV_ERR_VALUE
+    assert _accept(lib, T=float("nan")) == RV_ERR_VALUE
+    assert _accept(lib, eta=float("nan")) == RV_ERR_VALUE
+    assert _accept(lib, eta=float("-inf")) == RV_ERR_VALUE
+    assert _accept(lib, g=0) == RV_ERR_SHAPE
+    assert _accept(lib, g=64) == RV_ERR_UNSUPPORTED
+    assert _accept(lib, V=1) == RV_ERR_SHAPE
+    assert _accept(lib, V=(1 << 22) + 1) == RV_ERR_UNSUPPORTED
+    assert _accept(lib, B=0) == RV_ERR_SHAPE
+    need = rv.rapid_accept_workspace_size(1, 4, 32000)
+    assert _accept(lib, wsb=need - 1) == RV_ERR_WORKSPACE
+    assert _accept(lib, z=MIS) == RV_ERR_ALIGNMENT
+    assert _accept(lib, ws=MIS) == RV_ERR_ALIGNMENT
+
+
+def test_workspace_size_host_arithmetic(lib):
+    a = rv.rapid_accept_workspace_size(1, 10, 128256)
+    b = rv.rapid_accept_workspace_size(8, 10, 152064)
+    assert 0 < a < b
+    assert a % 256 == 0 and b % 256 == 0
+    assert rv.rapid_accept_workspace_size(0, 10, 100) == 0
+    assert rv.rapid_accept_workspace_size(1, 0, 100) == 0
+    assert rv.rapid_accept_workspace_size(1, 64, 100) == 0
+
+
+@pytest.mark.parametrize("L,B,Hq,Hkv,n,d", [(131072, 1, 32, 8, 11, 128), (122880, 1, 64, 8, 11, 128),
+                                            (131072, 8, 28, 4, 11, 128), (1048576, 1, 32, 8, 32, 128),
+                                            (4096, 1, 8, 2, 5, 64), (0, 1, 8, 2, 5, 64),
+                                            (1, 3, 4, 4, 1, 128)])
+def test_default_split_covers_the_sequence(lib, L, B, Hq, Hkv, n, d):
+    split_len, S = rv.rv_prefix_default_split(L, B, Hq, Hkv, n, d)
+    assert split_len % 128 == 0 and split_len > 0
+    assert S >= 1 and S * split_len >= L
+    assert (S - 1) * split_len < max(L, 1)
+    if L == 131072 and B == 1 and Hq == 32:
+        # 8 kv heads x 32 splits: one 4-wave workgroup per compute unit
+        assert (split_len, S) == (4096, 32)
