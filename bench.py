@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Verify-step benchmark on one MI355X.
+
+One step is the whole hot path on one batch of synthetic inputs:
+spec_attn_prefix (history pass over the KV cache), spec_attn_block (masked
+draft block), lse_merge, and rapid_accept (RAPID's vocabulary pass), back to
+back on one stream.  Default workload: the LLaMA-3.1-8B-shaped verify layer
+(32 query / 8 kv heads, d=128, 131072-token bf16 KV cache, gamma=10, vocab
+128256, T=1, eta=0.5), inputs resident in HBM.  Three copies of the KV cache
+and of the logits rotate from step to step so that no step reads what the
+previous one left in the 256 MB last-level cache.
+
+Prints one JSON line: steps/s (value), per-kernel device times from HIP
+events recorded on the library's stream inside the timed region, the
+KV-stream bandwidth, the roofline of the history kernel, and the fp64 CPU
+oracle timed on the host as a reported baseline.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "verify steps/s + KV-stream HBM GB/s, 8B-shaped layer, 128K ctx, gamma=10"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "spec_attn_prefix_llama8b_traffic.json")
+PREFIX_SRC = os.path.join(ROOT, "speculative_decoding_verify_split_amd", "csrc", "attn_prefix.hip")
+
+
+def _src_sha():
+    return hashlib.sha256(open(PREFIX_SRC, "rb").read()).hexdigest()
+
+
+def _traffic_per_launch():
+    """HBM bytes per history-kernel launch from the committed counter
+    summary, or None if it is missing or was taken on other kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != _src_sha():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _cpu_baseline(ai, vi, budget_s):
+    """Time the fp64 oracle on the host: full unsplit attention over every
+    head plus the step-by-step acceptance, repeated within the budget."""
+    from oracle import attn_ref, rapid_accept_ref
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: count the affinity mask
+        pass
+    if threads is None:
+        threads = len(os.sched_getaffinity(0))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        attn_ref(ai.q, ai.k_cache, ai.v_cache, ai.k_blk, ai.v_blk, ai.seq_lens, ai.parent,
+                 ai.sm_scale)
+        rapid_accept_ref(vi.z, vi.y, vi.draft, vi.r, vi.u, vi.T, vi.eta)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or reps >= 20:
+            break
+    return {"value": reps / el, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%d full verify step(s) of the same workload (all %d query heads over "
+                      "%d history tokens + vocabulary pass), %.1f s" %
+                      (reps, ai.q.shape[1], int(ai.seq_lens.max()), el)}
+
+
+def _calibrate_copy(n_bytes, reps):
+    """A plain device copy of known size, for scaling HBM counters."""
+    import torch
+    src = torch.empty(n_bytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": n_bytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama8b")
+    ap.add_argument("--eta", type=float, default=None)
+    ap.add_argument("--rotate", type=int, default=3)
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of host time for the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build measures one GPU only (no multi-GPU path); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        _calibrate_copy(args.calibrate_copy, max(1, args.steps))
+        return
+
+    from speculative_decoding_verify_split_amd import rapid_verify as rv
+    from speculative_decoding_verify_split_amd.step import VerifyStep
+    from workloads import CONFIGS, config_attention, config_vocab
+
+    cfg = CONFIGS[args.workload]
+    eta = cfg["etas"][min(1, len(cfg["etas"]) - 1)] if args.eta is None else args.eta
+    ai = config_attention(args.workload)
+    vi = config_vocab(args.workload, eta=eta)
+    st = VerifyStep(ai, vi, want_ratio=False, want_p_hat=False)
+    R = max(1, args.rotate)
+    kvs = [(st.k_cache, st.v_cache)] + [(st.k_cache.clone(), st.v_cache.clone())
+                                        for _ in range(R - 1)]
+    logits = [(st.z, st.y)] + [(st.z.clone(), st.y.clone()) for _ in range(R - 1)]
+
+    def step(i, ev=None):
+        kc, vc = kvs[i % R]
+        z, y = logits[i % R]
+        if ev is not None:
+            ev[0].record()
+        rv.spec_attn_prefix(st.q, kc, vc, st.seq_lens, st.max_seq_len, st.split_len,
+                            st.num_splits, st.o_part, st.lse_part, st.sm_scale)
+        if ev is not None:
+            ev[1].record()
+        rv.spec_attn_block(st.q, st.k_blk, st.v_blk, st.parent, st.o_blk, st.lse_blk, st.sm_scale)
+        rv.lse_merge(st.o_part, st.lse_part, st.o_blk, st.lse_blk, st.out, st.lse_out)
+        if ev is not None:
+            ev[2].record()
+        rv.rapid_accept(z, y, st.draft, st.r, st.u, st.T, st.eta, st.n_accept, st.out_tokens,
+                        st.workspace)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    prefix_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    attn_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    acc_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    step_dev_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    B, Hkv, d = st.B, st.Hkv, st.d
+    kv_bytes = int(2 * Hkv * d * 2 * int(np.sum(ai.seq_lens)))  # K and V, bf16
+    prefix_s = float(np.mean(prefix_ms)) / 1e3
+    attn_s = float(np.mean(attn_ms)) / 1e3
+    achieved = kv_bytes / prefix_s / 1e9
+    n_acc = st.n_accept.cpu().numpy()
+
+    line = {
+        "metric": METRIC,
+        "value": K / elapsed,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "dtype_detail": "attention: bf16 K/V/Q on MFMA with fp32 accumulation and softmax; "
+                        "vocabulary pass: fp32",
+        "data": "synthetic (seeded; K/V/Q ~ N(0,1) bf16, logits ~ N(0,9))",
+        "config": {"workload": cfg["desc"], "batch": B, "q_heads": st.Hq, "kv_heads": Hkv,
+                   "head_dim": d, "kv_tokens": int(np.max(ai.seq_lens)), "block_rows": st.n,
+                   "gamma": st.gamma, "vocab": st.V, "T": st.T, "eta": st.eta,
+                   "split_len": st.split_len, "num_splits": st.num_splits,
+                   "rotated_copies": R, "parallelism": "single GPU"},
+        "kv_stream_GBps": kv_bytes / attn_s / 1e9,
+        "kv_stream_frac_of_peak": kv_bytes / attn_s / 1e9 / HBM_PEAK_GBPS,
+        "kernels_us": {"spec_attn_prefix": prefix_s * 1e6,
+                       "spec_attn_block+lse_merge": (attn_s - prefix_s) * 1e6,
+                       "rapid_accept": float(np.mean(acc_ms)) * 1e3,
+                       "device_step": float(np.mean(step_dev_ms)) * 1e3},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": _traffic_per_launch(),
+                     "kernel": "spec_attn_prefix (history pass)",
+                     "algorithmic_bytes_per_launch": kv_bytes},
+        "mean_n_accept": float(np.mean(n_acc)),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = _cpu_baseline(ai, vi, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
