@@ -102,7 +102,7 @@ rv_status rv_prefix_default_split(int64_t max_seq_len, int B, int Hq, int Hkv, i
  *   v_cache   bf16 [B, Hkv, L_max, d]  history values
  *   seq_lens  int32 [B] (device)       history length of each sequence
  *   max_seq_len  host bound >= every seq_lens[b]; sizes the grid
- *   sm_scale  score scale: s_j = sm_scale * <q, k_j>
+ *   sm_scale  score scale, finite and > 0: s_j = sm_scale * <q, k_j>
  *   split_len tokens per split (a positive multiple of 128)
  *   num_splits S >= ceil(max_seq_len / split_len): capacity of the partials
  *   o_part    fp32 [B, Hq, n, S, d]  out: sum_j softmax_split(s)_j v_j
@@ -129,6 +129,7 @@ rv_status spec_attn_prefix(const void* q, const void* k_cache, const void* v_cac
  *                block rows j <= i.  Otherwise a tree shared by the batch:
  *                parent_host[0] == -1 and 0 <= parent_host[i] < i; row i sees
  *                itself and its ancestors.  Invalid trees -> RV_ERR_VALUE.
+ *   sm_scale     score scale, finite and > 0
  *   o_blk        fp32 [B, Hq, n, d]   out: normalised over the visible rows
  *   lse_blk      fp32 [B, Hq, n]      out: natural-log sum exp of the scores
  * Supports d in {64, 128}, 1 <= n <= 64.

@@ -24,6 +24,8 @@
 //   Loads use buffer resources bounded by the split's length, so keys past
 //   the split or the sequence read as zero and are masked to -inf.
 
+#include <type_traits>
+
 #include "rv_device.h"
 #include "rv_internal.h"
 
@@ -32,29 +34,73 @@ namespace {
 
 constexpr int KT = kKeysPerTile;
 constexpr int NW = kWavesPerGroup;
+// Slack, in base-2 units, before the running max of a row is raised.
+constexpr float kRescaleSlack = 8.0f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Max over the four lanes lr + 16 g (g = 0..3) that share a row, with the
+// gfx950 row-swap permutes (no LDS traffic).  Symmetric, so all four lanes
+// get the same value.
+__device__ __forceinline__ float row_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float row_sum4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 template <int D>
 struct PrefixGeom {
   static constexpr int KS = D / 32;             // MFMA k-steps over the head dim
   static constexpr int NB = D / 16;             // 16-column blocks of the output
   static constexpr int VCH = KT * D / 8 / 64;   // 16-byte V chunks per lane per tile
-  static constexpr int VROW = 2 * D + 8;        // bytes per key row of a V tile in LDS
+  static constexpr int VROW = 2 * D + 32;       // bytes per key row of a V tile in LDS
   static constexpr int VTILE = KT * VROW;       // bytes per wave V tile
   static constexpr int OROW = D + 4;            // floats per row of the merge buffer
 };
 
-template <int D, int MT>
-__global__ __launch_bounds__(NW * 64, 1) void prefix_kernel(
+// One 32-key tile in registers: K as MFMA A fragments, V as 16-byte chunks.
+template <int D>
+struct TileRegs {
+  i32x4 k[2][PrefixGeom<D>::KS];
+  i32x4 v[PrefixGeom<D>::VCH];
+};
+
+struct NoMask {};
+
+// BLOCK = false: history pass over split s of the cache (no mask).
+// BLOCK = true:  the draft block's own keys (one "split" holding all n block
+//                rows), with row i seeing block key j iff bit j of
+//                mask.bits[i] is set.
+template <int D, int MT, bool BLOCK>
+__global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ seq_lens, int Hq, int Hkv,
     int n, int64_t L_max, float scale_log2, int64_t split_len, int S, int RG,
-    float* __restrict__ o_part, float* __restrict__ lse_part) {
+    float* __restrict__ o_part, float* __restrict__ lse_part,
+    const typename std::conditional<BLOCK, BlockMask, NoMask>::type mask) {
   using Gm = PrefixGeom<D>;
   constexpr int KS = Gm::KS, NB = Gm::NB, VCH = Gm::VCH, VROW = Gm::VROW, OROW = Gm::OROW;
   constexpr int VBYTES = NW * Gm::VTILE;
   constexpr int OBYTES = MT * 16 * OROW * 4;
   constexpr int SMEM = VBYTES > OBYTES ? VBYTES : OBYTES;
+  // The widest shape keeps its query fragments in LDS to stay within 512
+  // registers per lane; the others keep them in registers.
+  constexpr bool kQLds = (D == 128 && MT == 4);
+  constexpr int QLDS_BYTES = kQLds ? MT * KS * 64 * 16 : 16;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  __shared__ __attribute__((aligned(16))) bf16x8 q_lds[QLDS_BYTES / 16];
   __shared__ float m_lds[MT * 16];
   __shared__ float l_lds[MT * 16];
 
@@ -71,8 +117,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefix_kernel(
   const int row0 = rg * MT * 16;
   const int rows_here = min(MT * 16, M - row0);
 
-  int64_t L = seq_lens[b];
-  L = L < 0 ? 0 : (L > L_max ? L_max : L);
+  int64_t L;
+  if constexpr (BLOCK) {
+    L = n;
+  } else {
+    L = seq_lens[b];
+    L = L < 0 ? 0 : (L > L_max ? L_max : L);
+  }
   const int64_t kbeg = (int64_t)s * split_len;
   int64_t kend = kbeg + split_len;
   if (kend > L) kend = L;
@@ -80,23 +131,41 @@ __global__ __launch_bounds__(NW * 64, 1) void prefix_kernel(
   const int ntiles = (nkeys + KT - 1) / KT;
 
   // Query fragments, B operand of S^T = K Q^T: lane (row lr, group lg) holds
-  // d = 32*ks + 8*lg .. +7 of its row.
-  bf16x8 qf[MT][KS];
+  // d = 32*ks + 8*lg .. +7 of its row.  In block mode each row also carries
+  // its visibility bits over the block keys.
+  bf16x8 qf[kQLds ? 1 : MT][KS];
+  uint64_t vis[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int row = row0 + mt * 16 + lr;
+    vis[mt] = ~0ull;
+    bf16x8 frag[KS];
     if (row < M) {
       const int gq = row / n;
       const int i = row - gq * n;
       const int h = kvh * G + gq;
+      if constexpr (BLOCK) vis[mt] = mask.bits[i];
       const uint16_t* qp = q + (((int64_t)b * Hq + h) * n + i) * D + lg * 8;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[mt][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
+      for (int ks = 0; ks < KS; ++ks) frag[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
     } else {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qf[mt][ks] = bf16x8{};
+      for (int ks = 0; ks < KS; ++ks) frag[ks] = bf16x8{};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if constexpr (kQLds) {
+        if (wave == 0) q_lds[(mt * KS + ks) * 64 + lane] = frag[ks];
+      } else {
+        qf[kQLds ? 0 : mt][ks] = frag[ks];
+      }
     }
   }
+  if constexpr (kQLds) __syncthreads();
+  auto qfrag = [&](int mt, int ks) -> bf16x8 {
+    if constexpr (kQLds) return q_lds[(mt * KS + ks) * 64 + lane];
+    else return qf[kQLds ? 0 : mt][ks];
+  };
 
   const size_t slab = ((size_t)b * Hkv + kvh) * (size_t)L_max * D + (size_t)kbeg * D;
   const uint32_t nbytes = (uint32_t)nkeys * D * 2;
@@ -116,36 +185,38 @@ __global__ __launch_bounds__(NW * 64, 1) void prefix_kernel(
   }
 
   unsigned char* vt = smem + wave * Gm::VTILE;
-  i32x4 kreg[2][KS], vreg[VCH];
 
-  auto load_tile = [&](int tt, i32x4(&kr)[2][KS], i32x4(&vr)[VCH]) {
+  // Loads past the split read zeros (buffer range check) and are never used.
+  auto load_tile = [&](int tt, TileRegs<D>& r) {
     const uint32_t base = (uint32_t)tt * KT * D * 2;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        kr[kb][ks] = buffer_load16(krs, base + (uint32_t)(((kb * 16 + lr) * D + ks * 32 + lg * 8) * 2));
+        r.k[kb][ks] = buffer_load16_stream(
+            krs, base + (uint32_t)(((kb * 16 + lr) * D + ks * 32 + lg * 8) * 2));
 #pragma unroll
-    for (int i = 0; i < VCH; ++i) vr[i] = buffer_load16(vrs, base + (uint32_t)((i * 64 + lane) * 16));
+    for (int i = 0; i < VCH; ++i)
+      r.v[i] = buffer_load16_stream(vrs, base + (uint32_t)((i * 64 + lane) * 16));
   };
 
-  int t = wave;
-  if (t < ntiles) load_tile(t, kreg, vreg);
-  for (; t < ntiles; t += NW) {
-    i32x4 knext[2][KS], vnext[VCH];
-    load_tile(t + NW, knext, vnext);  // past the split: reads zeros, never used
+  // Per-lane byte offsets into the wave's V tile for the transposed operand
+  // reads: in 16-lane group lg, source lane sl = 4 e + q points at
+  // V[key 16 h + 4 lg + e][16 nb + 4 q]; ds_read_b64_tr_b16 then hands lane
+  // (lr, lg) the four values V[16 h + 4 lg + e][16 nb + lr], e = 0..3.
+  const int sl = lane & 15;
+  const int vtr_off = (4 * lg + (sl >> 2)) * VROW + (sl & 3) * 8;
 
-    // Stage the V tile: chunk c = 64 i + lane is key c / (D/8), columns
-    // 8 (c % (D/8)) .. +7.
+  auto compute_tile = [&](const TileRegs<D>& r, int t) {
+    // Stage the V tile in its natural [key][d] layout: chunk c = 64 i + lane
+    // is key c / (D/8), columns 8 (c % (D/8)) .. +7.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
 #pragma unroll
     for (int i = 0; i < VCH; ++i) {
       const int c = i * 64 + lane;
       const int key = c / (D / 8);
       const int dch = c - key * (D / 8);
-      i32x2* dst = reinterpret_cast<i32x2*>(vt + key * VROW + dch * 16);
-      dst[0] = i32x2{vreg[i][0], vreg[i][1]};
-      dst[1] = i32x2{vreg[i][2], vreg[i][3]};
+      *reinterpret_cast<i32x4*>(vt + key * VROW + dch * 16) = r.v[i];
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
@@ -158,76 +229,125 @@ __global__ __launch_bounds__(NW * 64, 1) void prefix_kernel(
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, kreg[kb][ks]), qf[mt][ks], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.k[kb][ks]),
+                                                        qfrag(mt, ks), acc, 0, 0, 0);
         sacc[kb][mt] = acc;
       }
 
-    // Online softmax.  Lane (lr, lg) holds row lr's scores for keys
-    // 16 kb + 4 lg + v; the 4 lanes lr + 16 g share a row.
-    const int key0 = t * KT + lg * 4;
+    // Masking is needed only for a split's partial last tile (and always
+    // for the draft block's tree/causal mask).
+    const bool masked = BLOCK || (t + 1) * KT > nkeys;
+    if (masked) {
+      const int key0 = t * KT + lg * 4;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int kk = key0 + kb * 16 + v;
+            bool ok = kk < nkeys;
+            if constexpr (BLOCK) ok = ok && ((vis[mt] >> kk) & 1ull);
+            if (!ok) sacc[kb][mt][v] = -INFINITY;
+          }
+    }
+
+    // Online softmax with a lazily updated running max: row lr's scores for
+    // keys 16 kb + 4 lg + v live in lanes lr + 16 g.  The running max m_run
+    // (base-2 units) is raised only when a tile's max exceeds it by more
+    // than kRescaleSlack, so p = 2^(x - m_run) <= 2^kRescaleSlack and the
+    // accumulators are rescaled only on those rare tiles.
     bf16x8 pf[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      float x[8];
+      float mx = fmaxf(fmaxf(fmaxf(sacc[0][mt][0], sacc[0][mt][1]),
+                             fmaxf(sacc[0][mt][2], sacc[0][mt][3])),
+                       fmaxf(fmaxf(sacc[1][mt][0], sacc[1][mt][1]),
+                             fmaxf(sacc[1][mt][2], sacc[1][mt][3])));
+      mx = row_max4(mx);
+      const float m_tile = mx * scale_log2;
+      const bool raise = m_tile > m_run[mt] + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        const float m_new = raise ? m_tile : m_run[mt];
+        const float alpha = exp2_hw(m_run[mt] - m_new);
+        l_run[mt] *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) oacc[nb][mt] *= alpha;
+        m_run[mt] = m_new;
+      }
+      // A row with no visible key so far keeps an empty state.
+      const float neg_m = (m_run[mt] == -INFINITY) ? 0.f : -m_run[mt];
+      float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int kk = key0 + kb * 16 + v;
-          x[kb * 4 + v] = kk < nkeys ? sacc[kb][mt][v] * scale_log2 : -INFINITY;
+          const float p = exp2_hw(fmaf(sacc[kb][mt][v], scale_log2, neg_m));
+          ps += p;
+          pf[mt][kb * 4 + v] = (__bf16)p;
         }
-      float mx = x[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, x[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[mt], mx);
-      const float alpha = exp2_hw(m_run[mt] - m_new);
-      float ps = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = exp2_hw(x[e] - m_new);
-        ps += p;
-        pf[mt][e] = (__bf16)p;
-      }
-      l_run[mt] = l_run[mt] * alpha + ps;
-      m_run[mt] = m_new;
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) oacc[nb][mt] *= alpha;
+      l_run[mt] += ps;
     }
 
     // O^T += V^T P^T: A operand lane (column d = 16 nb + lr, group lg) holds
     // V[key][d] for keys 4 lg + e (e < 4) and 16 + 4 lg + (e - 4) (e >= 4),
-    // the same key order as pf.
+    // the same key order as pf; two transposed LDS reads per operand.
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      bf16x8 va;
-      const unsigned char* col = vt + (nb * 16 + lr) * 2;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = (e < 4) ? (lg * 4 + e) : (16 + lg * 4 + e - 4);
-        va[e] = *reinterpret_cast<const __bf16*>(col + key * VROW);
-      }
+      const unsigned char* base = vt + vtr_off + nb * 32;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(base));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4*)(base + 16 * VROW));
+      const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         oacc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[mt], oacc[nb][mt], 0, 0, 0);
     }
+  };
 
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kreg[kb][ks] = knext[kb][ks];
-#pragma unroll
-    for (int i = 0; i < VCH; ++i) vreg[i] = vnext[i];
+  // Register pipeline: while tile t is computed, the next tiles of this wave
+  // (t + NW, and t + 2 NW when registers allow) are in flight.
+  // (the draft block has at most one tile per wave; the widest shape would
+  // spill with a third buffer)
+  constexpr bool kDeep = !BLOCK && !(D == 128 && MT == 4);
+  TileRegs<D> ra, rb, rc;
+  int t = wave;
+  if (t < ntiles) {
+    load_tile(t, ra);
+    if constexpr (kDeep) {
+      load_tile(t + NW, rb);
+      for (;;) {
+        load_tile(t + 2 * NW, rc);
+        compute_tile(ra, t);
+        t += NW;
+        if (t >= ntiles) break;
+        load_tile(t + 2 * NW, ra);
+        compute_tile(rb, t);
+        t += NW;
+        if (t >= ntiles) break;
+        load_tile(t + 2 * NW, rb);
+        compute_tile(rc, t);
+        t += NW;
+        if (t >= ntiles) break;
+      }
+    } else {
+      for (;;) {
+        load_tile(t + NW, rb);
+        compute_tile(ra, t);
+        t += NW;
+        if (t >= ntiles) break;
+        load_tile(t + NW, ra);
+        compute_tile(rb, t);
+        t += NW;
+        if (t >= ntiles) break;
+      }
+    }
   }
 
   // Row sums: each lane holds a quarter of its row's keys.
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    l_run[mt] += __shfl_xor(l_run[mt], 16, 64);
-    l_run[mt] += __shfl_xor(l_run[mt], 32, 64);
-  }
+  for (int mt = 0; mt < MT; ++mt) l_run[mt] = row_sum4(l_run[mt]);
 
   // Merge the four waves' states through LDS, one wave at a time.
   __syncthreads();  // V tiles are dead; the buffer becomes the merge buffer
@@ -283,17 +403,39 @@ __global__ __launch_bounds__(NW * 64, 1) void prefix_kernel(
   }
 }
 
-template <int D, int MT>
-hipError_t launch_prefix(const void* q, const void* k, const void* v, const int32_t* seq_lens,
-                         int B, int Hq, int Hkv, int n, int64_t L_max, float scale_log2,
-                         int64_t split_len, int S, int RG, float* o_part, float* lse_part,
-                         hipStream_t stream) {
+template <int D, int MT, bool BLOCK, typename MaskT>
+hipError_t launch_attn(const void* q, const void* k, const void* v, const int32_t* seq_lens,
+                       int B, int Hq, int Hkv, int n, int64_t L_max, float scale_log2,
+                       int64_t split_len, int S, int RG, float* o_part, float* lse_part,
+                       const MaskT& mask, hipStream_t stream) {
   dim3 grid((unsigned)S, (unsigned)(Hkv * RG), (unsigned)B);
-  hipLaunchKernelGGL((prefix_kernel<D, MT>), grid, dim3(NW * 64), 0, stream,
+  hipLaunchKernelGGL((attn_kernel<D, MT, BLOCK>), grid, dim3(NW * 64), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), seq_lens, Hq, Hkv, n, L_max, scale_log2,
-                     split_len, S, RG, o_part, lse_part);
+                     split_len, S, RG, o_part, lse_part, mask);
   return hipGetLastError();
+}
+
+template <bool BLOCK, typename MaskT>
+rv_status dispatch_attn(int d, int MTW, const void* q, const void* k, const void* v,
+                        const int32_t* seq_lens, int B, int Hq, int Hkv, int n, int64_t L_max,
+                        float scale_log2, int64_t split_len, int S, int RG, float* o_part,
+                        float* lse_part, const MaskT& mask, hipStream_t s) {
+  hipError_t e;
+#define RV_ATTN_CASE(DD, MM)                                                                 \
+  if (d == DD && MTW == MM)                                                                  \
+    e = launch_attn<DD, MM, BLOCK>(q, k, v, seq_lens, B, Hq, Hkv, n, L_max, scale_log2,      \
+                                   split_len, S, RG, o_part, lse_part, mask, s);
+  RV_ATTN_CASE(64, 1)
+  else RV_ATTN_CASE(64, 2) else RV_ATTN_CASE(64, 3) else RV_ATTN_CASE(64, 4)
+  else RV_ATTN_CASE(128, 1) else RV_ATTN_CASE(128, 2) else RV_ATTN_CASE(128, 3)
+  else RV_ATTN_CASE(128, 4) else return RV_ERR_UNSUPPORTED;
+#undef RV_ATTN_CASE
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return RV_ERR_HIP;
+  }
+  return RV_OK;
 }
 
 }  // namespace
@@ -309,20 +451,28 @@ extern "C" rv_status spec_attn_prefix(const void* q, const void* k_cache, const 
   if (st != RV_OK) return st;
   const rv::RowPlan rp = rv::row_plan(Hq, Hkv, n);
   const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = hipSuccess;
-#define RV_PREFIX_CASE(DD, MM)                                                                  \
-  if (d == DD && rp.MTW == MM)                                                                  \
-    e = rv::launch_prefix<DD, MM>(q, k_cache, v_cache, seq_lens, B, Hq, Hkv, n, L_max,          \
-                                  scale_log2, split_len, num_splits, rp.RG, o_part, lse_part, s);
-  RV_PREFIX_CASE(64, 1)
-  else RV_PREFIX_CASE(64, 2) else RV_PREFIX_CASE(64, 3) else RV_PREFIX_CASE(64, 4)
-  else RV_PREFIX_CASE(128, 1) else RV_PREFIX_CASE(128, 2) else RV_PREFIX_CASE(128, 3)
-  else RV_PREFIX_CASE(128, 4) else return RV_ERR_UNSUPPORTED;
-#undef RV_PREFIX_CASE
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    return RV_ERR_HIP;
-  }
-  return RV_OK;
+  return rv::dispatch_attn<false>(d, rp.MTW, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, n, L_max,
+                                  scale_log2, split_len, num_splits, rp.RG, o_part, lse_part,
+                                  rv::NoMask{}, static_cast<hipStream_t>(stream));
+}
+
+// spec_attn_block: the draft block's keys under the causal or tree mask
+// (LongSpec summary, section 2.3: only the few speculative tokens need a
+// mask).  The block tensors [B, Hkv, n, d] have the cache's layout with
+// L_max = n, so the same MFMA kernel runs them as one split of n keys with a
+// per-row visibility mask; o_blk/lse_blk are the S = 1 partial layout.
+extern "C" rv_status spec_attn_block(const void* q, const void* k_blk, const void* v_blk,
+                                     const int32_t* parent_host, int B, int Hq, int Hkv, int n,
+                                     int d, float sm_scale, float* o_blk, float* lse_blk,
+                                     void* stream) {
+  rv::BlockMask mask;
+  rv_status st = rv::check_block(q, k_blk, v_blk, parent_host, B, Hq, Hkv, n, d, sm_scale, o_blk,
+                                 lse_blk, &mask);
+  if (st != RV_OK) return st;
+  const rv::RowPlan rp = rv::row_plan(Hq, Hkv, n);
+  const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  const int64_t split = ((n + rv::kSplitQuantum - 1) / rv::kSplitQuantum) * rv::kSplitQuantum;
+  return rv::dispatch_attn<true>(d, rp.MTW, q, k_blk, v_blk, nullptr, B, Hq, Hkv, n, n,
+                                 scale_log2, split, 1, rp.RG, o_blk, lse_blk, mask,
+                                 static_cast<hipStream_t>(stream));
 }

@@ -4,10 +4,11 @@
 // With M = max_k LSE_k and a_k = exp(LSE_k - M):
 //   O = sum_k a_k O_k / sum_k a_k,   LSE = M + log sum_k a_k.
 //
-// One wave per output row; the row's S partials are contiguous
-// ([row][S][d]), so each step reads one 4*d-byte line with all 64 lanes.
-// Partials are combined in a fixed order (splits ascending, then the block),
-// so the result is bit-deterministic.
+// One 4-wave workgroup per output row; the row's S partials are contiguous
+// ([row][S][d]).  Wave w folds splits w, w + 4, ... (each step one 4*d-byte
+// line read by all 64 lanes, four steps in flight), the four wave sums are
+// added in wave order and the block partial last, so the result is
+// bit-deterministic.
 
 #include "rv_device.h"
 #include "rv_internal.h"
@@ -19,13 +20,16 @@ template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_part,
                                                     const float* __restrict__ lse_part, int S,
                                                     const float* __restrict__ o_blk,
-                                                    const float* __restrict__ lse_blk, int rows,
+                                                    const float* __restrict__ lse_blk,
                                                     uint16_t* __restrict__ out,
                                                     float* __restrict__ lse_out) {
   constexpr int PER = D / 64;
+  constexpr int NWV = 4;
+  __shared__ float part[NWV][D];
+  __shared__ float wpart[NWV];
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  const int wave = threadIdx.x >> 6;
+  const int row = blockIdx.x;
   const float* lp = lse_part + (size_t)row * S;
   float M = -INFINITY;
   for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[s]);
@@ -37,15 +41,16 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   float wsum = 0.f;
   if (M != -INFINITY) {
+    // wave w folds splits w, w + 4, w + 8, ... in ascending order
     const float* op = o_part + (size_t)row * S * D + lane * PER;
-    int s = 0;
-    for (; s + 4 <= S; s += 4) {
+    int s = wave;
+    for (; s + 3 * NWV < S; s += 4 * NWV) {
       float a[4], val[4][PER];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        a[j] = exp2_hw((lp[s + j] - M) * kLog2e);
+        a[j] = exp2_hw((lp[s + j * NWV] - M) * kLog2e);
 #pragma unroll
-        for (int e = 0; e < PER; ++e) val[j][e] = op[(size_t)(s + j) * D + e];
+        for (int e = 0; e < PER; ++e) val[j][e] = op[(size_t)(s + j * NWV) * D + e];
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -54,24 +59,38 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
         for (int e = 0; e < PER; ++e) acc[e] = fmaf(a[j], val[j][e], acc[e]);
       }
     }
-    for (; s < S; ++s) {
+    for (; s < S; s += NWV) {
       const float a = exp2_hw((lp[s] - M) * kLog2e);
       wsum += a;
 #pragma unroll
       for (int e = 0; e < PER; ++e) acc[e] = fmaf(a, op[(size_t)s * D + e], acc[e]);
     }
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) part[wave][lane * PER + e] = acc[e];
+  if (lane == 0) wpart[wave] = wsum;
+  __syncthreads();
+  if (wave != 0) return;
+  float tot = ((wpart[0] + wpart[1]) + wpart[2]) + wpart[3];
+  float res[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int c = lane * PER + e;
+    res[e] = ((part[0][c] + part[1][c]) + part[2][c]) + part[3][c];
+  }
+  if (M != -INFINITY) {
     const float a = exp2_hw((lb - M) * kLog2e);
-    wsum += a;
+    tot += a;
     const float* bp = o_blk + (size_t)row * D + lane * PER;
 #pragma unroll
-    for (int e = 0; e < PER; ++e) acc[e] = fmaf(a, bp[e], acc[e]);
+    for (int e = 0; e < PER; ++e) res[e] = fmaf(a, bp[e], res[e]);
   }
-  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  const float inv = tot > 0.f ? 1.0f / tot : 0.f;
   uint16_t* dst = out + (size_t)row * D + lane * PER;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) dst[e] = f32_to_bf16_bits(acc[e] * inv);
+  for (int e = 0; e < PER; ++e) dst[e] = f32_to_bf16_bits(res[e] * inv);
   if (lse_out != nullptr && lane == 0)
-    lse_out[row] = (M == -INFINITY) ? -INFINITY : M + log2_hw(wsum) * kLn2;
+    lse_out[row] = (M == -INFINITY) ? -INFINITY : M + log2_hw(tot) * kLn2;
 }
 
 }  // namespace
@@ -84,14 +103,14 @@ extern "C" rv_status lse_merge(const float* o_part, const float* lse_part, int S
   if (st != RV_OK) return st;
   const int rows = B * Hq * n;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  dim3 grid((unsigned)((rows + 3) / 4));
+  dim3 grid((unsigned)rows);
   uint16_t* o16 = static_cast<uint16_t*>(out);
   if (d == 64)
     hipLaunchKernelGGL((rv::merge_kernel<64>), grid, dim3(256), 0, s, o_part, lse_part, S, o_blk,
-                       lse_blk, rows, o16, lse_out);
+                       lse_blk, o16, lse_out);
   else
     hipLaunchKernelGGL((rv::merge_kernel<128>), grid, dim3(256), 0, s, o_part, lse_part, S, o_blk,
-                       lse_blk, rows, o16, lse_out);
+                       lse_blk, o16, lse_out);
   if (hipGetLastError() != hipSuccess) return RV_ERR_HIP;
   return RV_OK;
 }

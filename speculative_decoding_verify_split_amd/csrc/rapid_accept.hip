@@ -72,16 +72,30 @@ __device__ float block_sum(float v) {
   return r;
 }
 
-// Base-2 log-sum-exp of a row from its per-chunk (max, sum) pairs, computed
-// by one wave; every lane returns the same value.
-__device__ float wave_combine(const float* __restrict__ st, int C) {
-  const int lane = threadIdx.x & 63;
-  float m = -INFINITY;
-  for (int c = lane; c < C; c += 64) m = fmaxf(m, st[2 * c]);
-  m = wave_max(m);
-  float l = 0.f;
-  for (int c = lane; c < C; c += 64) l += st[2 * c + 1] * exp2_hw(st[2 * c] - m);
-  l = wave_sum(l);
+// Merge two (max, sum-of-2^(x - max)) pairs.  Symmetric in its arguments, so
+// both lanes of a butterfly step obtain bit-identical results.
+__device__ __forceinline__ void lse_pair_merge(float& m, float& l, float mo, float lo) {
+  const float mn = fmaxf(m, mo);
+  const float a = (m == -INFINITY) ? 0.f : l * exp2_hw(m - mn);
+  const float c = (mo == -INFINITY) ? 0.f : lo * exp2_hw(mo - mn);
+  l = a + c;
+  m = mn;
+}
+
+// Base-2 log-sum-exp of a row from its per-chunk (max, sum) pairs, reduced by
+// a group of `width` lanes (a power of two <= 64) in one pass: lane j of the
+// group folds chunks j, j + width, ... in order, then the group merges by
+// butterfly.  Every lane of the group returns the same value.
+template <int width>
+__device__ __forceinline__ float group_combine(const float* __restrict__ st, int C, int j) {
+  float m = -INFINITY, l = 0.f;
+  for (int c = j; c < C; c += width) lse_pair_merge(m, l, st[2 * c], st[2 * c + 1]);
+#pragma unroll
+  for (int o = width / 2; o >= 1; o >>= 1) {
+    const float mo = __shfl_xor(m, o, 64);
+    const float lo = __shfl_xor(l, o, 64);
+    lse_pair_merge(m, l, mo, lo);
+  }
   return m + log2_hw(l);
 }
 
@@ -131,22 +145,48 @@ __global__ __launch_bounds__(TPB) void stats_kernel(const float* __restrict__ z,
   }
 }
 
+// grid (C, gamma + 1, B).  Rows t < gamma: chunk stats of s; chunk 0 also
+// publishes the row's z and y log-sum-exps.  Row gamma: chunk 0 publishes
+// the last target row's log-sum-exp (for the bonus draw).
 template <bool VEC>
 __global__ __launch_bounds__(TPB) void phat_kernel(const float* __restrict__ z,
                                                    const float* __restrict__ y, int gamma, int V,
                                                    float invT2, float eta2, int C,
                                                    const float* __restrict__ zstat,
                                                    const float* __restrict__ ystat,
-                                                   float* __restrict__ sstat) {
+                                                   float* __restrict__ sstat,
+                                                   float* __restrict__ rowtab) {
   const int c = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
-  const float lz = wave_combine(zstat + ((size_t)b * (gamma + 1) + t) * C * 2, C);
-  const float ly = wave_combine(ystat + ((size_t)b * gamma + t) * C * 2, C);
+  const int lane = threadIdx.x & 63;
+  float* rt = rowtab + (size_t)b * 3 * (gamma + 1);
+  if (t == gamma) {
+    if (c == 0 && threadIdx.x < 64) {
+      const float lz = group_combine<64>(zstat + ((size_t)b * (gamma + 1) + t) * C * 2, C, lane);
+      if (lane == 0) rt[t] = lz;
+    }
+    return;
+  }
+  __shared__ float sh_l[2];
+  if (threadIdx.x < 64) {
+    const float lz = group_combine<64>(zstat + ((size_t)b * (gamma + 1) + t) * C * 2, C, lane);
+    const float ly = group_combine<64>(ystat + ((size_t)b * gamma + t) * C * 2, C, lane);
+    if (lane == 0) {
+      sh_l[0] = lz;
+      sh_l[1] = ly;
+      if (c == 0) {
+        rt[t] = lz;
+        rt[(gamma + 1) + t] = ly;
+      }
+    }
+  }
   const float* zrow = z + ((size_t)b * (gamma + 1) + t) * V;
   const float* yrow = y + ((size_t)b * gamma + t) * V;
   const int start = c * CH + threadIdx.x * PER;
   float zx[PER], yx[PER];
   load_run<VEC>(zrow, V, start, zx);
   load_run<VEC>(yrow, V, start, yx);
+  __syncthreads();
+  const float lz = sh_l[0], ly = sh_l[1];
   float s2[PER];
   float tm = -INFINITY;
 #pragma unroll
@@ -168,34 +208,12 @@ __global__ __launch_bounds__(TPB) void phat_kernel(const float* __restrict__ z,
   }
 }
 
-// Row constants of one sequence, computed cooperatively into LDS.
+// Row constants of one sequence in LDS: base-2 LSEs of z/T, y/T and s.
 struct RowLse {
   float lz[kMaxGamma + 1];
   float ly[kMaxGamma];
   float ls[kMaxGamma];
 };
-
-__device__ void row_constants(RowLse& rc, int b, int gamma, int C, const float* zstat,
-                              const float* ystat, const float* sstat, int only_row) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int t = wave; t <= gamma; t += TPB / 64) {
-    if (only_row >= 0 && t != only_row) continue;
-    const float vz = wave_combine(zstat + ((size_t)b * (gamma + 1) + t) * C * 2, C);
-    float vy = 0.f, vs = 0.f;
-    if (t < gamma) {
-      vy = wave_combine(ystat + ((size_t)b * gamma + t) * C * 2, C);
-      vs = wave_combine(sstat + ((size_t)b * gamma + t) * C * 2, C);
-    }
-    if (lane == 0) {
-      rc.lz[t] = vz;
-      if (t < gamma) {
-        rc.ly[t] = vy;
-        rc.ls[t] = vs;
-      }
-    }
-  }
-  __syncthreads();
-}
 
 // Draw weight of one entry at row ts: max(p_hat - q, 0) (kind 0) or p_hat
 // (kind 1) for a rejected draft row, p_gamma for the bonus row.
@@ -208,19 +226,34 @@ __device__ __forceinline__ float draw_weight(float zv, float yv, int ts, int gam
   return kind == 0 ? fmaxf(ph - q, 0.f) : ph;
 }
 
+// grid (C, B).  Every chunk recomputes the row LSEs of s (16 lanes per row,
+// all rows at once), the ratios and the first-reject cut, then writes its
+// share of the draw weights; chunk 0 writes the per-sequence outputs.
 template <bool VEC>
 __global__ __launch_bounds__(TPB) void decide_kernel(
     const float* __restrict__ z, const float* __restrict__ y, const int32_t* __restrict__ draft,
     const float* __restrict__ r, int gamma, int V, float invT2, float eta2, int C,
-    const float* __restrict__ zstat, const float* __restrict__ ystat,
-    const float* __restrict__ sstat, float* __restrict__ wsum, int32_t* __restrict__ tstar_ws,
-    int32_t* __restrict__ n_accept, int32_t* __restrict__ out_tokens,
-    float* __restrict__ ratio_out, float* __restrict__ p_hat_out) {
+    const float* __restrict__ sstat, float* __restrict__ rowtab, float* __restrict__ wsum,
+    int32_t* __restrict__ tstar_ws, int32_t* __restrict__ n_accept,
+    int32_t* __restrict__ out_tokens, float* __restrict__ ratio_out,
+    float* __restrict__ p_hat_out) {
   const int c = blockIdx.x, b = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   __shared__ RowLse rc;
   __shared__ int sh_ts;
-  row_constants(rc, b, gamma, C, zstat, ystat, sstat, -1);
+  float* rt = rowtab + (size_t)b * 3 * (gamma + 1);
+  for (int i = threadIdx.x; i <= gamma; i += TPB) {
+    rc.lz[i] = rt[i];
+    if (i < gamma) rc.ly[i] = rt[(gamma + 1) + i];
+  }
+  {
+    const int grp = threadIdx.x >> 4, j = threadIdx.x & 15;
+    for (int t = grp; t < gamma; t += TPB / 16) {
+      const float ls = group_combine<16>(sstat + ((size_t)b * gamma + t) * C * 2, C, j);
+      if (j == 0) rc.ls[t] = ls;
+    }
+  }
+  __syncthreads();
 
   if (wave == 0) {
     bool bad = false, acc = true;
@@ -248,6 +281,7 @@ __global__ __launch_bounds__(TPB) void decide_kernel(
       if (lane <= gamma)
         out_tokens[(size_t)b * (gamma + 1) + lane] =
             (lane < ts) ? draft[(size_t)b * gamma + lane] : -1;
+      if (lane < gamma) rt[2 * (gamma + 1) + lane] = rc.ls[lane];
       if (lane == 0) {
         n_accept[b] = ts;
         tstar_ws[b] = ts;
@@ -297,40 +331,54 @@ __global__ __launch_bounds__(TPB) void decide_kernel(
   }
 }
 
+// grid (B).  Inverse CDF of the draw row with the caller's uniform:
+// chunk -> wave -> lane -> element, each level taking the first unit of
+// positive weight whose running total exceeds the target; if rounding leaves
+// none, the last unit of positive weight (and every lower level then takes
+// its last positive unit, i.e. the largest id of positive weight).
 template <bool VEC>
 __global__ __launch_bounds__(TPB) void draw_kernel(
     const float* __restrict__ z, const float* __restrict__ y, const float* __restrict__ u,
-    int gamma, int V, float invT2, float eta2, int C, const float* __restrict__ zstat,
-    const float* __restrict__ ystat, const float* __restrict__ sstat,
+    int gamma, int V, float invT2, float eta2, int C, const float* __restrict__ rowtab,
     const float* __restrict__ wsum, const int32_t* __restrict__ tstar_ws,
     int32_t* __restrict__ out_tokens) {
   const int b = blockIdx.x;
-  const int ts = tstar_ws[b];
-  if (ts < 0) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   __shared__ RowLse rc;
   __shared__ int sh_chunk, sh_kind;
   __shared__ float sh_tau;
   __shared__ float wtot[TPB / 64];
-  row_constants(rc, b, gamma, C, zstat, ystat, sstat, ts);
+  extern __shared__ float wsh[];  // [C][2]
+  const int ts = tstar_ws[b];
+  if (ts < 0) return;  // uniform
+  const float* rt = rowtab + (size_t)b * 3 * (gamma + 1);
+  for (int i = threadIdx.x; i <= gamma; i += TPB) {
+    rc.lz[i] = rt[i];
+    if (i < gamma) {
+      rc.ly[i] = rt[(gamma + 1) + i];
+      rc.ls[i] = rt[2 * (gamma + 1) + i];
+    }
+  }
+  const float* ws = wsum + (size_t)b * C * 2;
+  for (int i = threadIdx.x; i < 2 * C; i += TPB) wsh[i] = ws[i];
+  __syncthreads();
 
   if (threadIdx.x == 0) {
-    // Chunk level.  kind 1 (p_hat itself) only if a rejected row has no
-    // residual mass, which exact arithmetic rules out.
-    const float* ws = wsum + (size_t)b * C * 2;
+    // kind 1 (p_hat itself) only if a rejected row has no residual mass,
+    // which exact arithmetic rules out.
     float W = 0.f;
-    for (int c = 0; c < C; ++c) W += ws[2 * c];
+    for (int c = 0; c < C; ++c) W += wsh[2 * c];
     int kind = 0;
     if (!(W > 0.f)) {
       kind = 1;
       W = 0.f;
-      for (int c = 0; c < C; ++c) W += ws[2 * c + 1];
+      for (int c = 0; c < C; ++c) W += wsh[2 * c + 1];
     }
     float tau = u[(size_t)b * (gamma + 1) + ts] * W;
     float base = 0.f, last_base = 0.f;
     int pick = -1, last = -1;
     for (int c = 0; c < C; ++c) {
-      const float wc = ws[2 * c + kind];
+      const float wc = wsh[2 * c + kind];
       if (wc > 0.f) {
         if (base + wc > tau) {
           pick = c;
@@ -341,7 +389,7 @@ __global__ __launch_bounds__(TPB) void draw_kernel(
       }
       base += wc;
     }
-    if (pick < 0) {  // rounding: take the last chunk with weight
+    if (pick < 0) {
       pick = last < 0 ? 0 : last;
       base = last_base;
       tau = INFINITY;
@@ -440,17 +488,18 @@ hipError_t launch_accept(const float* z, const float* y, const int32_t* draft, c
   float* zstat = ws + L.zstat;
   float* ystat = ws + L.ystat;
   float* sstat = ws + L.sstat;
+  float* rowtab = ws + L.rowtab;
   float* wsm = ws + L.wsum;
   int32_t* tstar = reinterpret_cast<int32_t*>(ws + L.tstar);
   hipLaunchKernelGGL((stats_kernel<VEC>), dim3(C, 2 * gamma + 1, B), dim3(TPB), 0, s, z, y, gamma,
                      V, invT2, C, zstat, ystat);
-  hipLaunchKernelGGL((phat_kernel<VEC>), dim3(C, gamma, B), dim3(TPB), 0, s, z, y, gamma, V,
-                     invT2, eta2, C, zstat, ystat, sstat);
+  hipLaunchKernelGGL((phat_kernel<VEC>), dim3(C, gamma + 1, B), dim3(TPB), 0, s, z, y, gamma, V,
+                     invT2, eta2, C, zstat, ystat, sstat, rowtab);
   hipLaunchKernelGGL((decide_kernel<VEC>), dim3(C, B), dim3(TPB), 0, s, z, y, draft, r, gamma, V,
-                     invT2, eta2, C, zstat, ystat, sstat, wsm, tstar, n_accept, out_tokens,
-                     ratio_out, p_hat_out);
-  hipLaunchKernelGGL((draw_kernel<VEC>), dim3(B), dim3(TPB), 0, s, z, y, u, gamma, V, invT2, eta2,
-                     C, zstat, ystat, sstat, wsm, tstar, out_tokens);
+                     invT2, eta2, C, sstat, rowtab, wsm, tstar, n_accept, out_tokens, ratio_out,
+                     p_hat_out);
+  hipLaunchKernelGGL((draw_kernel<VEC>), dim3(B), dim3(TPB), (size_t)C * 2 * sizeof(float), s, z,
+                     y, u, gamma, V, invT2, eta2, C, rowtab, wsm, tstar, out_tokens);
   return hipGetLastError();
 }
 

@@ -30,6 +30,14 @@ __device__ __forceinline__ i32x4 buffer_load16(__amdgpu_buffer_rsrc_t rs, uint32
   return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
 }
 
+// Same, with the non-temporal cache policy (the `nt` bit of the buffer
+// instruction's cache-policy field): for data read exactly once, such as
+// the KV stream.  Measured on MI355X with the history pass's tile pattern:
+// ~7.0 TB/s of streaming reads versus ~6.0 TB/s with the default policy.
+__device__ __forceinline__ i32x4 buffer_load16_stream(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 2);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

@@ -47,7 +47,7 @@ rv_status check_prefix(const void* q, const void* k_cache, const void* v_cache,
   if (split_len <= 0 || split_len % kSplitQuantum != 0) return RV_ERR_SHAPE;
   if (num_splits < 1 || num_splits > 65535) return RV_ERR_SHAPE;
   if ((max_seq_len + split_len - 1) / split_len > num_splits) return RV_ERR_SHAPE;
-  if (!isfinite(sm_scale)) return RV_ERR_VALUE;
+  if (!isfinite(sm_scale) || !(sm_scale > 0.0f)) return RV_ERR_VALUE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o_part) ||
       !aligned16(lse_part))
     return RV_ERR_ALIGNMENT;
@@ -62,7 +62,7 @@ rv_status check_block(const void* q, const void* k_blk, const void* v_blk,
   if (!q || !k_blk || !v_blk || !o_blk || !lse_blk) return RV_ERR_NULL;
   rv_status st = check_heads(B, Hq, Hkv, n, d);
   if (st != RV_OK) return st;
-  if (!isfinite(sm_scale)) return RV_ERR_VALUE;
+  if (!isfinite(sm_scale) || !(sm_scale > 0.0f)) return RV_ERR_VALUE;
   if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(o_blk) ||
       !aligned16(lse_blk))
     return RV_ERR_ALIGNMENT;
@@ -111,6 +111,8 @@ AcceptLayout accept_layout(int B, int gamma, int V) {
   off += round_words((size_t)B * gamma * C * 2);
   L.sstat = off;
   off += round_words((size_t)B * gamma * C * 2);
+  L.rowtab = off;
+  off += round_words((size_t)B * 3 * (gamma + 1));
   L.wsum = off;
   off += round_words((size_t)B * C * 2);
   L.tstar = off;

@@ -84,6 +84,8 @@ def test_prefix_validation(lib):
     assert _prefix(lib, max_seq_len=5000) == RV_ERR_SHAPE  # beyond L_max
     assert _prefix(lib, scale=float("nan")) == RV_ERR_VALUE
     assert _prefix(lib, scale=float("inf")) == RV_ERR_VALUE
+    assert _prefix(lib, scale=0.0) == RV_ERR_VALUE
+    assert _prefix(lib, scale=-0.5) == RV_ERR_VALUE
     assert _prefix(lib, k=MIS) == RV_ERR_ALIGNMENT
     assert _prefix(lib, lse=MIS) == RV_ERR_ALIGNMENT
     assert _prefix(lib, L_max=1 << 24, max_seq_len=1 << 24, d=128, S=1 << 14) == RV_ERR_UNSUPPORTED
@@ -111,6 +113,7 @@ def test_block_validation(lib):
     assert _block(lib, parent=[-1, 0, 1, -1, 0]) == RV_ERR_VALUE    # second root
     assert _block(lib, o=MIS) == RV_ERR_ALIGNMENT
     assert _block(lib, scale=float("nan")) == RV_ERR_VALUE
+    assert _block(lib, scale=-1.0) == RV_ERR_VALUE
 
 
 def _merge(lib, **kw):

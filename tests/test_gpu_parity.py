@@ -115,8 +115,10 @@ def test_prefix_and_block_partials_match_split_oracle():
                 assert np.abs(lse_part[b, h, :, s] - l).max() <= 1e-2
             o, l = attn_keys_ref(q, bf16_bits_to_f64(ai.k_blk[b, g]), bf16_bits_to_f64(ai.v_blk[b, g]),
                                  vis, 1.0)
-            np.testing.assert_allclose(o_blk[b, h], o, rtol=0, atol=1e-4)
-            np.testing.assert_allclose(lse_blk[b, h], l, rtol=0, atol=1e-4)
+            # the block part runs on the same bf16 MFMA path as the history
+            # splits, so it is held to the same attention tolerance
+            assert attn_row_errors(o_blk[b, h], o).max() <= ATTN_ROW_TOL
+            assert np.abs(lse_blk[b, h] - l).max() <= 1e-2
 
 
 def test_seq_lens_are_clamped_on_the_device():
