@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librapid_verify.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["rv_validate.cpp", "attn_prefix.hip", "lse_merge.hip",
+SOURCES = ["rv_validate.cpp", "attn_prefix.hip", "attn_block.hip", "lse_merge.hip",
            "rapid_accept.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

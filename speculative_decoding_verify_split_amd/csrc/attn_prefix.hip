@@ -5,26 +5,28 @@
 //
 // Work decomposition (gfx950, 64-wide waves):
 //   grid  = (split s, kv-head x row-group, sequence b); 4 waves per workgroup.
-//   A workgroup owns one split of one (b, kv-head): the G = Hq/Hkv query heads
-//   of that kv-head share every K/V byte, so their G*n rows are stacked into
-//   16-row MFMA tiles (up to 4 tiles per wave; larger groups use several row
+//   A workgroup owns one split of one (b, kv-head).  The G = Hq/Hkv query
+//   heads of that kv-head share every K/V byte, so their G*n rows are stacked
+//   into 16-row MFMA tiles (up to 4 per wave; larger groups use several row
 //   groups).  Wave w streams the split's 32-key tiles w, w+4, w+8, ...
-//   Scores are computed transposed, S^T = K Q^T, with
-//   v_mfma_f32_16x16x32_bf16: the K tile is the A operand and is loaded
-//   straight from HBM into registers (each lane reads 4 x 16 B of one key row;
-//   one instruction covers 16 keys x 64 contiguous bytes).  In the transposed
-//   layout a lane holds 8 scores of one query row, which is exactly the B
-//   operand layout of the P V product, so P needs no shuffle.  V must be
-//   transposed for its operand: each wave stages its 32 x d V tile in a
-//   private LDS slice (row pitch 2d + 8 bytes: conflict-free gathers) and
-//   gathers 8 keys of one column per lane.  Online softmax runs in fp32 in
-//   base-2 units; the next tile's K/V loads are in flight while the current
-//   tile is computed.  The four waves' (max, sum, O) states are merged through
-//   LDS and one normalised partial (O, LSE) per row is written.
-//   Loads use buffer resources bounded by the split's length, so keys past
-//   the split or the sequence read as zero and are masked to -inf.
-
-#include <type_traits>
+//
+// Per tile:
+//   * K and V arrive by non-temporal 16-byte buffer loads (read once; range-
+//     checked, so keys past the split read as zero), two tiles ahead of use.
+//   * Scores are computed transposed, S^T = K Q^T, on
+//     v_mfma_f32_16x16x32_bf16 with K straight from registers as the A
+//     operand (one load instruction covers 16 keys x 64 contiguous bytes).
+//     In that layout a lane holds 8 scores of one query row: exactly the B
+//     operand of the P V product, so P needs no shuffle.
+//   * Online softmax in fp32, base-2 units, with a lazily raised running
+//     max (raised only when a tile exceeds it by more than 8), so the fp32
+//     accumulators are rescaled only on rare tiles; row max/sum across the
+//     four lanes of a row use the gfx950 row-swap permutes.
+//   * V is staged per wave in LDS in its natural [key][d] layout (row pitch
+//     2d + 32 bytes) and read back transposed for the A operand of
+//     O^T += V^T P^T with ds_read_b64_tr_b16, two reads per 16 columns.
+// The four waves' (max, sum, O) states are then merged through LDS and one
+// normalised partial (O, LSE) per row is written.
 
 #include "rv_device.h"
 #include "rv_internal.h"
@@ -77,19 +79,13 @@ struct TileRegs {
   i32x4 v[PrefixGeom<D>::VCH];
 };
 
-struct NoMask {};
-
-// BLOCK = false: history pass over split s of the cache (no mask).
-// BLOCK = true:  the draft block's own keys (one "split" holding all n block
-//                rows), with row i seeing block key j iff bit j of
-//                mask.bits[i] is set.
-template <int D, int MT, bool BLOCK>
+// History pass over split s of the cache (no mask).
+template <int D, int MT>
 __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ seq_lens, int Hq, int Hkv,
     int n, int64_t L_max, float scale_log2, int64_t split_len, int S, int RG,
-    float* __restrict__ o_part, float* __restrict__ lse_part,
-    const typename std::conditional<BLOCK, BlockMask, NoMask>::type mask) {
+    float* __restrict__ o_part, float* __restrict__ lse_part) {
   using Gm = PrefixGeom<D>;
   constexpr int KS = Gm::KS, NB = Gm::NB, VCH = Gm::VCH, VROW = Gm::VROW, OROW = Gm::OROW;
   constexpr int VBYTES = NW * Gm::VTILE;
@@ -117,13 +113,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
   const int row0 = rg * MT * 16;
   const int rows_here = min(MT * 16, M - row0);
 
-  int64_t L;
-  if constexpr (BLOCK) {
-    L = n;
-  } else {
-    L = seq_lens[b];
-    L = L < 0 ? 0 : (L > L_max ? L_max : L);
-  }
+  int64_t L = seq_lens[b];
+  L = L < 0 ? 0 : (L > L_max ? L_max : L);
   const int64_t kbeg = (int64_t)s * split_len;
   int64_t kend = kbeg + split_len;
   if (kend > L) kend = L;
@@ -131,20 +122,16 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
   const int ntiles = (nkeys + KT - 1) / KT;
 
   // Query fragments, B operand of S^T = K Q^T: lane (row lr, group lg) holds
-  // d = 32*ks + 8*lg .. +7 of its row.  In block mode each row also carries
-  // its visibility bits over the block keys.
+  // d = 32*ks + 8*lg .. +7 of its row.
   bf16x8 qf[kQLds ? 1 : MT][KS];
-  uint64_t vis[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int row = row0 + mt * 16 + lr;
-    vis[mt] = ~0ull;
     bf16x8 frag[KS];
     if (row < M) {
       const int gq = row / n;
       const int i = row - gq * n;
       const int h = kvh * G + gq;
-      if constexpr (BLOCK) vis[mt] = mask.bits[i];
       const uint16_t* qp = q + (((int64_t)b * Hq + h) * n + i) * D + lg * 8;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) frag[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
@@ -234,10 +221,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
         sacc[kb][mt] = acc;
       }
 
-    // Masking is needed only for a split's partial last tile (and always
-    // for the draft block's tree/causal mask).
-    const bool masked = BLOCK || (t + 1) * KT > nkeys;
-    if (masked) {
+    // Keys past the split are masked only in a split's partial last tile.
+    if ((t + 1) * KT > nkeys) {
       const int key0 = t * KT + lg * 4;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -245,10 +230,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const int kk = key0 + kb * 16 + v;
-            bool ok = kk < nkeys;
-            if constexpr (BLOCK) ok = ok && ((vis[mt] >> kk) & 1ull);
-            if (!ok) sacc[kb][mt][v] = -INFINITY;
+            if (key0 + kb * 16 + v >= nkeys) sacc[kb][mt][v] = -INFINITY;
           }
     }
 
@@ -275,7 +257,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
         for (int nb = 0; nb < NB; ++nb) oacc[nb][mt] *= alpha;
         m_run[mt] = m_new;
       }
-      // A row with no visible key so far keeps an empty state.
+      // (every tile holds a valid key, so m_run is finite from here on;
+      // the guard keeps an empty state well defined)
       const float neg_m = (m_run[mt] == -INFINITY) ? 0.f : -m_run[mt];
       float ps = 0.f;
 #pragma unroll
@@ -308,9 +291,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
 
   // Register pipeline: while tile t is computed, the next tiles of this wave
   // (t + NW, and t + 2 NW when registers allow) are in flight.
-  // (the draft block has at most one tile per wave; the widest shape would
-  // spill with a third buffer)
-  constexpr bool kDeep = !BLOCK && !(D == 128 && MT == 4);
+  // (the widest shape would spill with a third buffer)
+  constexpr bool kDeep = !(D == 128 && MT == 4);
   TileRegs<D> ra, rb, rc;
   int t = wave;
   if (t < ntiles) {
@@ -403,29 +385,28 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
   }
 }
 
-template <int D, int MT, bool BLOCK, typename MaskT>
+template <int D, int MT>
 hipError_t launch_attn(const void* q, const void* k, const void* v, const int32_t* seq_lens,
                        int B, int Hq, int Hkv, int n, int64_t L_max, float scale_log2,
                        int64_t split_len, int S, int RG, float* o_part, float* lse_part,
-                       const MaskT& mask, hipStream_t stream) {
+                       hipStream_t stream) {
   dim3 grid((unsigned)S, (unsigned)(Hkv * RG), (unsigned)B);
-  hipLaunchKernelGGL((attn_kernel<D, MT, BLOCK>), grid, dim3(NW * 64), 0, stream,
+  hipLaunchKernelGGL((attn_kernel<D, MT>), grid, dim3(NW * 64), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), seq_lens, Hq, Hkv, n, L_max, scale_log2,
-                     split_len, S, RG, o_part, lse_part, mask);
+                     split_len, S, RG, o_part, lse_part);
   return hipGetLastError();
 }
 
-template <bool BLOCK, typename MaskT>
 rv_status dispatch_attn(int d, int MTW, const void* q, const void* k, const void* v,
                         const int32_t* seq_lens, int B, int Hq, int Hkv, int n, int64_t L_max,
                         float scale_log2, int64_t split_len, int S, int RG, float* o_part,
-                        float* lse_part, const MaskT& mask, hipStream_t s) {
+                        float* lse_part, hipStream_t s) {
   hipError_t e;
 #define RV_ATTN_CASE(DD, MM)                                                                 \
   if (d == DD && MTW == MM)                                                                  \
-    e = launch_attn<DD, MM, BLOCK>(q, k, v, seq_lens, B, Hq, Hkv, n, L_max, scale_log2,      \
-                                   split_len, S, RG, o_part, lse_part, mask, s);
+    e = launch_attn<DD, MM>(q, k, v, seq_lens, B, Hq, Hkv, n, L_max, scale_log2, split_len,  \
+                            S, RG, o_part, lse_part, s);
   RV_ATTN_CASE(64, 1)
   else RV_ATTN_CASE(64, 2) else RV_ATTN_CASE(64, 3) else RV_ATTN_CASE(64, 4)
   else RV_ATTN_CASE(128, 1) else RV_ATTN_CASE(128, 2) else RV_ATTN_CASE(128, 3)
@@ -451,28 +432,7 @@ extern "C" rv_status spec_attn_prefix(const void* q, const void* k_cache, const 
   if (st != RV_OK) return st;
   const rv::RowPlan rp = rv::row_plan(Hq, Hkv, n);
   const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
-  return rv::dispatch_attn<false>(d, rp.MTW, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, n, L_max,
-                                  scale_log2, split_len, num_splits, rp.RG, o_part, lse_part,
-                                  rv::NoMask{}, static_cast<hipStream_t>(stream));
-}
-
-// spec_attn_block: the draft block's keys under the causal or tree mask
-// (LongSpec summary, section 2.3: only the few speculative tokens need a
-// mask).  The block tensors [B, Hkv, n, d] have the cache's layout with
-// L_max = n, so the same MFMA kernel runs them as one split of n keys with a
-// per-row visibility mask; o_blk/lse_blk are the S = 1 partial layout.
-extern "C" rv_status spec_attn_block(const void* q, const void* k_blk, const void* v_blk,
-                                     const int32_t* parent_host, int B, int Hq, int Hkv, int n,
-                                     int d, float sm_scale, float* o_blk, float* lse_blk,
-                                     void* stream) {
-  rv::BlockMask mask;
-  rv_status st = rv::check_block(q, k_blk, v_blk, parent_host, B, Hq, Hkv, n, d, sm_scale, o_blk,
-                                 lse_blk, &mask);
-  if (st != RV_OK) return st;
-  const rv::RowPlan rp = rv::row_plan(Hq, Hkv, n);
-  const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
-  const int64_t split = ((n + rv::kSplitQuantum - 1) / rv::kSplitQuantum) * rv::kSplitQuantum;
-  return rv::dispatch_attn<true>(d, rp.MTW, q, k_blk, v_blk, nullptr, B, Hq, Hkv, n, n,
-                                 scale_log2, split, 1, rp.RG, o_blk, lse_blk, mask,
-                                 static_cast<hipStream_t>(stream));
+  return rv::dispatch_attn(d, rp.MTW, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, n, L_max,
+                           scale_log2, split_len, num_splits, rp.RG, o_part, lse_part,
+                           static_cast<hipStream_t>(stream));
 }

@@ -31,6 +31,17 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
   const int wave = threadIdx.x >> 6;
   const int row = blockIdx.x;
   const float* lp = lse_part + (size_t)row * S;
+  const float* op = o_part + (size_t)row * S * D + lane * PER;
+  // The first batch of this wave's partials is requested before the max is
+  // known (empty splits hold zeros), so the row costs one memory round trip.
+  constexpr int FIRST = 8;
+  float val0[FIRST][PER];
+#pragma unroll
+  for (int j = 0; j < FIRST; ++j) {
+    const int s = wave + j * NWV;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) val0[j][e] = (s < S) ? op[(size_t)s * D + e] : 0.f;
+  }
   float M = -INFINITY;
   for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[s]);
   M = wave_max(M);
@@ -42,8 +53,17 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
   float wsum = 0.f;
   if (M != -INFINITY) {
     // wave w folds splits w, w + 4, w + 8, ... in ascending order
-    const float* op = o_part + (size_t)row * S * D + lane * PER;
-    int s = wave;
+#pragma unroll
+    for (int j = 0; j < FIRST; ++j) {
+      const int s = wave + j * NWV;
+      if (s < S) {
+        const float a = exp2_hw((lp[s] - M) * kLog2e);
+        wsum += a;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(a, val0[j][e], acc[e]);
+      }
+    }
+    int s = wave + FIRST * NWV;
     for (; s + 3 * NWV < S; s += 4 * NWV) {
       float a[4], val[4][PER];
 #pragma unroll

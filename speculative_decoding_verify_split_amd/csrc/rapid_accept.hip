@@ -242,6 +242,13 @@ __global__ __launch_bounds__(TPB) void decide_kernel(
   __shared__ RowLse rc;
   __shared__ int sh_ts;
   float* rt = rowtab + (size_t)b * 3 * (gamma + 1);
+  // Round trip 1: row table, s statistics, draft ids and acceptance uniforms.
+  int x = 0;
+  float rv = 0.f;
+  if (wave == 0 && lane < gamma) {
+    x = draft[(size_t)b * gamma + lane];
+    rv = r[(size_t)b * gamma + lane];
+  }
   for (int i = threadIdx.x; i <= gamma; i += TPB) {
     rc.lz[i] = rt[i];
     if (i < gamma) rc.ly[i] = rt[(gamma + 1) + i];
@@ -256,10 +263,10 @@ __global__ __launch_bounds__(TPB) void decide_kernel(
   __syncthreads();
 
   if (wave == 0) {
+    // Round trip 2: the draft tokens' target and draft logits.
     bool bad = false, acc = true;
     float ratio = 0.f;
     if (lane < gamma) {
-      const int x = draft[(size_t)b * gamma + lane];
       bad = (x < 0 || x >= V);
       if (!bad) {
         float p, q, s2;
@@ -267,10 +274,10 @@ __global__ __launch_bounds__(TPB) void decide_kernel(
              invT2, eta2, rc.lz[lane], rc.ly[lane], p, q, s2);
         const float ph = exp2_hw(s2 - rc.ls[lane]);
         ratio = fminf(1.0f, ph / q);
-        acc = r[(size_t)b * gamma + lane] <= ratio;
+        acc = rv <= ratio;
       }
     }
-    const uint64_t badm = __ballot(bad);
+  const uint64_t badm = __ballot(bad);
     const uint64_t rej = __ballot(lane < gamma && !acc);
     int ts = rej ? (int)__ffsll((long long)rej) - 1 : gamma;
     if (badm) ts = -1;
@@ -278,9 +285,7 @@ __global__ __launch_bounds__(TPB) void decide_kernel(
     if (c == 0) {
       if (ratio_out != nullptr && lane < gamma)
         ratio_out[(size_t)b * gamma + lane] = bad ? __builtin_nanf("") : ratio;
-      if (lane <= gamma)
-        out_tokens[(size_t)b * (gamma + 1) + lane] =
-            (lane < ts) ? draft[(size_t)b * gamma + lane] : -1;
+      if (lane <= gamma) out_tokens[(size_t)b * (gamma + 1) + lane] = (lane < ts) ? x : -1;
       if (lane < gamma) rt[2 * (gamma + 1) + lane] = rc.ls[lane];
       if (lane == 0) {
         n_accept[b] = ts;
@@ -349,11 +354,14 @@ __global__ __launch_bounds__(TPB) void draw_kernel(
   __shared__ float sh_tau;
   __shared__ float wtot[TPB / 64];
   extern __shared__ float wsh[];  // [C][2]
+  __shared__ float ush[kMaxGamma + 1];
+  // One round trip: the cut, the row table, the chunk weights and every
+  // sampling uniform of the sequence.
   const int ts = tstar_ws[b];
-  if (ts < 0) return;  // uniform
   const float* rt = rowtab + (size_t)b * 3 * (gamma + 1);
   for (int i = threadIdx.x; i <= gamma; i += TPB) {
     rc.lz[i] = rt[i];
+    ush[i] = u[(size_t)b * (gamma + 1) + i];
     if (i < gamma) {
       rc.ly[i] = rt[(gamma + 1) + i];
       rc.ls[i] = rt[2 * (gamma + 1) + i];
@@ -362,6 +370,7 @@ __global__ __launch_bounds__(TPB) void draw_kernel(
   const float* ws = wsum + (size_t)b * C * 2;
   for (int i = threadIdx.x; i < 2 * C; i += TPB) wsh[i] = ws[i];
   __syncthreads();
+  if (ts < 0) return;  // uniform
 
   if (threadIdx.x == 0) {
     // kind 1 (p_hat itself) only if a rejected row has no residual mass,
@@ -374,7 +383,7 @@ __global__ __launch_bounds__(TPB) void draw_kernel(
       W = 0.f;
       for (int c = 0; c < C; ++c) W += wsh[2 * c + 1];
     }
-    float tau = u[(size_t)b * (gamma + 1) + ts] * W;
+    float tau = ush[ts] * W;
     float base = 0.f, last_base = 0.f;
     int pick = -1, last = -1;
     for (int c = 0; c < C; ++c) {
