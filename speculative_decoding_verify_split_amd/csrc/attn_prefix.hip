@@ -25,8 +25,9 @@
 //   * V is staged per wave in LDS in its natural [key][d] layout (row pitch
 //     2d + 32 bytes) and read back transposed for the A operand of
 //     O^T += V^T P^T with ds_read_b64_tr_b16, two reads per 16 columns.
-// The four waves' (max, sum, O) states are then merged through LDS and one
-// normalised partial (O, LSE) per row is written.
+// The four waves park their (max, sum, O) states in per-wave LDS slots and,
+// after one barrier, all threads merge them and write one normalised partial
+// (O, LSE) per row.
 
 #include "rv_device.h"
 #include "rv_internal.h"
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
   using Gm = PrefixGeom<D>;
   constexpr int KS = Gm::KS, NB = Gm::NB, VCH = Gm::VCH, VROW = Gm::VROW, OROW = Gm::OROW;
   constexpr int VBYTES = NW * Gm::VTILE;
-  constexpr int OBYTES = MT * 16 * OROW * 4;
+  constexpr int OBYTES = NW * MT * 16 * OROW * 4;  // one merge slot per wave
   constexpr int SMEM = VBYTES > OBYTES ? VBYTES : OBYTES;
   // The widest shape keeps its query fragments in LDS to stay within 512
   // registers per lane; the others keep them in registers.
@@ -97,8 +98,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
   constexpr int QLDS_BYTES = kQLds ? MT * KS * 64 * 16 : 16;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   __shared__ __attribute__((aligned(16))) bf16x8 q_lds[QLDS_BYTES / 16];
-  __shared__ float m_lds[MT * 16];
-  __shared__ float l_lds[MT * 16];
+  __shared__ float m_lds[NW][MT * 16];
+  __shared__ float l_lds[NW][MT * 16];
 
   const int s = blockIdx.x;
   const int kvh = blockIdx.y / RG;
@@ -331,41 +332,44 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) l_run[mt] = row_sum4(l_run[mt]);
 
-  // Merge the four waves' states through LDS, one wave at a time.
-  __syncthreads();  // V tiles are dead; the buffer becomes the merge buffer
+  // Each wave parks its state (running max, row sum, unnormalised O) in its
+  // own LDS slot; after one barrier all threads merge the four slots per
+  // row in wave order and write the normalised partial.
+  __syncthreads();  // V tiles are dead; the buffer becomes the merge slots
   float* obuf = reinterpret_cast<float*>(smem);
-  for (int w = 0; w < NW; ++w) {
-    if (wave == w) {
+  {
+    float* slot = obuf + wave * (MT * 16 * OROW);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int row = mt * 16 + lr;
-        const float mo = (w == 0) ? -INFINITY : m_lds[row];
-        const float lo = (w == 0) ? 0.f : l_lds[row];
-        const float mn = fmaxf(mo, m_run[mt]);
-        const float a = (mo == -INFINITY) ? 0.f : exp2_hw(mo - mn);
-        const float c = (m_run[mt] == -INFINITY) ? 0.f : exp2_hw(m_run[mt] - mn);
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = mt * 16 + lr;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          f32x4* op = reinterpret_cast<f32x4*>(obuf + row * OROW + nb * 16 + lg * 4);
-          const f32x4 prev = (w == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : *op;
-          *op = a * prev + c * oacc[nb][mt];
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        if (lg == 0) {
-          m_lds[row] = mn;
-          l_lds[row] = a * lo + c * l_run[mt];
-        }
+      for (int nb = 0; nb < NB; ++nb)
+        *reinterpret_cast<f32x4*>(slot + row * OROW + nb * 16 + lg * 4) = oacc[nb][mt];
+      if (lg == 0) {
+        m_lds[wave][row] = m_run[mt];
+        l_lds[wave][row] = l_run[mt];
       }
     }
-    __syncthreads();
   }
+  __syncthreads();
 
-  // Normalised partial output and its natural-log LSE.
   for (int idx = threadIdx.x; idx < rows_here * (D / 4); idx += NW * 64) {
     const int row = idx / (D / 4);
     const int c4 = idx - row * (D / 4);
-    const float l = l_lds[row];
-    const f32x4 o = *reinterpret_cast<const f32x4*>(obuf + row * OROW + c4 * 4);
+    float mw[NW], M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      mw[w] = m_lds[w][row];
+      M = fmaxf(M, mw[w]);
+    }
+    float l = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float a = (mw[w] == -INFINITY) ? 0.f : exp2_hw(mw[w] - M);
+      l += a * l_lds[w][row];
+      o += a * *reinterpret_cast<const f32x4*>(obuf + (w * MT * 16 + row) * OROW + c4 * 4);
+    }
     const f32x4 res = l > 0.f ? o / l : f32x4{0.f, 0.f, 0.f, 0.f};
     const int grow = row0 + row;
     const int gq = grow / n;
@@ -373,15 +377,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
     const int h = kvh * G + gq;
     float* dst = o_part + ((((int64_t)b * Hq + h) * n + i) * S + s) * D + c4 * 4;
     *reinterpret_cast<f32x4*>(dst) = res;
-  }
-  for (int row = threadIdx.x; row < rows_here; row += NW * 64) {
-    const float l = l_lds[row];
-    const float lse = l > 0.f ? (m_lds[row] + log2_hw(l)) * kLn2 : -INFINITY;
-    const int grow = row0 + row;
-    const int gq = grow / n;
-    const int i = grow - gq * n;
-    const int h = kvh * G + gq;
-    lse_part[(((int64_t)b * Hq + h) * n + i) * S + s] = lse;
+    if (c4 == 0) {
+      lse_part[(((int64_t)b * Hq + h) * n + i) * S + s] =
+          l > 0.f ? (M + log2_hw(l)) * kLn2 : -INFINITY;
+    }
   }
 }
 

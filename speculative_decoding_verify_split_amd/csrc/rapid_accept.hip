@@ -83,18 +83,27 @@ __device__ __forceinline__ void lse_pair_merge(float& m, float& l, float mo, flo
 }
 
 // Base-2 log-sum-exp of a row from its per-chunk (max, sum) pairs, reduced by
-// a group of `width` lanes (a power of two <= 64) in one pass: lane j of the
-// group folds chunks j, j + width, ... in order, then the group merges by
-// butterfly.  Every lane of the group returns the same value.
+// a group of `width` lanes (16 or 64, aligned) in one pass: lane j of the
+// group folds chunks j, j + width, ... in order, then the group merges with
+// symmetric lane pairings (DPP quad permutes and mirrors, then the row-swap
+// permutes).  Every lane of the group returns the same value.
 template <int width>
 __device__ __forceinline__ float group_combine(const float* __restrict__ st, int C, int j) {
+  static_assert(width == 16 || width == 64, "group width");
   float m = -INFINITY, l = 0.f;
   for (int c = j; c < C; c += width) lse_pair_merge(m, l, st[2 * c], st[2 * c + 1]);
-#pragma unroll
-  for (int o = width / 2; o >= 1; o >>= 1) {
-    const float mo = __shfl_xor(m, o, 64);
-    const float lo = __shfl_xor(l, o, 64);
-    lse_pair_merge(m, l, mo, lo);
+  lse_pair_merge(m, l, dpp_f<kDppXor1>(m), dpp_f<kDppXor1>(l));
+  lse_pair_merge(m, l, dpp_f<kDppXor2>(m), dpp_f<kDppXor2>(l));
+  lse_pair_merge(m, l, dpp_f<kDppHalfMirror>(m), dpp_f<kDppHalfMirror>(l));
+  lse_pair_merge(m, l, dpp_f<kDppMirror>(m), dpp_f<kDppMirror>(l));
+  if constexpr (width == 64) {
+    float2 a = swap16(m), c = swap16(l);
+    m = a.x; l = c.x;
+    lse_pair_merge(m, l, a.y, c.y);
+    a = swap32(m);
+    c = swap32(l);
+    m = a.x; l = c.x;
+    lse_pair_merge(m, l, a.y, c.y);
   }
   return m + log2_hw(l);
 }
@@ -372,40 +381,64 @@ __global__ __launch_bounds__(TPB) void draw_kernel(
   __syncthreads();
   if (ts < 0) return;  // uniform
 
-  if (threadIdx.x == 0) {
-    // kind 1 (p_hat itself) only if a rejected row has no residual mass,
-    // which exact arithmetic rules out.
-    float W = 0.f;
-    for (int c = 0; c < C; ++c) W += wsh[2 * c];
+  if (wave == 0) {
+    // Chunk level, one wave: an inclusive scan of the chunk weights in
+    // blocks of 64 (fixed pattern), then the first chunk of positive weight
+    // whose running total exceeds u * W.  kind 1 (p_hat itself) only if a
+    // rejected row has no residual mass, which exact arithmetic rules out.
     int kind = 0;
-    if (!(W > 0.f)) {
-      kind = 1;
-      W = 0.f;
-      for (int c = 0; c < C; ++c) W += wsh[2 * c + 1];
-    }
-    float tau = ush[ts] * W;
-    float base = 0.f, last_base = 0.f;
-    int pick = -1, last = -1;
-    for (int c = 0; c < C; ++c) {
-      const float wc = wsh[2 * c + kind];
-      if (wc > 0.f) {
-        if (base + wc > tau) {
-          pick = c;
-          break;
+    float W = 0.f;
+    for (int pass = 0; pass < 2; ++pass) {
+      kind = pass;
+      float carry = 0.f;
+      for (int c0 = 0; c0 < C; c0 += 64) {
+        const int c = c0 + lane;
+        float incl = (c < C) ? wsh[2 * c + kind] : 0.f;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const float v = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += v;
         }
-        last = c;
-        last_base = base;
+        carry += __shfl(incl, 63, 64);
       }
-      base += wc;
+      W = carry;
+      if (W > 0.f) break;
     }
-    if (pick < 0) {
+    const float tau = ush[ts] * W;
+    float carry = 0.f;
+    int pick = -1, last = -1;
+    float pick_base = 0.f;
+    for (int c0 = 0; c0 < C && pick < 0; c0 += 64) {
+      const int c = c0 + lane;
+      const float wc = (c < C) ? wsh[2 * c + kind] : 0.f;
+      float incl = wc;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float v = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += v;
+      }
+      const float excl = carry + (incl - wc);
+      const uint64_t hit = __ballot(wc > 0.f && carry + incl > tau);
+      const uint64_t pos = __ballot(wc > 0.f);
+      if (hit) {
+        const int lsel = (int)__ffsll((long long)hit) - 1;
+        pick = c0 + lsel;
+        pick_base = __shfl(excl, lsel, 64);
+      } else if (pos) {
+        last = c0 + 63 - (int)__builtin_clzll(pos);
+      }
+      carry += __shfl(incl, 63, 64);
+    }
+    float tau_c = tau - pick_base;
+    if (pick < 0) {  // rounding: the last chunk with weight, its last positive id
       pick = last < 0 ? 0 : last;
-      base = last_base;
-      tau = INFINITY;
+      tau_c = INFINITY;
     }
-    sh_chunk = pick;
-    sh_kind = kind;
-    sh_tau = tau - base;
+    if (lane == 0) {
+      sh_chunk = pick;
+      sh_kind = kind;
+      sh_tau = tau_c;
+    }
   }
   __syncthreads();
   const int chunk = sh_chunk, kind = sh_kind;

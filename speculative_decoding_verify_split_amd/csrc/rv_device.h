@@ -38,16 +38,60 @@ __device__ __forceinline__ i32x4 buffer_load16_stream(__amdgpu_buffer_rsrc_t rs,
   return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 2);
 }
 
+// Lane permutations used by the all-reductions below.  Every step pairs
+// lanes symmetrically (an involution), so both lanes of a pair compute
+// op(a, b) and op(b, a): max and + are commutative, hence every lane ends
+// with the bit-identical result, and the order of combination is fixed.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i inside each 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i inside each 16
+
+// Partner across 16-lane rows (i <-> i ^ 16) or wave halves (i <-> i ^ 32),
+// with the gfx950 row-swap permutes: swapping a value with a copy of itself
+// leaves {own, partner} in the two results.
+__device__ __forceinline__ float2 swap16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float2 swap32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_f<kDppMirror>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v = v + dpp_f<kDppXor1>(v);
+  v = v + dpp_f<kDppXor2>(v);
+  v = v + dpp_f<kDppHalfMirror>(v);
+  return v + dpp_f<kDppMirror>(v);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = row16_max(v);
+  float2 a = swap16(v);
+  v = fmaxf(a.x, a.y);
+  a = swap32(v);
+  return fmaxf(a.x, a.y);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v = row16_sum(v);
+  float2 a = swap16(v);
+  v = a.x + a.y;
+  a = swap32(v);
+  return a.x + a.y;
 }
 
 // Round-to-nearest-even fp32 -> bf16 bit pattern.

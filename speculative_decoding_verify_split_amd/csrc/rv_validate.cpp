@@ -66,7 +66,7 @@ rv_status check_block(const void* q, const void* k_blk, const void* v_blk,
   if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(o_blk) ||
       !aligned16(lse_blk))
     return RV_ERR_ALIGNMENT;
-  if ((int64_t)B * Hq > 0x7fffffff / 64) return RV_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hq > 65535) return RV_ERR_UNSUPPORTED;  // grid dimension y
   BlockMask m;
   memset(&m, 0, sizeof(m));
   if (parent_host == nullptr) {
