@@ -12,7 +12,7 @@
 //
 // Per tile:
 //   * K and V arrive by non-temporal 16-byte buffer loads (read once; range-
-//     checked, so keys past the split read as zero), two tiles ahead of use.
+//     checked, so keys past the split read as zero), one tile ahead of use.
 //   * Scores are computed transposed, S^T = K Q^T, on
 //     v_mfma_f32_16x16x32_bf16 with K straight from registers as the A
 //     operand (one load instruction covers 16 keys x 64 contiguous bytes).
@@ -290,41 +290,22 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
     }
   };
 
-  // Register pipeline: while tile t is computed, the next tiles of this wave
-  // (t + NW, and t + 2 NW when registers allow) are in flight.
-  // (the widest shape would spill with a third buffer)
-  constexpr bool kDeep = !(D == 128 && MT == 4);
-  TileRegs<D> ra, rb, rc;
+  // Two register buffers: while tile t is computed, tile t + NW of this wave
+  // is in flight.  (Measured on MI355X at the 8B shape: a third buffer, which
+  // costs registers and 3x unrolled code, is ~1.5 us slower per launch.)
+  TileRegs<D> ra, rb;
   int t = wave;
   if (t < ntiles) {
     load_tile(t, ra);
-    if constexpr (kDeep) {
+    for (;;) {
       load_tile(t + NW, rb);
-      for (;;) {
-        load_tile(t + 2 * NW, rc);
-        compute_tile(ra, t);
-        t += NW;
-        if (t >= ntiles) break;
-        load_tile(t + 2 * NW, ra);
-        compute_tile(rb, t);
-        t += NW;
-        if (t >= ntiles) break;
-        load_tile(t + 2 * NW, rb);
-        compute_tile(rc, t);
-        t += NW;
-        if (t >= ntiles) break;
-      }
-    } else {
-      for (;;) {
-        load_tile(t + NW, rb);
-        compute_tile(ra, t);
-        t += NW;
-        if (t >= ntiles) break;
-        load_tile(t + NW, ra);
-        compute_tile(rb, t);
-        t += NW;
-        if (t >= ntiles) break;
-      }
+      compute_tile(ra, t);
+      t += NW;
+      if (t >= ntiles) break;
+      load_tile(t + NW, ra);
+      compute_tile(rb, t);
+      t += NW;
+      if (t >= ntiles) break;
     }
   }
 

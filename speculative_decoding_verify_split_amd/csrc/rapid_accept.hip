@@ -16,12 +16,14 @@
 //                  chunk 0 writes n_accept, the accepted tokens and the
 //                  ratios; every chunk writes its share of the draw weights
 //                  (max(p_hat - q, 0) at t* < gamma, p_gamma otherwise) and,
-//                  on request, p_hat
-//   draw_kernel    (b):             inverse CDF with the caller's uniform:
-//                  chunk -> wave -> lane -> element, each level taking the
-//                  first unit whose running total exceeds the target
-// No atomics; every reduction has a fixed order, so results are bit-exact
-// run to run.
+//                  on request, p_hat.  The last chunk to finish (one
+//                  per-sequence arrival counter) then draws the token by
+//                  inverse CDF with the caller's uniform: chunk -> wave ->
+//                  lane -> element, each level taking the first unit whose
+//                  running total exceeds the target.
+// Every reduction has a fixed order and the counter only decides which
+// workgroup runs the draw, so results are bit-exact run to run; no
+// workgroup ever waits for another.
 
 #include "rv_device.h"
 #include "rv_internal.h"
@@ -122,8 +124,12 @@ template <bool VEC>
 __global__ __launch_bounds__(TPB) void stats_kernel(const float* __restrict__ z,
                                                     const float* __restrict__ y, int gamma, int V,
                                                     float invT2, int C, float* __restrict__ zstat,
-                                                    float* __restrict__ ystat) {
+                                                    float* __restrict__ ystat,
+                                                    uint32_t* __restrict__ arrivals) {
   const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
+  // The decide kernel counts chunk arrivals per sequence; start from zero on
+  // every call (the workspace is not assumed to be initialised).
+  if (c == 0 && r == 0 && threadIdx.x == 0) arrivals[b] = 0u;
   const float* row;
   float* dst;
   if (r <= gamma) {
@@ -167,7 +173,7 @@ __global__ __launch_bounds__(TPB) void phat_kernel(const float* __restrict__ z,
                                                    float* __restrict__ rowtab) {
   const int c = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
-  float* rt = rowtab + (size_t)b * 3 * (gamma + 1);
+  float* rt = rowtab + (size_t)b * 2 * (gamma + 1);
   if (t == gamma) {
     if (c == 0 && threadIdx.x < 64) {
       const float lz = group_combine<64>(zstat + ((size_t)b * (gamma + 1) + t) * C * 2, C, lane);
@@ -235,151 +241,28 @@ __device__ __forceinline__ float draw_weight(float zv, float yv, int ts, int gam
   return kind == 0 ? fmaxf(ph - q, 0.f) : ph;
 }
 
-// grid (C, B).  Every chunk recomputes the row LSEs of s (16 lanes per row,
-// all rows at once), the ratios and the first-reject cut, then writes its
-// share of the draw weights; chunk 0 writes the per-sequence outputs.
-template <bool VEC>
-__global__ __launch_bounds__(TPB) void decide_kernel(
-    const float* __restrict__ z, const float* __restrict__ y, const int32_t* __restrict__ draft,
-    const float* __restrict__ r, int gamma, int V, float invT2, float eta2, int C,
-    const float* __restrict__ sstat, float* __restrict__ rowtab, float* __restrict__ wsum,
-    int32_t* __restrict__ tstar_ws, int32_t* __restrict__ n_accept,
-    int32_t* __restrict__ out_tokens, float* __restrict__ ratio_out,
-    float* __restrict__ p_hat_out) {
-  const int c = blockIdx.x, b = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __shared__ RowLse rc;
-  __shared__ int sh_ts;
-  float* rt = rowtab + (size_t)b * 3 * (gamma + 1);
-  // Round trip 1: row table, s statistics, draft ids and acceptance uniforms.
-  int x = 0;
-  float rv = 0.f;
-  if (wave == 0 && lane < gamma) {
-    x = draft[(size_t)b * gamma + lane];
-    rv = r[(size_t)b * gamma + lane];
-  }
-  for (int i = threadIdx.x; i <= gamma; i += TPB) {
-    rc.lz[i] = rt[i];
-    if (i < gamma) rc.ly[i] = rt[(gamma + 1) + i];
-  }
-  {
-    const int grp = threadIdx.x >> 4, j = threadIdx.x & 15;
-    for (int t = grp; t < gamma; t += TPB / 16) {
-      const float ls = group_combine<16>(sstat + ((size_t)b * gamma + t) * C * 2, C, j);
-      if (j == 0) rc.ls[t] = ls;
-    }
-  }
-  __syncthreads();
-
-  if (wave == 0) {
-    // Round trip 2: the draft tokens' target and draft logits.
-    bool bad = false, acc = true;
-    float ratio = 0.f;
-    if (lane < gamma) {
-      bad = (x < 0 || x >= V);
-      if (!bad) {
-        float p, q, s2;
-        pq_s(z[((size_t)b * (gamma + 1) + lane) * V + x], y[((size_t)b * gamma + lane) * V + x],
-             invT2, eta2, rc.lz[lane], rc.ly[lane], p, q, s2);
-        const float ph = exp2_hw(s2 - rc.ls[lane]);
-        ratio = fminf(1.0f, ph / q);
-        acc = rv <= ratio;
-      }
-    }
-  const uint64_t badm = __ballot(bad);
-    const uint64_t rej = __ballot(lane < gamma && !acc);
-    int ts = rej ? (int)__ffsll((long long)rej) - 1 : gamma;
-    if (badm) ts = -1;
-    if (lane == 0) sh_ts = ts;
-    if (c == 0) {
-      if (ratio_out != nullptr && lane < gamma)
-        ratio_out[(size_t)b * gamma + lane] = bad ? __builtin_nanf("") : ratio;
-      if (lane <= gamma) out_tokens[(size_t)b * (gamma + 1) + lane] = (lane < ts) ? x : -1;
-      if (lane < gamma) rt[2 * (gamma + 1) + lane] = rc.ls[lane];
-      if (lane == 0) {
-        n_accept[b] = ts;
-        tstar_ws[b] = ts;
-      }
-    }
-  }
-  __syncthreads();
-  const int ts = sh_ts;
-  const int start = c * CH + threadIdx.x * PER;
-
-  if (p_hat_out != nullptr) {
-    for (int t = 0; t < gamma; ++t) {
-      float zx[PER], yx[PER];
-      load_run<VEC>(z + ((size_t)b * (gamma + 1) + t) * V, V, start, zx);
-      load_run<VEC>(y + ((size_t)b * gamma + t) * V, V, start, yx);
-      float* dst = p_hat_out + ((size_t)b * gamma + t) * V;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        float p, q, s2;
-        pq_s(zx[e], yx[e], invT2, eta2, rc.lz[t], rc.ly[t], p, q, s2);
-        if (start + e < V) dst[start + e] = exp2_hw(s2 - rc.ls[t]);
-      }
-    }
-  }
-  if (ts < 0) return;  // uniform across the workgroup
-
-  float zx[PER], yx[PER];
-  load_run<VEC>(z + ((size_t)b * (gamma + 1) + ts) * V, V, start, zx);
-  if (ts < gamma)
-    load_run<VEC>(y + ((size_t)b * gamma + ts) * V, V, start, yx);
-  else
-#pragma unroll
-    for (int e = 0; e < PER; ++e) yx[e] = 0.f;
-  float w0 = 0.f, w1 = 0.f;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    if (start + e < V) {
-      w0 += draw_weight(zx[e], yx[e], ts, gamma, 0, invT2, eta2, rc);
-      w1 += draw_weight(zx[e], yx[e], ts, gamma, 1, invT2, eta2, rc);
-    }
-  }
-  const float W0 = block_sum(w0);
-  const float W1 = block_sum(w1);
-  if (threadIdx.x == 0) {
-    wsum[((size_t)b * C + c) * 2 + 0] = W0;
-    wsum[((size_t)b * C + c) * 2 + 1] = W1;
-  }
-}
-
-// grid (B).  Inverse CDF of the draw row with the caller's uniform:
+// Inverse CDF of the draw row ts of sequence b with the caller's uniform:
 // chunk -> wave -> lane -> element, each level taking the first unit of
 // positive weight whose running total exceeds the target; if rounding leaves
 // none, the last unit of positive weight (and every lower level then takes
-// its last positive unit, i.e. the largest id of positive weight).
+// its last positive unit, i.e. the largest id of positive weight).  Run by
+// one whole workgroup; wsh is LDS for the 2 C chunk weights.
 template <bool VEC>
-__global__ __launch_bounds__(TPB) void draw_kernel(
-    const float* __restrict__ z, const float* __restrict__ y, const float* __restrict__ u,
-    int gamma, int V, float invT2, float eta2, int C, const float* __restrict__ rowtab,
-    const float* __restrict__ wsum, const int32_t* __restrict__ tstar_ws,
-    int32_t* __restrict__ out_tokens) {
-  const int b = blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __shared__ RowLse rc;
+__device__ void draw_row(const float* __restrict__ z, const float* __restrict__ y,
+                         const float* __restrict__ u, int b, int ts, int gamma, int V,
+                         float invT2, float eta2, int C, const RowLse& rc,
+                         const float* __restrict__ wsum, float* wsh,
+                         int32_t* __restrict__ out_tokens) {
   __shared__ int sh_chunk, sh_kind;
   __shared__ float sh_tau;
   __shared__ float wtot[TPB / 64];
-  extern __shared__ float wsh[];  // [C][2]
-  __shared__ float ush[kMaxGamma + 1];
-  // One round trip: the cut, the row table, the chunk weights and every
-  // sampling uniform of the sequence.
-  const int ts = tstar_ws[b];
-  const float* rt = rowtab + (size_t)b * 3 * (gamma + 1);
-  for (int i = threadIdx.x; i <= gamma; i += TPB) {
-    rc.lz[i] = rt[i];
-    ush[i] = u[(size_t)b * (gamma + 1) + i];
-    if (i < gamma) {
-      rc.ly[i] = rt[(gamma + 1) + i];
-      rc.ls[i] = rt[2 * (gamma + 1) + i];
-    }
-  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // The chunk weights were published by the other workgroups before their
+  // arrival was counted; read them past the caches.
   const float* ws = wsum + (size_t)b * C * 2;
-  for (int i = threadIdx.x; i < 2 * C; i += TPB) wsh[i] = ws[i];
+  for (int i = threadIdx.x; i < 2 * C; i += TPB) wsh[i] = __builtin_nontemporal_load(ws + i);
+  const float u_ts = u[(size_t)b * (gamma + 1) + ts];
   __syncthreads();
-  if (ts < 0) return;  // uniform
 
   if (wave == 0) {
     // Chunk level, one wave: an inclusive scan of the chunk weights in
@@ -404,7 +287,7 @@ __global__ __launch_bounds__(TPB) void draw_kernel(
       W = carry;
       if (W > 0.f) break;
     }
-    const float tau = ush[ts] * W;
+    const float tau = u_ts * W;
     float carry = 0.f;
     int pick = -1, last = -1;
     float pick_base = 0.f;
@@ -520,6 +403,124 @@ __global__ __launch_bounds__(TPB) void draw_kernel(
   out_tokens[(size_t)b * (gamma + 1) + ts] = tok;
 }
 
+// grid (C, B).  Every chunk recomputes the row LSEs of s (16 lanes per row,
+// all rows at once), the ratios and the first-reject cut, then writes its
+// share of the draw weights; chunk 0 writes the per-sequence outputs.
+template <bool VEC>
+__global__ __launch_bounds__(TPB) void decide_kernel(
+    const float* __restrict__ z, const float* __restrict__ y, const int32_t* __restrict__ draft,
+    const float* __restrict__ r, int gamma, int V, float invT2, float eta2, int C,
+    const float* __restrict__ sstat, float* __restrict__ rowtab, float* __restrict__ wsum,
+    uint32_t* __restrict__ arrivals, const float* __restrict__ u,
+    int32_t* __restrict__ n_accept, int32_t* __restrict__ out_tokens,
+    float* __restrict__ ratio_out, float* __restrict__ p_hat_out) {
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ RowLse rc;
+  __shared__ int sh_ts;
+  float* rt = rowtab + (size_t)b * 2 * (gamma + 1);
+  // Round trip 1: row table, s statistics, draft ids and acceptance uniforms.
+  int x = 0;
+  float rv = 0.f;
+  if (wave == 0 && lane < gamma) {
+    x = draft[(size_t)b * gamma + lane];
+    rv = r[(size_t)b * gamma + lane];
+  }
+  for (int i = threadIdx.x; i <= gamma; i += TPB) {
+    rc.lz[i] = rt[i];
+    if (i < gamma) rc.ly[i] = rt[(gamma + 1) + i];
+  }
+  {
+    const int grp = threadIdx.x >> 4, j = threadIdx.x & 15;
+    for (int t = grp; t < gamma; t += TPB / 16) {
+      const float ls = group_combine<16>(sstat + ((size_t)b * gamma + t) * C * 2, C, j);
+      if (j == 0) rc.ls[t] = ls;
+    }
+  }
+  __syncthreads();
+
+  if (wave == 0) {
+    // Round trip 2: the draft tokens' target and draft logits.
+    bool bad = false, acc = true;
+    float ratio = 0.f;
+    if (lane < gamma) {
+      bad = (x < 0 || x >= V);
+      if (!bad) {
+        float p, q, s2;
+        pq_s(z[((size_t)b * (gamma + 1) + lane) * V + x], y[((size_t)b * gamma + lane) * V + x],
+             invT2, eta2, rc.lz[lane], rc.ly[lane], p, q, s2);
+        const float ph = exp2_hw(s2 - rc.ls[lane]);
+        ratio = fminf(1.0f, ph / q);
+        acc = rv <= ratio;
+      }
+    }
+  const uint64_t badm = __ballot(bad);
+    const uint64_t rej = __ballot(lane < gamma && !acc);
+    int ts = rej ? (int)__ffsll((long long)rej) - 1 : gamma;
+    if (badm) ts = -1;
+    if (lane == 0) sh_ts = ts;
+    if (c == 0) {
+      if (ratio_out != nullptr && lane < gamma)
+        ratio_out[(size_t)b * gamma + lane] = bad ? __builtin_nanf("") : ratio;
+      if (lane <= gamma) out_tokens[(size_t)b * (gamma + 1) + lane] = (lane < ts) ? x : -1;
+      if (lane == 0) n_accept[b] = ts;
+    }
+  }
+  __syncthreads();
+  const int ts = sh_ts;
+  const int start = c * CH + threadIdx.x * PER;
+
+  if (p_hat_out != nullptr) {
+    for (int t = 0; t < gamma; ++t) {
+      float zx[PER], yx[PER];
+      load_run<VEC>(z + ((size_t)b * (gamma + 1) + t) * V, V, start, zx);
+      load_run<VEC>(y + ((size_t)b * gamma + t) * V, V, start, yx);
+      float* dst = p_hat_out + ((size_t)b * gamma + t) * V;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        float p, q, s2;
+        pq_s(zx[e], yx[e], invT2, eta2, rc.lz[t], rc.ly[t], p, q, s2);
+        if (start + e < V) dst[start + e] = exp2_hw(s2 - rc.ls[t]);
+      }
+    }
+  }
+  if (ts < 0) return;  // uniform across the workgroup
+
+  float zx[PER], yx[PER];
+  load_run<VEC>(z + ((size_t)b * (gamma + 1) + ts) * V, V, start, zx);
+  if (ts < gamma)
+    load_run<VEC>(y + ((size_t)b * gamma + ts) * V, V, start, yx);
+  else
+#pragma unroll
+    for (int e = 0; e < PER; ++e) yx[e] = 0.f;
+  float w0 = 0.f, w1 = 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    if (start + e < V) {
+      w0 += draw_weight(zx[e], yx[e], ts, gamma, 0, invT2, eta2, rc);
+      w1 += draw_weight(zx[e], yx[e], ts, gamma, 1, invT2, eta2, rc);
+    }
+  }
+  const float W0 = block_sum(w0);
+  const float W1 = block_sum(w1);
+  // Publish this chunk's draw weights, then count its arrival.  The
+  // workgroup that arrives last draws the token: which workgroup that is
+  // does not change what is drawn, and nothing ever waits for another
+  // workgroup.
+  __shared__ uint32_t sh_arrived;
+  if (threadIdx.x == 0) {
+    wsum[((size_t)b * C + c) * 2 + 0] = W0;
+    wsum[((size_t)b * C + c) * 2 + 1] = W1;
+    __threadfence();
+    sh_arrived = atomicAdd(arrivals + b, 1u);
+  }
+  __syncthreads();
+  if (sh_arrived != (uint32_t)(C - 1)) return;  // uniform
+  __threadfence();
+  extern __shared__ float wsh[];  // [C][2]
+  draw_row<VEC>(z, y, u, b, ts, gamma, V, invT2, eta2, C, rc, wsum, wsh, out_tokens);
+}
+
 template <bool VEC>
 hipError_t launch_accept(const float* z, const float* y, const int32_t* draft, const float* r,
                          const float* u, int B, int gamma, int V, float invT2, float eta2,
@@ -532,16 +533,14 @@ hipError_t launch_accept(const float* z, const float* y, const int32_t* draft, c
   float* sstat = ws + L.sstat;
   float* rowtab = ws + L.rowtab;
   float* wsm = ws + L.wsum;
-  int32_t* tstar = reinterpret_cast<int32_t*>(ws + L.tstar);
+  uint32_t* arrivals = reinterpret_cast<uint32_t*>(ws + L.arrivals);
   hipLaunchKernelGGL((stats_kernel<VEC>), dim3(C, 2 * gamma + 1, B), dim3(TPB), 0, s, z, y, gamma,
-                     V, invT2, C, zstat, ystat);
+                     V, invT2, C, zstat, ystat, arrivals);
   hipLaunchKernelGGL((phat_kernel<VEC>), dim3(C, gamma + 1, B), dim3(TPB), 0, s, z, y, gamma, V,
                      invT2, eta2, C, zstat, ystat, sstat, rowtab);
-  hipLaunchKernelGGL((decide_kernel<VEC>), dim3(C, B), dim3(TPB), 0, s, z, y, draft, r, gamma, V,
-                     invT2, eta2, C, sstat, rowtab, wsm, tstar, n_accept, out_tokens, ratio_out,
-                     p_hat_out);
-  hipLaunchKernelGGL((draw_kernel<VEC>), dim3(B), dim3(TPB), (size_t)C * 2 * sizeof(float), s, z,
-                     y, u, gamma, V, invT2, eta2, C, rowtab, wsm, tstar, out_tokens);
+  hipLaunchKernelGGL((decide_kernel<VEC>), dim3(C, B), dim3(TPB), (size_t)C * 2 * sizeof(float),
+                     s, z, y, draft, r, gamma, V, invT2, eta2, C, sstat, rowtab, wsm, arrivals,
+                     u, n_accept, out_tokens, ratio_out, p_hat_out);
   return hipGetLastError();
 }
 

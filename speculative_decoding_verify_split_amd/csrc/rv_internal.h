@@ -55,9 +55,9 @@ struct AcceptLayout {
   size_t zstat;        // [B][gamma+1][C][2]  (max, sum) of z/T in log2 units
   size_t ystat;        // [B][gamma][C][2]
   size_t sstat;        // [B][gamma][C][2]    of s = z/T + eta (q - p)
-  size_t rowtab;       // [B][3][gamma+1]     base-2 LSE of z/T, y/T and s per row
+  size_t rowtab;       // [B][2][gamma+1]     base-2 LSE of z/T and y/T per row
   size_t wsum;         // [B][C][2]           residual and p_hat weight per chunk
-  size_t tstar;        // [B] int32           row of the draw (-1: bad draft id)
+  size_t arrivals;     // [B] uint32          chunks done with their draw weight
   size_t words;        // total
 };
 AcceptLayout accept_layout(int B, int gamma, int V);

@@ -112,10 +112,10 @@ AcceptLayout accept_layout(int B, int gamma, int V) {
   L.sstat = off;
   off += round_words((size_t)B * gamma * C * 2);
   L.rowtab = off;
-  off += round_words((size_t)B * 3 * (gamma + 1));
+  off += round_words((size_t)B * 2 * (gamma + 1));
   L.wsum = off;
   off += round_words((size_t)B * C * 2);
-  L.tstar = off;
+  L.arrivals = off;
   off += round_words((size_t)B);
   L.words = off;
   return L;
