@@ -100,6 +100,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of host time for the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay measurement reported beside the eager one")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -164,6 +166,35 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
+    graph = None
+    if not args.no_graph:
+        # The same steps captured once per rotated copy and replayed: the
+        # library only enqueues kernels on the caller's stream.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(R):
+                step(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for i in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        for i in range(K):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        g_el = time.perf_counter() - g0
+        graph = {"steps_per_s": K / g_el, "ms_per_step": g_el * 1e3 / K,
+                 "note": "same K steps replayed from HIP graphs (one per rotated copy), "
+                         "after the timed eager region"}
+
     prefix_ms = [e[0].elapsed_time(e[1]) for e in evs]
     attn_ms = [e[0].elapsed_time(e[2]) for e in evs]
     acc_ms = [e[2].elapsed_time(e[3]) for e in evs]
@@ -206,6 +237,7 @@ def main():
                      "kernel": "spec_attn_prefix (history pass)",
                      "algorithmic_bytes_per_launch": kv_bytes},
         "mean_n_accept": float(np.mean(n_acc)),
+        "graph_replay": graph,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
