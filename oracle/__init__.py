@@ -31,6 +31,10 @@ What it computes, and from which passage:
 All floating point is IEEE binary64.  bf16 inputs arrive as raw uint16 bit
 patterns and are widened exactly; fp32 inputs are widened exactly.
 
+Blog section 2.4 also prints a tail-preserving adjustment of p_hat and a
+different residual; both are available as options of ``rapid_accept_ref``
+(off by default) with the readings stated in ``rapid``.
+
 Every function is pinned by ``-m "not gpu"`` tests against facts fixed
 outside this package (library routines, closed forms, brute force, the
 fixed points the pages state, exact enumeration and Monte-Carlo of the
@@ -51,4 +55,5 @@ from .rapid import (  # noqa: F401
     retrieval_augmented_target,
     inverse_cdf_ref,
     rapid_accept_ref,
+    tail_preserve_ref,
 )

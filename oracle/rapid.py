@@ -20,7 +20,7 @@ Readings where the pages are silent or disagree (each restated where used):
   for the target).
 * The residual on rejection is norm(max(p_hat - q, 0)), i.e. the background
   rule with p replaced by p_hat.  (Blog section 2.4 also prints a different
-  residual and a tail-preserving rule; neither is part of this step.)
+  residual and a tail-preserving rule; both are options, off by default.)
 * When all gamma drafts are accepted, a bonus token is drawn from the target
   distribution of the last row, p_gamma = softmax(z_gamma/T), with u_gamma.
 * The acceptance inequality is inclusive (r <= ratio), with r in [0, 1).
@@ -29,6 +29,15 @@ Readings where the pages are silent or disagree (each restated where used):
   rounding leaves no such k, pick the largest k with w_k > 0.
 * A rejected row with W == 0 cannot happen in exact arithmetic (W == 0 forces
   p_hat == q, hence ratio 1); if it did, the token is drawn from p_hat.
+
+Two further rules printed in blog section 2.4, off by default:
+* tail preservation: every entry of p_hat below 0.1 times its largest entry
+  is replaced by the target's p; the page states no renormalisation, but
+  without one p_hat is no distribution, so the result is renormalised.
+* the printed residual norm(max(p - p_hat, p - q)) = norm(p - min(p_hat, q)):
+  its entries can be negative and the page gives no clip, so it is clipped
+  at zero.  The page's claim that the output then follows p holds exactly
+  when p >= min(p_hat, q) everywhere (no clipping needed).
 """
 
 import numpy as np
@@ -62,6 +71,16 @@ def retrieval_augmented_target(z_row, y_row, T, eta):
     return p, q, softmax_ref(s)
 
 
+def tail_preserve_ref(p, p_hat, frac=0.1):
+    """Blog section 2.4's tail rule: p_hat_k := p_k where
+    p_hat_k < frac * max_j p_hat_j, then renormalise."""
+    p = np.asarray(p, dtype=np.float64)
+    p_hat = np.asarray(p_hat, dtype=np.float64)
+    keep = p_hat >= frac * np.max(p_hat)
+    adj = np.where(keep, p_hat, p)
+    return adj / np.sum(adj)
+
+
 def inverse_cdf_ref(w, u):
     """Inverse-CDF draw from the unnormalised weights w with uniform u.
 
@@ -80,8 +99,13 @@ def inverse_cdf_ref(w, u):
     return k, C, W
 
 
-def rapid_accept_ref(z, y, draft, r, u, T, eta):
+def rapid_accept_ref(z, y, draft, r, u, T, eta, tail_preserve=False, residual="p_hat"):
     """One verify step of RAPID's acceptance, per sequence, step by step.
+
+    tail_preserve  apply the tail rule to p_hat (and use it everywhere p_hat
+                   is used: ratios, residual, p_hat output)
+    residual       "p_hat": max(p_hat - q, 0) (the background rule with p
+                   replaced by p_hat); "printed": max(p - min(p_hat, q), 0)
 
     z     [B, gamma+1, V] target logits (row t scores the token after row t)
     y     [B, gamma, V]   draft logits; draft[b, t] was drawn from softmax(y[b,t]/T)
@@ -107,20 +131,25 @@ def rapid_accept_ref(z, y, draft, r, u, T, eta):
         raise ValueError("y must be [B, gamma, V]")
     if not (T > 0):
         raise ValueError("T must be positive")
+    if residual not in ("p_hat", "printed"):
+        raise ValueError("residual must be 'p_hat' or 'printed'")
     n_accept = np.zeros(B, dtype=np.int64)
     out_tokens = np.full((B, gamma + 1), -1, dtype=np.int64)
     ratio = np.zeros((B, gamma))
     p_hat_all = np.zeros((B, gamma, V))
     draws = []
     for b in range(B):
-        q_rows = []
+        q_rows, p_rows = [], []
         for t in range(gamma):
             x = int(draft[b, t])
             if not (0 <= x < V):
                 raise ValueError("draft token id out of range")
-            _, q, p_hat = retrieval_augmented_target(z[b, t], y[b, t], T, eta)
+            p, q, p_hat = retrieval_augmented_target(z[b, t], y[b, t], T, eta)
+            if tail_preserve:
+                p_hat = tail_preserve_ref(p, p_hat)
             p_hat_all[b, t] = p_hat
             q_rows.append(q)
+            p_rows.append(p)
             ratio[b, t] = min(1.0, p_hat[x] / q[x])
         # First-reject cut: keep drafts while r_t <= ratio_t.
         t_star = gamma
@@ -133,7 +162,11 @@ def rapid_accept_ref(z, y, draft, r, u, T, eta):
         out_tokens[b, :t_star] = draft[b, :t_star]
         ub = float(u[b, t_star])
         if t_star < gamma:
-            w = np.maximum(p_hat_all[b, t_star] - q_rows[t_star], 0.0)
+            if residual == "p_hat":
+                w = np.maximum(p_hat_all[b, t_star] - q_rows[t_star], 0.0)
+            else:
+                w = np.maximum(p_rows[t_star] - np.minimum(p_hat_all[b, t_star], q_rows[t_star]),
+                               0.0)
             kind = "residual"
             if not np.any(w > 0):
                 w = p_hat_all[b, t_star]
