@@ -189,6 +189,34 @@ rv_status rapid_accept(const float* z, const float* y, const int32_t* draft, con
                        float* p_hat_out, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/*
+ * Options of rapid_accept_ex: RAPID blog post, section 2.4 prints two more
+ * inference rules.
+ *   RV_ACCEPT_TAIL_PRESERVE    every entry of p_hat below 0.1 x max p_hat
+ *                              takes the target's p, and the result is
+ *                              renormalised (the page states no
+ *                              renormalisation; without one p_hat is not a
+ *                              distribution).  The adjusted p_hat is used in
+ *                              the ratios, the residual and p_hat_out.
+ *   RV_ACCEPT_PRINTED_RESIDUAL on rejection draw from the printed residual
+ *                              norm(max(p - p_hat, p - q)) =
+ *                              norm(p - min(p_hat, q)), clipped at zero
+ *                              (its entries can be negative; the page gives
+ *                              no clip).
+ */
+#define RV_ACCEPT_TAIL_PRESERVE 1u
+#define RV_ACCEPT_PRINTED_RESIDUAL 2u
+
+/*
+ * rapid_accept_ex -- rapid_accept with options (flags = 0 is rapid_accept).
+ * Same arguments and workspace; unknown flag bits -> RV_ERR_VALUE.
+ */
+rv_status rapid_accept_ex(const float* z, const float* y, const int32_t* draft, const float* r,
+                          const float* u, int B, int gamma, int V, float T, float eta,
+                          unsigned flags, int32_t* n_accept, int32_t* out_tokens,
+                          float* ratio_out, float* p_hat_out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

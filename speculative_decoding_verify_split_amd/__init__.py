@@ -11,7 +11,10 @@ from .rapid_verify import (  # noqa: F401
     RapidVerifyError,
     load_library,
     lse_merge,
+    RV_ACCEPT_PRINTED_RESIDUAL,
+    RV_ACCEPT_TAIL_PRESERVE,
     rapid_accept,
+    rapid_accept_ex,
     rapid_accept_workspace_size,
     rv_prefix_default_split,
     rv_status_string,

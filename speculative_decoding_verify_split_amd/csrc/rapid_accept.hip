@@ -11,11 +11,17 @@
 //   stats_kernel   (chunk, row, b): max and sum of 2^(x - max) of z/T (rows
 //                  0..gamma) and y/T (rows 0..gamma-1), base-2 units
 //   phat_kernel    (chunk, t, b):   the same for s = z/T + eta (q - p)
+//   tail_kernel    (chunk, t, b):   only with RV_ACCEPT_TAIL_PRESERVE (blog
+//                  section 2.4's tail rule): per chunk, the sum of the
+//                  tail-adjusted row (p_hat where p_hat >= 0.1 max p_hat,
+//                  p elsewhere), from which decide_kernel renormalises
 //   decide_kernel  (chunk, b):      every chunk recomputes the gamma ratios
 //                  min(1, p_hat_t[x_t]/q_t[x_t]) and the first-reject cut t*;
 //                  chunk 0 writes n_accept, the accepted tokens and the
 //                  ratios; every chunk writes its share of the draw weights
-//                  (max(p_hat - q, 0) at t* < gamma, p_gamma otherwise) and,
+//                  (max(p_hat - q, 0) at t* < gamma, or with
+//                  RV_ACCEPT_PRINTED_RESIDUAL section 2.4's printed
+//                  max(p - min(p_hat, q), 0); p_gamma otherwise) and,
 //                  on request, p_hat.  The last chunk to finish (one
 //                  per-sequence arrival counter) then draws the token by
 //                  inverse CDF with the caller's uniform: chunk -> wave ->
@@ -90,7 +96,8 @@ __device__ __forceinline__ void lse_pair_merge(float& m, float& l, float mo, flo
 // symmetric lane pairings (DPP quad permutes and mirrors, then the row-swap
 // permutes).  Every lane of the group returns the same value.
 template <int width>
-__device__ __forceinline__ float group_combine(const float* __restrict__ st, int C, int j) {
+__device__ __forceinline__ float group_combine(const float* __restrict__ st, int C, int j,
+                                               float* max_out = nullptr) {
   static_assert(width == 16 || width == 64, "group width");
   float m = -INFINITY, l = 0.f;
   for (int c = j; c < C; c += width) lse_pair_merge(m, l, st[2 * c], st[2 * c + 1]);
@@ -107,7 +114,16 @@ __device__ __forceinline__ float group_combine(const float* __restrict__ st, int
     m = a.x; l = c.x;
     lse_pair_merge(m, l, a.y, c.y);
   }
+  if (max_out) *max_out = m;
   return m + log2_hw(l);
+}
+
+// Sum of st[c], c < C, by a 16-lane group: lane j adds c = j, j + 16, ... in
+// order, then the group adds by symmetric pairings; all 16 lanes agree.
+__device__ __forceinline__ float group16_sum(const float* __restrict__ st, int C, int j) {
+  float v = 0.f;
+  for (int c = j; c < C; c += 16) v += st[c];
+  return row16_sum(v);
 }
 
 // p, q and s/ln2 of one vocabulary entry.  x2 = z/T/ln2, lz = log2 sum 2^x2,
@@ -223,22 +239,84 @@ __global__ __launch_bounds__(TPB) void phat_kernel(const float* __restrict__ z,
   }
 }
 
-// Row constants of one sequence in LDS: base-2 LSEs of z/T, y/T and s.
+// log2(0.1): the tail rule keeps p_hat_k when p_hat_k >= 0.1 max p_hat, i.e.
+// when s_k >= max s + log2(0.1) in base-2 units.
+constexpr float kLog2Tenth = -3.321928094887362f;
+
+// Row constants of one sequence in LDS: base-2 LSEs of z/T, y/T and s, and
+// for the tail rule each row's keep threshold on s and 1 / (sum of the
+// adjusted p_hat).
 struct RowLse {
   float lz[kMaxGamma + 1];
   float ly[kMaxGamma];
   float ls[kMaxGamma];
+  float thr[kMaxGamma];
+  float zinv[kMaxGamma];
+  unsigned flags;
 };
 
-// Draw weight of one entry at row ts: max(p_hat - q, 0) (kind 0) or p_hat
-// (kind 1) for a rejected draft row, p_gamma for the bonus row.
+// The (possibly tail-adjusted) p_hat of one entry of draft row t.
+__device__ __forceinline__ float p_hat_entry(float p, float s2, int t, const RowLse& rc) {
+  const float ph = exp2_hw(s2 - rc.ls[t]);
+  if (!(rc.flags & RV_ACCEPT_TAIL_PRESERVE)) return ph;
+  return (s2 >= rc.thr[t] ? ph : p) * rc.zinv[t];
+}
+
+// Draw weight of one entry at row ts: the residual (kind 0) or p_hat itself
+// (kind 1) for a rejected draft row, p_gamma for the bonus row.  The
+// residual is max(p_hat - q, 0), or with RV_ACCEPT_PRINTED_RESIDUAL
+// max(p - min(p_hat, q), 0).
 __device__ __forceinline__ float draw_weight(float zv, float yv, int ts, int gamma, int kind,
                                              float invT2, float eta2, const RowLse& rc) {
   if (ts == gamma) return exp2_hw(zv * invT2 - rc.lz[gamma]);
   float p, q, s2;
   pq_s(zv, yv, invT2, eta2, rc.lz[ts], rc.ly[ts], p, q, s2);
-  const float ph = exp2_hw(s2 - rc.ls[ts]);
-  return kind == 0 ? fmaxf(ph - q, 0.f) : ph;
+  const float ph = p_hat_entry(p, s2, ts, rc);
+  if (kind != 0) return ph;
+  return (rc.flags & RV_ACCEPT_PRINTED_RESIDUAL) ? fmaxf(p - fminf(ph, q), 0.f)
+                                                  : fmaxf(ph - q, 0.f);
+}
+
+// grid (C, gamma, B), RV_ACCEPT_TAIL_PRESERVE only: chunk sums of the
+// unnormalised tail-adjusted p_hat (p_hat where s >= max s + log2 0.1, else
+// p).  The row's LSE and max of s come from the same 16-lane combine the
+// decide kernel uses, so both kernels classify every entry identically.
+template <bool VEC>
+__global__ __launch_bounds__(TPB) void tail_kernel(const float* __restrict__ z,
+                                                   const float* __restrict__ y, int gamma, int V,
+                                                   float invT2, float eta2, int C,
+                                                   const float* __restrict__ sstat,
+                                                   const float* __restrict__ rowtab,
+                                                   float* __restrict__ tstat) {
+  const int c = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
+  __shared__ float sh[4];
+  const float* rt = rowtab + (size_t)b * 2 * (gamma + 1);
+  if (threadIdx.x < 16) {
+    float ms;
+    const float ls = group_combine<16>(sstat + ((size_t)b * gamma + t) * C * 2, C,
+                                       threadIdx.x, &ms);
+    if (threadIdx.x == 0) {
+      sh[0] = ls;
+      sh[1] = ms + kLog2Tenth;
+      sh[2] = rt[t];
+      sh[3] = rt[(gamma + 1) + t];
+    }
+  }
+  const int start = c * CH + threadIdx.x * PER;
+  float zx[PER], yx[PER];
+  load_run<VEC>(z + ((size_t)b * (gamma + 1) + t) * V, V, start, zx);
+  load_run<VEC>(y + ((size_t)b * gamma + t) * V, V, start, yx);
+  __syncthreads();
+  const float ls = sh[0], thr = sh[1], lz = sh[2], ly = sh[3];
+  float acc = 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    float p, q, s2;
+    pq_s(zx[e], yx[e], invT2, eta2, lz, ly, p, q, s2);
+    if (start + e < V) acc += (s2 >= thr) ? exp2_hw(s2 - ls) : p;
+  }
+  const float cs = block_sum(acc);
+  if (threadIdx.x == 0) tstat[((size_t)b * gamma + t) * C + c] = cs;
 }
 
 // Inverse CDF of the draw row ts of sequence b with the caller's uniform:
@@ -410,7 +488,8 @@ template <bool VEC>
 __global__ __launch_bounds__(TPB) void decide_kernel(
     const float* __restrict__ z, const float* __restrict__ y, const int32_t* __restrict__ draft,
     const float* __restrict__ r, int gamma, int V, float invT2, float eta2, int C,
-    const float* __restrict__ sstat, float* __restrict__ rowtab, float* __restrict__ wsum,
+    const float* __restrict__ sstat, const float* __restrict__ tstat, unsigned flags,
+    float* __restrict__ rowtab, float* __restrict__ wsum,
     uint32_t* __restrict__ arrivals, const float* __restrict__ u,
     int32_t* __restrict__ n_accept, int32_t* __restrict__ out_tokens,
     float* __restrict__ ratio_out, float* __restrict__ p_hat_out) {
@@ -430,11 +509,20 @@ __global__ __launch_bounds__(TPB) void decide_kernel(
     rc.lz[i] = rt[i];
     if (i < gamma) rc.ly[i] = rt[(gamma + 1) + i];
   }
+  if (threadIdx.x == 0) rc.flags = flags;
   {
     const int grp = threadIdx.x >> 4, j = threadIdx.x & 15;
     for (int t = grp; t < gamma; t += TPB / 16) {
-      const float ls = group_combine<16>(sstat + ((size_t)b * gamma + t) * C * 2, C, j);
-      if (j == 0) rc.ls[t] = ls;
+      float ms;
+      const float ls = group_combine<16>(sstat + ((size_t)b * gamma + t) * C * 2, C, j, &ms);
+      float zsum = 1.f;
+      if (flags & RV_ACCEPT_TAIL_PRESERVE)
+        zsum = group16_sum(tstat + ((size_t)b * gamma + t) * C, C, j);
+      if (j == 0) {
+        rc.ls[t] = ls;
+        rc.thr[t] = ms + kLog2Tenth;
+        rc.zinv[t] = 1.0f / zsum;
+      }
     }
   }
   __syncthreads();
@@ -449,7 +537,7 @@ __global__ __launch_bounds__(TPB) void decide_kernel(
         float p, q, s2;
         pq_s(z[((size_t)b * (gamma + 1) + lane) * V + x], y[((size_t)b * gamma + lane) * V + x],
              invT2, eta2, rc.lz[lane], rc.ly[lane], p, q, s2);
-        const float ph = exp2_hw(s2 - rc.ls[lane]);
+        const float ph = p_hat_entry(p, s2, lane, rc);
         ratio = fminf(1.0f, ph / q);
         acc = rv <= ratio;
       }
@@ -480,7 +568,7 @@ __global__ __launch_bounds__(TPB) void decide_kernel(
       for (int e = 0; e < PER; ++e) {
         float p, q, s2;
         pq_s(zx[e], yx[e], invT2, eta2, rc.lz[t], rc.ly[t], p, q, s2);
-        if (start + e < V) dst[start + e] = exp2_hw(s2 - rc.ls[t]);
+        if (start + e < V) dst[start + e] = p_hat_entry(p, s2, t, rc);
       }
     }
   }
@@ -524,7 +612,7 @@ __global__ __launch_bounds__(TPB) void decide_kernel(
 template <bool VEC>
 hipError_t launch_accept(const float* z, const float* y, const int32_t* draft, const float* r,
                          const float* u, int B, int gamma, int V, float invT2, float eta2,
-                         const AcceptLayout& L, float* ws, int32_t* n_accept,
+                         unsigned flags, const AcceptLayout& L, float* ws, int32_t* n_accept,
                          int32_t* out_tokens, float* ratio_out, float* p_hat_out,
                          hipStream_t s) {
   const int C = L.chunks;
@@ -532,15 +620,19 @@ hipError_t launch_accept(const float* z, const float* y, const int32_t* draft, c
   float* ystat = ws + L.ystat;
   float* sstat = ws + L.sstat;
   float* rowtab = ws + L.rowtab;
+  float* tstat = ws + L.tstat;
   float* wsm = ws + L.wsum;
   uint32_t* arrivals = reinterpret_cast<uint32_t*>(ws + L.arrivals);
   hipLaunchKernelGGL((stats_kernel<VEC>), dim3(C, 2 * gamma + 1, B), dim3(TPB), 0, s, z, y, gamma,
                      V, invT2, C, zstat, ystat, arrivals);
   hipLaunchKernelGGL((phat_kernel<VEC>), dim3(C, gamma + 1, B), dim3(TPB), 0, s, z, y, gamma, V,
                      invT2, eta2, C, zstat, ystat, sstat, rowtab);
+  if (flags & RV_ACCEPT_TAIL_PRESERVE)
+    hipLaunchKernelGGL((tail_kernel<VEC>), dim3(C, gamma, B), dim3(TPB), 0, s, z, y, gamma, V,
+                       invT2, eta2, C, sstat, rowtab, tstat);
   hipLaunchKernelGGL((decide_kernel<VEC>), dim3(C, B), dim3(TPB), (size_t)C * 2 * sizeof(float),
-                     s, z, y, draft, r, gamma, V, invT2, eta2, C, sstat, rowtab, wsm, arrivals,
-                     u, n_accept, out_tokens, ratio_out, p_hat_out);
+                     s, z, y, draft, r, gamma, V, invT2, eta2, C, sstat, tstat, flags, rowtab,
+                     wsm, arrivals, u, n_accept, out_tokens, ratio_out, p_hat_out);
   return hipGetLastError();
 }
 
@@ -552,13 +644,13 @@ extern "C" size_t rapid_accept_workspace_size(int B, int gamma, int V) {
   return rv::accept_layout(B, gamma, V).words * 4;
 }
 
-extern "C" rv_status rapid_accept(const float* z, const float* y, const int32_t* draft,
-                                  const float* r, const float* u, int B, int gamma, int V,
-                                  float T, float eta, int32_t* n_accept, int32_t* out_tokens,
-                                  float* ratio_out, float* p_hat_out, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
-  rv_status st = rv::check_accept(z, y, draft, r, u, B, gamma, V, T, eta, n_accept, out_tokens,
-                                  workspace, workspace_bytes);
+extern "C" rv_status rapid_accept_ex(const float* z, const float* y, const int32_t* draft,
+                                     const float* r, const float* u, int B, int gamma, int V,
+                                     float T, float eta, unsigned flags, int32_t* n_accept,
+                                     int32_t* out_tokens, float* ratio_out, float* p_hat_out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  rv_status st = rv::check_accept(z, y, draft, r, u, B, gamma, V, T, eta, flags, n_accept,
+                                  out_tokens, workspace, workspace_bytes);
   if (st != RV_OK) return st;
   const rv::AcceptLayout L = rv::accept_layout(B, gamma, V);
   const double log2e = 1.4426950408889634;
@@ -568,14 +660,23 @@ extern "C" rv_status rapid_accept(const float* z, const float* y, const int32_t*
   float* ws = static_cast<float*>(workspace);
   hipError_t e;
   if (V % 4 == 0)
-    e = rv::launch_accept<true>(z, y, draft, r, u, B, gamma, V, invT2, eta2, L, ws, n_accept,
-                                out_tokens, ratio_out, p_hat_out, s);
+    e = rv::launch_accept<true>(z, y, draft, r, u, B, gamma, V, invT2, eta2, flags, L, ws,
+                                n_accept, out_tokens, ratio_out, p_hat_out, s);
   else
-    e = rv::launch_accept<false>(z, y, draft, r, u, B, gamma, V, invT2, eta2, L, ws, n_accept,
-                                 out_tokens, ratio_out, p_hat_out, s);
+    e = rv::launch_accept<false>(z, y, draft, r, u, B, gamma, V, invT2, eta2, flags, L, ws,
+                                 n_accept, out_tokens, ratio_out, p_hat_out, s);
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return RV_ERR_HIP;
   }
   return RV_OK;
+}
+
+extern "C" rv_status rapid_accept(const float* z, const float* y, const int32_t* draft,
+                                  const float* r, const float* u, int B, int gamma, int V,
+                                  float T, float eta, int32_t* n_accept, int32_t* out_tokens,
+                                  float* ratio_out, float* p_hat_out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return rapid_accept_ex(z, y, draft, r, u, B, gamma, V, T, eta, 0u, n_accept, out_tokens,
+                         ratio_out, p_hat_out, workspace, workspace_bytes, stream);
 }

@@ -56,14 +56,17 @@ struct AcceptLayout {
   size_t ystat;        // [B][gamma][C][2]
   size_t sstat;        // [B][gamma][C][2]    of s = z/T + eta (q - p)
   size_t rowtab;       // [B][2][gamma+1]     base-2 LSE of z/T and y/T per row
+  size_t tstat;        // [B][gamma][C]       chunk sums of the tail-adjusted p_hat
   size_t wsum;         // [B][C][2]           residual and p_hat weight per chunk
   size_t arrivals;     // [B] uint32          chunks done with their draw weight
   size_t words;        // total
 };
 AcceptLayout accept_layout(int B, int gamma, int V);
 
+constexpr unsigned kAcceptFlags = RV_ACCEPT_TAIL_PRESERVE | RV_ACCEPT_PRINTED_RESIDUAL;
+
 rv_status check_accept(const float* z, const float* y, const int32_t* draft, const float* r,
-                       const float* u, int B, int gamma, int V, float T, float eta,
+                       const float* u, int B, int gamma, int V, float T, float eta, unsigned flags,
                        const int32_t* n_accept, const int32_t* out_tokens, const void* workspace,
                        size_t workspace_bytes);
 

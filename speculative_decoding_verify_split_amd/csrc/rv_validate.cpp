@@ -113,6 +113,8 @@ AcceptLayout accept_layout(int B, int gamma, int V) {
   off += round_words((size_t)B * gamma * C * 2);
   L.rowtab = off;
   off += round_words((size_t)B * 2 * (gamma + 1));
+  L.tstat = off;
+  off += round_words((size_t)B * gamma * C);
   L.wsum = off;
   off += round_words((size_t)B * C * 2);
   L.arrivals = off;
@@ -122,7 +124,7 @@ AcceptLayout accept_layout(int B, int gamma, int V) {
 }
 
 rv_status check_accept(const float* z, const float* y, const int32_t* draft, const float* r,
-                       const float* u, int B, int gamma, int V, float T, float eta,
+                       const float* u, int B, int gamma, int V, float T, float eta, unsigned flags,
                        const int32_t* n_accept, const int32_t* out_tokens, const void* workspace,
                        size_t workspace_bytes) {
   if (!z || !y || !draft || !r || !u || !n_accept || !out_tokens || !workspace)
@@ -130,6 +132,7 @@ rv_status check_accept(const float* z, const float* y, const int32_t* draft, con
   if (B < 1 || gamma < 1 || V < 2) return RV_ERR_SHAPE;
   if (gamma > kMaxGamma || V > kMaxVocab || B > 65535) return RV_ERR_UNSUPPORTED;
   if (!(T > 0.0f) || !isfinite(T) || !isfinite(eta)) return RV_ERR_VALUE;
+  if (flags & ~kAcceptFlags) return RV_ERR_VALUE;
   if (!aligned16(z) || !aligned16(y) || !aligned16(workspace)) return RV_ERR_ALIGNMENT;
   if (workspace_bytes < accept_layout(B, gamma, V).words * 4) return RV_ERR_WORKSPACE;
   return RV_OK;

@@ -13,8 +13,11 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librapid_verify.so")
 
-_c_i32p = ctypes.c_void_p
 _lib = None
+
+# rapid_accept_ex options (RAPID blog section 2.4's two further rules)
+RV_ACCEPT_TAIL_PRESERVE = 1
+RV_ACCEPT_PRINTED_RESIDUAL = 2
 
 
 class RapidVerifyError(RuntimeError):
@@ -52,6 +55,9 @@ def load_library():
     lib.rapid_accept.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp, vp, vp, vp,
                                  sz, vp]
     lib.rapid_accept.restype = i32
+    lib.rapid_accept_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, ctypes.c_uint,
+                                    vp, vp, vp, vp, vp, sz, vp]
+    lib.rapid_accept_ex.restype = i32
     _lib = lib
     return lib
 
@@ -167,11 +173,7 @@ def rapid_accept_workspace_size(B, gamma, V):
     return int(load_library().rapid_accept_workspace_size(B, gamma, V))
 
 
-def rapid_accept(z, y, draft, r, u, T, eta, n_accept, out_tokens, workspace, ratio_out=None,
-                 p_hat_out=None, stream=None):
-    """Vocabulary pass.  z fp32 [B,g+1,V]; y fp32 [B,g,V]; draft int32 [B,g];
-    r fp32 [B,g]; u fp32 [B,g+1]; n_accept int32 [B]; out_tokens int32 [B,g+1];
-    workspace uint8 tensor of rapid_accept_workspace_size bytes."""
+def _accept_args(z, y, draft, r, u, n_accept, out_tokens, workspace, ratio_out, p_hat_out):
     import torch
     _need(z, "z", torch.float32)
     B, g1, V = z.shape
@@ -187,7 +189,29 @@ def rapid_accept(z, y, draft, r, u, T, eta, n_accept, out_tokens, workspace, rat
         _need(ratio_out, "ratio_out", torch.float32, (B, g))
     if p_hat_out is not None:
         _need(p_hat_out, "p_hat_out", torch.float32, (B, g, V))
+    return B, g, V
+
+
+def rapid_accept(z, y, draft, r, u, T, eta, n_accept, out_tokens, workspace, ratio_out=None,
+                 p_hat_out=None, stream=None):
+    """Vocabulary pass.  z fp32 [B,g+1,V]; y fp32 [B,g,V]; draft int32 [B,g];
+    r fp32 [B,g]; u fp32 [B,g+1]; n_accept int32 [B]; out_tokens int32 [B,g+1];
+    workspace uint8 tensor of rapid_accept_workspace_size bytes."""
+    B, g, V = _accept_args(z, y, draft, r, u, n_accept, out_tokens, workspace, ratio_out,
+                           p_hat_out)
     _check(load_library().rapid_accept(
         _ptr(z), _ptr(y), _ptr(draft), _ptr(r), _ptr(u), B, g, V, float(T), float(eta),
         _ptr(n_accept), _ptr(out_tokens), _ptr(ratio_out), _ptr(p_hat_out), _ptr(workspace),
         workspace.numel(), _stream(stream)), "rapid_accept")
+
+
+def rapid_accept_ex(z, y, draft, r, u, T, eta, flags, n_accept, out_tokens, workspace,
+                    ratio_out=None, p_hat_out=None, stream=None):
+    """rapid_accept with options: RV_ACCEPT_TAIL_PRESERVE and/or
+    RV_ACCEPT_PRINTED_RESIDUAL."""
+    B, g, V = _accept_args(z, y, draft, r, u, n_accept, out_tokens, workspace, ratio_out,
+                           p_hat_out)
+    _check(load_library().rapid_accept_ex(
+        _ptr(z), _ptr(y), _ptr(draft), _ptr(r), _ptr(u), B, g, V, float(T), float(eta),
+        int(flags), _ptr(n_accept), _ptr(out_tokens), _ptr(ratio_out), _ptr(p_hat_out),
+        _ptr(workspace), workspace.numel(), _stream(stream)), "rapid_accept_ex")

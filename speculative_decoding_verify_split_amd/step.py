@@ -31,7 +31,7 @@ class VerifyStep:
     """
 
     def __init__(self, attn, vocab=None, split=None, want_ratio=True, want_p_hat=False,
-                 device="cuda"):
+                 device="cuda", flags=0):
         import torch
         self.device = device
         self.attn = attn
@@ -60,6 +60,7 @@ class VerifyStep:
             self.out = torch.empty((B, Hq, n, d), dtype=torch.bfloat16, device=device)
             self.lse_out = torch.empty((B, Hq, n), dtype=f32, device=device)
         self.vocab = vocab
+        self.flags = int(flags)
         if vocab is not None:
             Bv, g1, V = vocab.z.shape
             self.gamma, self.V = g1 - 1, V
@@ -90,9 +91,15 @@ class VerifyStep:
                      stream)
 
     def accept(self, z=None, y=None, stream=None):
-        rv.rapid_accept(self.z if z is None else z, self.y if y is None else y, self.draft, self.r,
-                        self.u, self.T, self.eta, self.n_accept, self.out_tokens, self.workspace,
-                        self.ratio, self.p_hat, stream)
+        z = self.z if z is None else z
+        y = self.y if y is None else y
+        if self.flags:
+            rv.rapid_accept_ex(z, y, self.draft, self.r, self.u, self.T, self.eta, self.flags,
+                               self.n_accept, self.out_tokens, self.workspace, self.ratio,
+                               self.p_hat, stream)
+        else:
+            rv.rapid_accept(z, y, self.draft, self.r, self.u, self.T, self.eta, self.n_accept,
+                            self.out_tokens, self.workspace, self.ratio, self.p_hat, stream)
 
     def run(self, stream=None):
         if self.attn is not None:

@@ -163,6 +163,13 @@ def test_accept_validation(lib):
     assert _accept(lib, ws=MIS) == RV_ERR_ALIGNMENT
 
 
+def test_accept_ex_rejects_unknown_flags(lib):
+    args = [P, P, P, P, P, 1, 4, 32000, 1.0, 0.5]
+    assert lib.rapid_accept_ex(*args, 4, P, P, None, None, P, 1 << 20, None) == RV_ERR_VALUE
+    assert lib.rapid_accept_ex(*args, 0x80000000, P, P, None, None, P, 1 << 20, None) == RV_ERR_VALUE
+    assert lib.rapid_accept_ex(None, *args[1:], 1, P, P, None, None, P, 1 << 20, None) == RV_ERR_NULL
+
+
 def test_workspace_size_host_arithmetic(lib):
     a = rv.rapid_accept_workspace_size(1, 10, 128256)
     b = rv.rapid_accept_workspace_size(8, 10, 152064)

@@ -12,10 +12,13 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attn_keys_ref, attn_ref, bf16_bits_to_f64, block_visibility, rapid_accept_ref
+from oracle import (attn_keys_ref, attn_ref, bf16_bits_to_f64, block_visibility, rapid_accept_ref,
+                    retrieval_augmented_target)
 from oracle.compare import ATTN_ROW_TOL, P_HAT_TOL, attn_row_errors, compare_accept
 from workloads import (CONFIGS, config_attention, config_vocab, make_attention, make_vocab,
                        tree_parents)
+from speculative_decoding_verify_split_amd.rapid_verify import (RV_ACCEPT_PRINTED_RESIDUAL,
+                                                                RV_ACCEPT_TAIL_PRESERVE)
 from speculative_decoding_verify_split_amd.step import VerifyStep
 
 pytestmark = pytest.mark.gpu
@@ -149,15 +152,33 @@ def test_sm_scale_is_applied():
 
 # ------------------------------------------------------ vocabulary, small
 
-def _run_accept(vi, p_hat=True):
-    st = VerifyStep(None, vi, want_ratio=True, want_p_hat=p_hat)
+def _run_accept(vi, p_hat=True, flags=0):
+    st = VerifyStep(None, vi, want_ratio=True, want_p_hat=p_hat, flags=flags)
     st.accept()
     torch.cuda.synchronize()
     return st
 
 
-def _check_accept(vi, st, tag):
-    ref = rapid_accept_ref(vi.z, vi.y, vi.draft, vi.r, vi.u, vi.T, vi.eta)
+def _tail_margin(vi):
+    """Smallest relative distance of any p_hat entry to the tail threshold
+    0.1 max p_hat (oracle arithmetic); entries that close may be classified
+    either way by fp32 and fp64."""
+    m = np.inf
+    for b in range(vi.z.shape[0]):
+        for t in range(vi.y.shape[1]):
+            _, _, ph = retrieval_augmented_target(vi.z[b, t], vi.y[b, t], vi.T, vi.eta)
+            thr = 0.1 * ph.max()
+            m = min(m, np.min(np.abs(ph - thr)) / thr)
+    return m
+
+
+def _check_accept(vi, st, tag, flags=0):
+    tail = bool(flags & RV_ACCEPT_TAIL_PRESERVE)
+    ref = rapid_accept_ref(vi.z, vi.y, vi.draft, vi.r, vi.u, vi.T, vi.eta, tail_preserve=tail,
+                           residual="printed" if flags & RV_ACCEPT_PRINTED_RESIDUAL else "p_hat")
+    if tail and _tail_margin(vi) <= 1e-5:
+        announce("  %s: an entry lies within 1e-5 of the tail threshold; not compared" % tag)
+        return ref, None
     n_g = st.n_accept.cpu().numpy()
     tok = st.out_tokens.cpu().numpy()
     res = compare_accept(ref, n_g, tok, vi.r, vi.u)
@@ -297,6 +318,40 @@ def test_config_attention(name):
 @pytest.mark.timeout(1100)
 def test_config_attention_tree1m():
     _config_attention_check("tree1m")
+
+
+RULE_FLAGS = [RV_ACCEPT_TAIL_PRESERVE, RV_ACCEPT_PRINTED_RESIDUAL,
+              RV_ACCEPT_TAIL_PRESERVE | RV_ACCEPT_PRINTED_RESIDUAL]
+
+
+@pytest.mark.parametrize("flags", RULE_FLAGS)
+@pytest.mark.parametrize("case", VOCAB_CASES[:4] + [("V8192-g7-b5", VOCAB_CASES[5][1])],
+                         ids=[c[0] for c in VOCAB_CASES[:4]] + ["V8192-g7-b5"])
+def test_accept_rules_small(case, flags):
+    """RAPID blog section 2.4's tail rule and printed residual (flags)."""
+    name, kw = case
+    vi = make_vocab(**kw)
+    announce("rapid_accept_ex %s flags=%d" % (name, flags))
+    _check_accept(vi, _run_accept(vi, flags=flags), "%s flags=%d" % (name, flags), flags)
+
+
+def test_accept_rules_forced_rejections():
+    """Every sequence rejects its first draft, so every draw uses the rule's
+    residual."""
+    for flags in RULE_FLAGS:
+        vi = make_vocab(49, B=6, gamma=3, V=20000, z_sigma=3.0, noise=1.0, T=1.0, eta=1.0)
+        vi.r[:] = np.float32(1.0 - 2 ** -24)
+        announce("rapid_accept_ex forced rejections flags=%d" % flags)
+        ref, _ = _check_accept(vi, _run_accept(vi, flags=flags), "reject flags=%d" % flags, flags)
+        assert np.all(ref["n_accept"] <= 1)
+
+
+@pytest.mark.parametrize("flags", RULE_FLAGS)
+@pytest.mark.timeout(600)
+def test_config_vocab_rules(flags):
+    vi = config_vocab("llama8b", eta=2.0)
+    announce("rapid_accept_ex llama8b eta=2 flags=%d" % flags)
+    _check_accept(vi, _run_accept(vi, flags=flags), "llama8b flags=%d" % flags, flags)
 
 
 @pytest.mark.parametrize("name,eta", [("llama8b", 0.0), ("llama8b", 0.5), ("llama8b", 2.0),
