@@ -2,9 +2,10 @@
 """Verify-step benchmark on one MI355X.
 
 One step is the whole hot path on one batch of synthetic inputs:
-spec_attn_prefix (history pass over the KV cache), spec_attn_block (masked
-draft block), lse_merge, and rapid_accept (RAPID's vocabulary pass), back to
-back on one stream.  Default workload: the LLaMA-3.1-8B-shaped verify layer
+spec_attn_prefix (history pass over the KV cache), the masked draft block and
+the log-sum-exp merge (one spec_attn_block_merge call; --unfused runs
+spec_attn_block and lse_merge separately), and rapid_accept (RAPID's
+vocabulary pass), back to back on one stream.  Default workload: the LLaMA-3.1-8B-shaped verify layer
 (32 query / 8 kv heads, d=128, 131072-token bf16 KV cache, gamma=10, vocab
 128256, T=1, eta=0.5), inputs resident in HBM.  Three copies of the KV cache
 and of the logits rotate from step to step so that no step reads what the
@@ -102,6 +103,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay measurement reported beside the eager one")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run spec_attn_block and lse_merge as two calls")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -146,8 +149,13 @@ def main():
                             st.num_splits, st.o_part, st.lse_part, st.sm_scale)
         if ev is not None:
             ev[1].record()
-        rv.spec_attn_block(st.q, st.k_blk, st.v_blk, st.parent, st.o_blk, st.lse_blk, st.sm_scale)
-        rv.lse_merge(st.o_part, st.lse_part, st.o_blk, st.lse_blk, st.out, st.lse_out)
+        if args.unfused:
+            rv.spec_attn_block(st.q, st.k_blk, st.v_blk, st.parent, st.o_blk, st.lse_blk,
+                               st.sm_scale)
+            rv.lse_merge(st.o_part, st.lse_part, st.o_blk, st.lse_blk, st.out, st.lse_out)
+        else:
+            rv.spec_attn_block_merge(st.q, st.k_blk, st.v_blk, st.parent, st.o_part, st.lse_part,
+                                     st.out, st.lse_out, st.sm_scale)
         if ev is not None:
             ev[2].record()
         rv.rapid_accept(z, y, st.draft, st.r, st.u, st.T, st.eta, st.n_accept, st.out_tokens,
@@ -225,13 +233,18 @@ def main():
                    "head_dim": d, "kv_tokens": int(np.max(ai.seq_lens)), "block_rows": st.n,
                    "gamma": st.gamma, "vocab": st.V, "T": st.T, "eta": st.eta,
                    "split_len": st.split_len, "num_splits": st.num_splits,
-                   "rotated_copies": R, "parallelism": "single GPU"},
+                   "rotated_copies": R, "block_and_merge": "two calls" if args.unfused else
+                   "spec_attn_block_merge", "parallelism": "single GPU"},
         "kv_stream_GBps": kv_bytes / attn_s / 1e9,
         "kv_stream_frac_of_peak": kv_bytes / attn_s / 1e9 / HBM_PEAK_GBPS,
         "kernels_us": {"spec_attn_prefix": prefix_s * 1e6,
-                       "spec_attn_block+lse_merge": (attn_s - prefix_s) * 1e6,
+                       ("spec_attn_block+lse_merge" if args.unfused else
+                        "spec_attn_block_merge"): (attn_s - prefix_s) * 1e6,
                        "rapid_accept": float(np.mean(acc_ms)) * 1e3,
                        "device_step": float(np.mean(step_dev_ms)) * 1e3},
+        "device_step_us": {"median": float(np.median(step_dev_ms)) * 1e3,
+                           "p10": float(np.percentile(step_dev_ms, 10)) * 1e3,
+                           "p90": float(np.percentile(step_dev_ms, 90)) * 1e3},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": _traffic_per_launch(),
                      "kernel": "spec_attn_prefix (history pass)",

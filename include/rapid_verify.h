@@ -154,6 +154,24 @@ rv_status lse_merge(const float* o_part, const float* lse_part, int S, const flo
                     const float* lse_blk, int B, int Hq, int n, int d, void* out,
                     float* lse_out, void* stream);
 
+/*
+ * spec_attn_block_merge -- spec_attn_block and lse_merge in one pass (the
+ * same LongSpec section 2.3 split: masked block part, log-sum-exp merge with
+ * the history partials), for callers that need only the merged result: the
+ * block partial is computed where it is merged and never stored.
+ *
+ *   q, k_blk, v_blk, parent_host, sm_scale  as spec_attn_block
+ *   o_part, lse_part, S                     as lse_merge (from spec_attn_prefix)
+ *   out        bf16 [B, Hq, n, d]  (round to nearest even)
+ *   lse_out    fp32 [B, Hq, n] or NULL
+ * Same results as the two calls up to fp32 rounding order.  Supports d in
+ * {64, 128}, 1 <= n <= 64.
+ */
+rv_status spec_attn_block_merge(const void* q, const void* k_blk, const void* v_blk,
+                                const int32_t* parent_host, const float* o_part,
+                                const float* lse_part, int S, int B, int Hq, int Hkv, int n,
+                                int d, float sm_scale, void* out, float* lse_out, void* stream);
+
 /* Bytes of device workspace rapid_accept needs for (B, gamma, V). */
 size_t rapid_accept_workspace_size(int B, int gamma, int V);
 

@@ -20,5 +20,6 @@ from .rapid_verify import (  # noqa: F401
     rv_status_string,
     rv_version,
     spec_attn_block,
+    spec_attn_block_merge,
     spec_attn_prefix,
 )

@@ -2,23 +2,16 @@
 // keys under the speculative mask (LongSpec summary, gist.science, section 2.3
 // "Fast Tree Attention": only the few speculative tokens need a mask, and that
 // part gets a small dedicated kernel).  A chain uses the causal mask (row i
-// sees rows j <= i); a tree lets a node see itself and its ancestors.
-//
-// With at most 64 block keys per row there is no dense contraction worth a
-// matrix-core tile, so this runs on the vector ALU in fp32: one wave per
-// output row (four rows per workgroup).  Lane j scores block key j (if the
-// row's mask bit j is set), the wave reduces max and sum, and then each lane
-// owns d/64 output columns of P V.  Reductions use a fixed butterfly and the
-// P V sum runs over keys in ascending order, so results are bit-deterministic.
+// sees rows j <= i); a tree lets a node see itself and its ancestors.  One
+// wave per output row (four rows per workgroup); the per-row routine is in
+// block_row.h.
 
+#include "block_row.h"
 #include "rv_device.h"
 #include "rv_internal.h"
 
 namespace rv {
 namespace {
-
-__device__ __forceinline__ float bf16_lo(int w) { return __uint_as_float((uint32_t)w << 16); }
-__device__ __forceinline__ float bf16_hi(int w) { return __uint_as_float((uint32_t)w & 0xffff0000u); }
 
 // grid (ceil(n / 4), B * Hq): wave w of workgroup x handles block row 4x + w
 // of query head h of sequence b (blockIdx.y = b * Hq + h).
@@ -40,67 +33,12 @@ __global__ __launch_bounds__(256) void block_kernel(const uint16_t* __restrict__
   const int Hkv = Hq / G;
   const size_t kv0 = ((size_t)b * Hkv + h / G) * n * D;
   const size_t row = (size_t)bh * n + i;  // layout of q, o_blk and lse_blk
-
-  // V columns of this lane for the first 8 keys, requested up front.
-  const uint16_t* vcol = vb + kv0 + lane * PER;
-  typedef uint16_t u16xP __attribute__((ext_vector_type(PER)));
-  u16xP vpre[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    vpre[j] = (j < n) ? *reinterpret_cast<const u16xP*>(vcol + (size_t)j * D) : u16xP{};
-
-  float s = -INFINITY;
-  if (lane < n && ((mask.bits[i] >> lane) & 1ull)) {
-    const i32x4* kr = reinterpret_cast<const i32x4*>(kb + kv0 + (size_t)lane * D);
-    const i32x4* qr = reinterpret_cast<const i32x4*>(q + row * D);
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
-      const i32x4 kk = kr[c];
-      const i32x4 qq = qr[c];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[e] = fmaf(bf16_lo(qq[e]), bf16_lo(kk[e]), acc[e]);
-        acc[e] = fmaf(bf16_hi(qq[e]), bf16_hi(kk[e]), acc[e]);
-      }
-    }
-    s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * scale_log2;
-  }
-  const float m = wave_max(s);  // finite: a row always sees itself
-  const float p = (s == -INFINITY) ? 0.f : exp2_hw(s - m);
-  const float l = wave_sum(p);
-
-  // P V over keys in ascending order (masked keys have p = 0).
-  float o[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) o[e] = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float pj = __shfl(p, j < n ? j : 0, 64);
-#pragma unroll
-    for (int e = 0; e < PER; ++e)
-      o[e] = fmaf(j < n ? pj : 0.f, __uint_as_float((uint32_t)vpre[j][e] << 16), o[e]);
-  }
-  for (int j0 = 8; j0 < n; j0 += 8) {
-    u16xP vv[8];
-    float pj[8];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int j = j0 + jj;  // uniform across the wave
-      pj[jj] = __shfl(p, j < n ? j : 0, 64);
-      vv[jj] = (j < n) ? *reinterpret_cast<const u16xP*>(vcol + (size_t)j * D) : u16xP{};
-    }
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-#pragma unroll
-      for (int e = 0; e < PER; ++e)
-        o[e] = fmaf(j0 + jj < n ? pj[jj] : 0.f, __uint_as_float((uint32_t)vv[jj][e] << 16), o[e]);
-  }
-  const float inv = 1.0f / l;
+  float o[PER], lse2;
+  block_row_attention<D>(q + row * D, kb + kv0, vb + kv0, mask.bits[i], n, scale_log2, o, lse2);
   float* op = o_blk + row * D + lane * PER;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) op[e] = o[e] * inv;
-  if (lane == 0) lse_blk[row] = (m + log2_hw(l)) * kLn2;
+  for (int e = 0; e < PER; ++e) op[e] = o[e];
+  if (lane == 0) lse_blk[row] = lse2 * kLn2;
 }
 
 }  // namespace

@@ -4,31 +4,35 @@
 // against the full-context target; section 2.4, the retrieval-augmented target
 // p_hat = softmax(z/T + eta (q - p)) used in place of p at inference).
 //
-// Each row is a V-long fp32 stream (V ~ 1.3e5), so the pass is bandwidth-
-// and latency-bound; every row is cut into 4096-element chunks, one
-// 256-thread workgroup per chunk (16 contiguous elements per thread), and
+// Each row is a V-long fp32 stream (V ~ 1.3e5): little data, so the pass is
+// bound by latency, i.e. by how many workgroups share each dependent step.
+// Rows are cut into chunks, one 256-thread workgroup per chunk, and
 // cross-chunk results go through a small workspace:
-//   stats_kernel   (chunk, row, b): max and sum of 2^(x - max) of z/T (rows
-//                  0..gamma) and y/T (rows 0..gamma-1), base-2 units
-//   phat_kernel    (chunk, t, b):   the same for s = z/T + eta (q - p)
-//   tail_kernel    (chunk, t, b):   only with RV_ACCEPT_TAIL_PRESERVE (blog
-//                  section 2.4's tail rule): per chunk, the sum of the
-//                  tail-adjusted row (p_hat where p_hat >= 0.1 max p_hat,
-//                  p elsewhere), from which decide_kernel renormalises
-//   decide_kernel  (chunk, b):      every chunk recomputes the gamma ratios
-//                  min(1, p_hat_t[x_t]/q_t[x_t]) and the first-reject cut t*;
-//                  chunk 0 writes n_accept, the accepted tokens and the
-//                  ratios; every chunk writes its share of the draw weights
-//                  (max(p_hat - q, 0) at t* < gamma, or with
+//   stats_kernel   (chunk, row, b), 4096-element chunks: max and sum of
+//                  2^(x - max) of z/T (rows 0..gamma) and y/T (rows
+//                  0..gamma-1), base-2 units
+//   phat_kernel    (chunk, t, b), 4096-element chunks: the same for
+//                  s = z/T + eta (q - p); the chunk holding draft token x_t
+//                  also publishes z_t[x_t] and y_t[x_t]
+//   tail_kernel    (chunk, t, b), 4096-element chunks, only with
+//                  RV_ACCEPT_TAIL_PRESERVE (blog section 2.4's tail rule):
+//                  chunk sums of the tail-adjusted row (p_hat where
+//                  p_hat >= 0.1 max p_hat, p elsewhere), from which
+//                  decide_kernel renormalises
+//   decide_kernel  (chunk, b), 1024-element chunks: every chunk recomputes
+//                  the gamma ratios min(1, p_hat_t[x_t]/q_t[x_t]) and the
+//                  first-reject cut t*; chunk 0 writes n_accept, the accepted
+//                  tokens and the ratios; every chunk writes its share of the
+//                  draw weights (max(p_hat - q, 0) at t* < gamma, or with
 //                  RV_ACCEPT_PRINTED_RESIDUAL section 2.4's printed
-//                  max(p - min(p_hat, q), 0); p_gamma otherwise) and,
-//                  on request, p_hat.  The last chunk to finish (one
-//                  per-sequence arrival counter) then draws the token by
-//                  inverse CDF with the caller's uniform: chunk -> wave ->
-//                  lane -> element, each level taking the first unit whose
+//                  max(p - min(p_hat, q), 0); p_gamma otherwise) and, on
+//                  request, p_hat.  The last chunk to finish (one per-sequence
+//                  arrival counter) then draws the token by inverse CDF with
+//                  the caller's uniform: chunk -> thread -> element, each
+//                  level taking the first unit of positive weight whose
 //                  running total exceeds the target.
-// Every reduction has a fixed order and the counter only decides which
-// workgroup runs the draw, so results are bit-exact run to run; no
+// Every reduction and scan has a fixed order and the counter only decides
+// which workgroup runs the draw, so results are bit-exact run to run; no
 // workgroup ever waits for another.
 
 #include "rv_device.h"
@@ -38,16 +42,16 @@ namespace rv {
 namespace {
 
 constexpr int TPB = kVocabThreads;
-constexpr int PER = kVocabPerThread;
-constexpr int CH = kVocabChunk;
 
-template <bool VEC>
+// x[e] = row[start + e] for e < N (zero at or past V).
+template <bool VEC, int N>
 __device__ __forceinline__ void load_run(const float* __restrict__ row, int V, int start,
-                                         float (&x)[PER]) {
-  if (VEC && start + PER <= V) {
+                                         float (&x)[N]) {
+  static_assert(N % 4 == 0, "runs are whole float4s");
+  if (VEC && start + N <= V) {
     const f32x4* p = reinterpret_cast<const f32x4*>(row + start);
 #pragma unroll
-    for (int j = 0; j < PER / 4; ++j) {
+    for (int j = 0; j < N / 4; ++j) {
       const f32x4 v = p[j];
       x[4 * j + 0] = v[0];
       x[4 * j + 1] = v[1];
@@ -56,7 +60,7 @@ __device__ __forceinline__ void load_run(const float* __restrict__ row, int V, i
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < PER; ++e) x[e] = (start + e < V) ? row[start + e] : 0.f;
+    for (int e = 0; e < N; ++e) x[e] = (start + e < V) ? row[start + e] : 0.f;
   }
 }
 
@@ -78,6 +82,74 @@ __device__ float block_sum(float v) {
   const float r = (sh[0] + sh[1]) + (sh[2] + sh[3]);
   __syncthreads();
   return r;
+}
+
+// Two workgroup sums with one pair of barriers.
+__device__ float2 block_sum2(float a, float b) {
+  __shared__ float sh[2][TPB / 64];
+  a = wave_sum(a);
+  b = wave_sum(b);
+  if ((threadIdx.x & 63) == 0) {
+    sh[0][threadIdx.x >> 6] = a;
+    sh[1][threadIdx.x >> 6] = b;
+  }
+  __syncthreads();
+  const float2 r = make_float2((sh[0][0] + sh[0][1]) + (sh[0][2] + sh[0][3]),
+                               (sh[1][0] + sh[1][1]) + (sh[1][2] + sh[1][3]));
+  __syncthreads();
+  return r;
+}
+
+// Inclusive prefix sums of (v.x, v.y) over the workgroup in thread order:
+// a scan inside each wave, then the wave totals added in wave order.  *total
+// receives the workgroup sums, which equal the last thread's inclusive
+// values exactly (the same additions in the same order).
+__device__ float2 block_incl_scan2(float2 v, float2* total) {
+  __shared__ float2 sh[TPB / 64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float2 in = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float a = __shfl_up(in.x, o, 64);
+    const float b = __shfl_up(in.y, o, 64);
+    if (lane >= o) {
+      in.x += a;
+      in.y += b;
+    }
+  }
+  if (lane == 63) sh[wave] = in;
+  __syncthreads();
+  float2 run = make_float2(0.f, 0.f), off = run;
+#pragma unroll
+  for (int w = 0; w < TPB / 64; ++w) {
+    if (w == wave) off = run;
+    run.x += sh[w].x;
+    run.y += sh[w].y;
+  }
+  __syncthreads();
+  *total = run;
+  return make_float2(off.x + in.x, off.y + in.y);
+}
+
+// Index of the first thread with `hit` and of the last thread with `pos`
+// (-1 if none); every thread gets the same pair.
+__device__ int2 block_first_last(bool hit, bool pos) {
+  __shared__ int sf[TPB / 64], sl[TPB / 64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint64_t h = __ballot(hit), p = __ballot(pos);
+  if (lane == 0) {
+    sf[wave] = h ? wave * 64 + (int)__ffsll((long long)h) - 1 : -1;
+    sl[wave] = p ? wave * 64 + 63 - (int)__builtin_clzll(p) : -1;
+  }
+  __syncthreads();
+  int f = -1, l = -1;
+#pragma unroll
+  for (int w = 0; w < TPB / 64; ++w) {
+    if (f < 0) f = sf[w];
+    if (sl[w] >= 0) l = sl[w];
+  }
+  __syncthreads();
+  return make_int2(f, l);
 }
 
 // Merge two (max, sum-of-2^(x - max)) pairs.  Symmetric in its arguments, so
@@ -136,12 +208,19 @@ __device__ __forceinline__ void pq_s(float zv, float yv, float invT2, float eta2
   s2 = fmaf(eta2, q - p, x2);
 }
 
+// Row-table offsets, per sequence, in words: [4][gamma+1].
+__device__ __forceinline__ int rt_lz(int, int t) { return t; }
+__device__ __forceinline__ int rt_ly(int gamma, int t) { return (gamma + 1) + t; }
+__device__ __forceinline__ int rt_zx(int gamma, int t) { return 2 * (gamma + 1) + t; }
+__device__ __forceinline__ int rt_yx(int gamma, int t) { return 3 * (gamma + 1) + t; }
+
 template <bool VEC>
 __global__ __launch_bounds__(TPB) void stats_kernel(const float* __restrict__ z,
                                                     const float* __restrict__ y, int gamma, int V,
-                                                    float invT2, int C, float* __restrict__ zstat,
+                                                    float invT2, int cs, float* __restrict__ zstat,
                                                     float* __restrict__ ystat,
                                                     uint32_t* __restrict__ arrivals) {
+  constexpr int PER = kStatPer;
   const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   // The decide kernel counts chunk arrivals per sequence; start from zero on
   // every call (the workspace is not assumed to be initialised).
@@ -150,13 +229,13 @@ __global__ __launch_bounds__(TPB) void stats_kernel(const float* __restrict__ z,
   float* dst;
   if (r <= gamma) {
     row = z + ((size_t)b * (gamma + 1) + r) * V;
-    dst = zstat + (((size_t)b * (gamma + 1) + r) * C + c) * 2;
+    dst = zstat + (((size_t)b * (gamma + 1) + r) * cs + c) * 2;
   } else {
     const int t = r - gamma - 1;
     row = y + ((size_t)b * gamma + t) * V;
-    dst = ystat + (((size_t)b * gamma + t) * C + c) * 2;
+    dst = ystat + (((size_t)b * gamma + t) * cs + c) * 2;
   }
-  const int start = c * CH + threadIdx.x * PER;
+  const int start = c * kStatChunk + threadIdx.x * PER;
   float x[PER];
   load_run<VEC>(row, V, start, x);
   float tm = -INFINITY;
@@ -169,53 +248,69 @@ __global__ __launch_bounds__(TPB) void stats_kernel(const float* __restrict__ z,
   float ts = 0.f;
 #pragma unroll
   for (int e = 0; e < PER; ++e) ts += exp2_hw(x[e] - cm);
-  const float cs = block_sum(ts);
+  const float cs_sum = block_sum(ts);
   if (threadIdx.x == 0) {
     dst[0] = cm;
-    dst[1] = cs;
+    dst[1] = cs_sum;
   }
 }
 
-// grid (C, gamma + 1, B).  Rows t < gamma: chunk stats of s; chunk 0 also
-// publishes the row's z and y log-sum-exps.  Row gamma: chunk 0 publishes
-// the last target row's log-sum-exp (for the bonus draw).
+// grid (cp, gamma + 1, B).  Rows t < gamma: chunk stats of s; chunk 0 also
+// publishes the row's z and y log-sum-exps, and the chunk holding the draft
+// token x_t publishes z_t[x_t] and y_t[x_t] (no chunk does if x_t is out of
+// range; the decide kernel rejects such a draft before reading them).
+// Row gamma: chunk 0 publishes the last target row's log-sum-exp (for the
+// bonus draw).
 template <bool VEC>
 __global__ __launch_bounds__(TPB) void phat_kernel(const float* __restrict__ z,
-                                                   const float* __restrict__ y, int gamma, int V,
-                                                   float invT2, float eta2, int C,
+                                                   const float* __restrict__ y,
+                                                   const int32_t* __restrict__ draft, int gamma,
+                                                   int V, float invT2, float eta2, int cs, int cp,
                                                    const float* __restrict__ zstat,
                                                    const float* __restrict__ ystat,
                                                    float* __restrict__ sstat,
                                                    float* __restrict__ rowtab) {
+  constexpr int PER = kPhatPer;
   const int c = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63;
-  float* rt = rowtab + (size_t)b * 2 * (gamma + 1);
+  float* rt = rowtab + (size_t)b * 4 * (gamma + 1);
   if (t == gamma) {
     if (c == 0 && threadIdx.x < 64) {
-      const float lz = group_combine<64>(zstat + ((size_t)b * (gamma + 1) + t) * C * 2, C, lane);
-      if (lane == 0) rt[t] = lz;
+      const float lz =
+          group_combine<64>(zstat + ((size_t)b * (gamma + 1) + t) * cs * 2, cs, lane);
+      if (lane == 0) rt[rt_lz(gamma, t)] = lz;
     }
     return;
   }
+  // Issue the chunk loads first: they do not depend on the row statistics.
+  const int start = c * kPhatChunk + threadIdx.x * PER;
+  float zx[PER], yx[PER];
+  load_run<VEC>(z + ((size_t)b * (gamma + 1) + t) * V, V, start, zx);
+  load_run<VEC>(y + ((size_t)b * gamma + t) * V, V, start, yx);
+  const int x = draft[(size_t)b * gamma + t];
   __shared__ float sh_l[2];
   if (threadIdx.x < 64) {
-    const float lz = group_combine<64>(zstat + ((size_t)b * (gamma + 1) + t) * C * 2, C, lane);
-    const float ly = group_combine<64>(ystat + ((size_t)b * gamma + t) * C * 2, C, lane);
+    const float lz =
+        group_combine<64>(zstat + ((size_t)b * (gamma + 1) + t) * cs * 2, cs, lane);
+    const float ly = group_combine<64>(ystat + ((size_t)b * gamma + t) * cs * 2, cs, lane);
     if (lane == 0) {
       sh_l[0] = lz;
       sh_l[1] = ly;
       if (c == 0) {
-        rt[t] = lz;
-        rt[(gamma + 1) + t] = ly;
+        rt[rt_lz(gamma, t)] = lz;
+        rt[rt_ly(gamma, t)] = ly;
       }
     }
   }
-  const float* zrow = z + ((size_t)b * (gamma + 1) + t) * V;
-  const float* yrow = y + ((size_t)b * gamma + t) * V;
-  const int start = c * CH + threadIdx.x * PER;
-  float zx[PER], yx[PER];
-  load_run<VEC>(zrow, V, start, zx);
-  load_run<VEC>(yrow, V, start, yx);
+  const int off = x - start;
+  if (off >= 0 && off < PER) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e)
+      if (e == off) {
+        rt[rt_zx(gamma, t)] = zx[e];
+        rt[rt_yx(gamma, t)] = yx[e];
+      }
+  }
   __syncthreads();
   const float lz = sh_l[0], ly = sh_l[1];
   float s2[PER];
@@ -231,11 +326,11 @@ __global__ __launch_bounds__(TPB) void phat_kernel(const float* __restrict__ z,
   float ts = 0.f;
 #pragma unroll
   for (int e = 0; e < PER; ++e) ts += exp2_hw(s2[e] - cm);
-  const float cs = block_sum(ts);
+  const float csum = block_sum(ts);
   if (threadIdx.x == 0) {
-    float* dst = sstat + (((size_t)b * gamma + t) * C + c) * 2;
+    float* dst = sstat + (((size_t)b * gamma + t) * cp + c) * 2;
     dst[0] = cm;
-    dst[1] = cs;
+    dst[1] = csum;
   }
 }
 
@@ -277,35 +372,36 @@ __device__ __forceinline__ float draw_weight(float zv, float yv, int ts, int gam
                                                   : fmaxf(ph - q, 0.f);
 }
 
-// grid (C, gamma, B), RV_ACCEPT_TAIL_PRESERVE only: chunk sums of the
+// grid (cp, gamma, B), RV_ACCEPT_TAIL_PRESERVE only: chunk sums of the
 // unnormalised tail-adjusted p_hat (p_hat where s >= max s + log2 0.1, else
 // p).  The row's LSE and max of s come from the same 16-lane combine the
 // decide kernel uses, so both kernels classify every entry identically.
 template <bool VEC>
 __global__ __launch_bounds__(TPB) void tail_kernel(const float* __restrict__ z,
                                                    const float* __restrict__ y, int gamma, int V,
-                                                   float invT2, float eta2, int C,
+                                                   float invT2, float eta2, int cp,
                                                    const float* __restrict__ sstat,
                                                    const float* __restrict__ rowtab,
                                                    float* __restrict__ tstat) {
+  constexpr int PER = kPhatPer;
   const int c = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
   __shared__ float sh[4];
-  const float* rt = rowtab + (size_t)b * 2 * (gamma + 1);
+  const int start = c * kPhatChunk + threadIdx.x * PER;
+  float zx[PER], yx[PER];
+  load_run<VEC>(z + ((size_t)b * (gamma + 1) + t) * V, V, start, zx);
+  load_run<VEC>(y + ((size_t)b * gamma + t) * V, V, start, yx);
+  const float* rt = rowtab + (size_t)b * 4 * (gamma + 1);
   if (threadIdx.x < 16) {
     float ms;
-    const float ls = group_combine<16>(sstat + ((size_t)b * gamma + t) * C * 2, C,
+    const float ls = group_combine<16>(sstat + ((size_t)b * gamma + t) * cp * 2, cp,
                                        threadIdx.x, &ms);
     if (threadIdx.x == 0) {
       sh[0] = ls;
       sh[1] = ms + kLog2Tenth;
-      sh[2] = rt[t];
-      sh[3] = rt[(gamma + 1) + t];
+      sh[2] = rt[rt_lz(gamma, t)];
+      sh[3] = rt[rt_ly(gamma, t)];
     }
   }
-  const int start = c * CH + threadIdx.x * PER;
-  float zx[PER], yx[PER];
-  load_run<VEC>(z + ((size_t)b * (gamma + 1) + t) * V, V, start, zx);
-  load_run<VEC>(y + ((size_t)b * gamma + t) * V, V, start, yx);
   __syncthreads();
   const float ls = sh[0], thr = sh[1], lz = sh[2], ly = sh[3];
   float acc = 0.f;
@@ -315,96 +411,73 @@ __global__ __launch_bounds__(TPB) void tail_kernel(const float* __restrict__ z,
     pq_s(zx[e], yx[e], invT2, eta2, lz, ly, p, q, s2);
     if (start + e < V) acc += (s2 >= thr) ? exp2_hw(s2 - ls) : p;
   }
-  const float cs = block_sum(acc);
-  if (threadIdx.x == 0) tstat[((size_t)b * gamma + t) * C + c] = cs;
+  const float csum = block_sum(acc);
+  if (threadIdx.x == 0) tstat[((size_t)b * gamma + t) * cp + c] = csum;
 }
 
-// Inverse CDF of the draw row ts of sequence b with the caller's uniform:
-// chunk -> wave -> lane -> element, each level taking the first unit of
-// positive weight whose running total exceeds the target; if rounding leaves
-// none, the last unit of positive weight (and every lower level then takes
-// its last positive unit, i.e. the largest id of positive weight).  Run by
-// one whole workgroup; wsh is LDS for the 2 C chunk weights.
+// Inverse CDF of the draw row ts of sequence b with the caller's uniform,
+// run by one whole workgroup.  Chunk level: a scan of the cd chunk weights
+// (both kinds; kind 1, p_hat itself, only if a rejected row has no residual
+// mass, which exact arithmetic rules out) picks the first chunk of positive
+// weight whose running total exceeds u * W; thread level: the same over the
+// chunk's thread totals; element level: the same inside the thread.  Where
+// rounding leaves no such unit, the last unit of positive weight is taken
+// (and every lower level then takes its last positive unit, i.e. the largest
+// id of positive weight).
 template <bool VEC>
 __device__ void draw_row(const float* __restrict__ z, const float* __restrict__ y,
                          const float* __restrict__ u, int b, int ts, int gamma, int V,
-                         float invT2, float eta2, int C, const RowLse& rc,
-                         const float* __restrict__ wsum, float* wsh,
-                         int32_t* __restrict__ out_tokens) {
-  __shared__ int sh_chunk, sh_kind;
-  __shared__ float sh_tau;
-  __shared__ float wtot[TPB / 64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+                         float invT2, float eta2, int cd, const RowLse& rc,
+                         const float* __restrict__ wsum, int32_t* __restrict__ out_tokens) {
+  __shared__ float sh_base;
   // The chunk weights were published by the other workgroups before their
   // arrival was counted; read them past the caches.
-  const float* ws = wsum + (size_t)b * C * 2;
-  for (int i = threadIdx.x; i < 2 * C; i += TPB) wsh[i] = __builtin_nontemporal_load(ws + i);
+  const float* ws = wsum + (size_t)b * cd * 2;
   const float u_ts = u[(size_t)b * (gamma + 1) + ts];
-  __syncthreads();
+  auto chunk_w = [&](int i) {
+    return i < cd ? make_float2(__builtin_nontemporal_load(ws + 2 * i),
+                                __builtin_nontemporal_load(ws + 2 * i + 1))
+                  : make_float2(0.f, 0.f);
+  };
 
-  if (wave == 0) {
-    // Chunk level, one wave: an inclusive scan of the chunk weights in
-    // blocks of 64 (fixed pattern), then the first chunk of positive weight
-    // whose running total exceeds u * W.  kind 1 (p_hat itself) only if a
-    // rejected row has no residual mass, which exact arithmetic rules out.
-    int kind = 0;
-    float W = 0.f;
-    for (int pass = 0; pass < 2; ++pass) {
-      kind = pass;
-      float carry = 0.f;
-      for (int c0 = 0; c0 < C; c0 += 64) {
-        const int c = c0 + lane;
-        float incl = (c < C) ? wsh[2 * c + kind] : 0.f;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const float v = __shfl_up(incl, o, 64);
-          if (lane >= o) incl += v;
-        }
-        carry += __shfl(incl, 63, 64);
-      }
-      W = carry;
-      if (W > 0.f) break;
-    }
-    const float tau = u_ts * W;
-    float carry = 0.f;
-    int pick = -1, last = -1;
-    float pick_base = 0.f;
-    for (int c0 = 0; c0 < C && pick < 0; c0 += 64) {
-      const int c = c0 + lane;
-      const float wc = (c < C) ? wsh[2 * c + kind] : 0.f;
-      float incl = wc;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
-      }
-      const float excl = carry + (incl - wc);
-      const uint64_t hit = __ballot(wc > 0.f && carry + incl > tau);
-      const uint64_t pos = __ballot(wc > 0.f);
-      if (hit) {
-        const int lsel = (int)__ffsll((long long)hit) - 1;
-        pick = c0 + lsel;
-        pick_base = __shfl(excl, lsel, 64);
-      } else if (pos) {
-        last = c0 + 63 - (int)__builtin_clzll(pos);
-      }
-      carry += __shfl(incl, 63, 64);
-    }
-    float tau_c = tau - pick_base;
-    if (pick < 0) {  // rounding: the last chunk with weight, its last positive id
-      pick = last < 0 ? 0 : last;
-      tau_c = INFINITY;
-    }
-    if (lane == 0) {
-      sh_chunk = pick;
-      sh_kind = kind;
-      sh_tau = tau_c;
-    }
+  // Totals of both kinds, block of TPB chunks by block.  The last block's
+  // values stay in registers (with cd <= TPB the only block).
+  float2 wv = make_float2(0.f, 0.f), incl = wv, tot = wv, carry = wv;
+  for (int c0 = 0; c0 < cd; c0 += TPB) {
+    carry.x += tot.x;
+    carry.y += tot.y;
+    wv = chunk_w(c0 + threadIdx.x);
+    incl = block_incl_scan2(wv, &tot);
   }
-  __syncthreads();
-  const int chunk = sh_chunk, kind = sh_kind;
-  const float tau_c = sh_tau;
-  const int start = chunk * CH + threadIdx.x * PER;
+  const float2 W2 = make_float2(carry.x + tot.x, carry.y + tot.y);
+  const int kind = W2.x > 0.f ? 0 : 1;
+  const float tau = u_ts * (kind ? W2.y : W2.x);
+
+  int pick = -1, last = -1;
+  float tau_c = INFINITY;
+  float run = 0.f;
+  for (int c0 = 0; c0 < cd; c0 += TPB) {
+    if (cd > TPB) {
+      wv = chunk_w(c0 + threadIdx.x);
+      incl = block_incl_scan2(wv, &tot);
+    }
+    const float wk = kind ? wv.y : wv.x;
+    const float ik = run + (kind ? incl.y : incl.x);
+    const int2 fl = block_first_last(wk > 0.f && ik > tau, wk > 0.f);
+    if (fl.x >= 0) {
+      if ((int)threadIdx.x == fl.x) sh_base = ik - wk;
+      __syncthreads();
+      pick = c0 + fl.x;
+      tau_c = tau - sh_base;
+      break;
+    }
+    if (fl.y >= 0) last = c0 + fl.y;
+    run += kind ? tot.y : tot.x;
+  }
+  if (pick < 0) pick = last < 0 ? 0 : last;  // tau_c stays infinite
+
+  constexpr int PER = kDrawPer;
+  const int start = pick * kDrawChunk + threadIdx.x * PER;
   float zx[PER], yx[PER], w[PER];
   load_run<VEC>(z + ((size_t)b * (gamma + 1) + ts) * V, V, start, zx);
   if (ts < gamma)
@@ -418,53 +491,12 @@ __device__ void draw_row(const float* __restrict__ z, const float* __restrict__ 
     w[e] = (start + e < V) ? draw_weight(zx[e], yx[e], ts, gamma, kind, invT2, eta2, rc) : 0.f;
     tsum += w[e];
   }
-  // Inclusive scan of the thread totals inside each wave (fixed pattern).
-  float incl = tsum;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float v = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += v;
-  }
-  if (lane == 63) wtot[wave] = incl;
-  __syncthreads();
-  // Wave level (same arithmetic in every thread).
-  float tau = tau_c, base = 0.f;
-  int wsel = -1, wlast = -1;
-  float wlast_base = 0.f;
-  for (int ww = 0; ww < TPB / 64; ++ww) {
-    const float wt = wtot[ww];
-    if (wt > 0.f) {
-      if (base + wt > tau) {
-        wsel = ww;
-        break;
-      }
-      wlast = ww;
-      wlast_base = base;
-    }
-    base += wt;
-  }
-  if (wsel < 0) {
-    wsel = wlast < 0 ? 0 : wlast;
-    base = wlast_base;
-    tau = INFINITY;
-  }
-  if (wave != wsel) return;
-  const float tau_w = tau - base;
-  // Lane level.
-  const uint64_t hit = __ballot(tsum > 0.f && incl > tau_w);
-  int lsel;
-  float tau_l;
-  const float excl = incl - tsum;
-  if (hit) {
-    lsel = (int)__ffsll((long long)hit) - 1;
-    tau_l = tau_w - __shfl(excl, lsel, 64);
-  } else {
-    const uint64_t pos = __ballot(tsum > 0.f);
-    lsel = pos ? 63 - (int)__builtin_clzll(pos) : 0;
-    tau_l = INFINITY;
-  }
-  if (lane != lsel) return;
-  // Element level.
+  float2 ttot;
+  const float tincl = block_incl_scan2(make_float2(tsum, 0.f), &ttot).x;
+  const int2 fl = block_first_last(tsum > 0.f && tincl > tau_c, tsum > 0.f);
+  const int sel = fl.x >= 0 ? fl.x : (fl.y >= 0 ? fl.y : 0);
+  if ((int)threadIdx.x != sel) return;
+  const float tau_l = fl.x >= 0 ? tau_c - (tincl - tsum) : INFINITY;
   float acc = 0.f;
   int k = -1, klast = -1;
 #pragma unroll
@@ -481,43 +513,47 @@ __device__ void draw_row(const float* __restrict__ z, const float* __restrict__ 
   out_tokens[(size_t)b * (gamma + 1) + ts] = tok;
 }
 
-// grid (C, B).  Every chunk recomputes the row LSEs of s (16 lanes per row,
+// grid (cd, B).  Every chunk recomputes the row LSEs of s (16 lanes per row,
 // all rows at once), the ratios and the first-reject cut, then writes its
 // share of the draw weights; chunk 0 writes the per-sequence outputs.
 template <bool VEC>
 __global__ __launch_bounds__(TPB) void decide_kernel(
     const float* __restrict__ z, const float* __restrict__ y, const int32_t* __restrict__ draft,
-    const float* __restrict__ r, int gamma, int V, float invT2, float eta2, int C,
+    const float* __restrict__ r, int gamma, int V, float invT2, float eta2, int cp, int cd,
     const float* __restrict__ sstat, const float* __restrict__ tstat, unsigned flags,
-    float* __restrict__ rowtab, float* __restrict__ wsum,
+    const float* __restrict__ rowtab, float* __restrict__ wsum,
     uint32_t* __restrict__ arrivals, const float* __restrict__ u,
     int32_t* __restrict__ n_accept, int32_t* __restrict__ out_tokens,
     float* __restrict__ ratio_out, float* __restrict__ p_hat_out) {
+  constexpr int PER = kDrawPer;
   const int c = blockIdx.x, b = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   __shared__ RowLse rc;
   __shared__ int sh_ts;
-  float* rt = rowtab + (size_t)b * 2 * (gamma + 1);
-  // Round trip 1: row table, s statistics, draft ids and acceptance uniforms.
+  const float* rt = rowtab + (size_t)b * 4 * (gamma + 1);
+  // One round trip: draft ids, acceptance uniforms, the draft tokens' logits,
+  // the row table and the s statistics are all independent loads.
   int x = 0;
-  float rv = 0.f;
+  float rv = 0.f, zxv = 0.f, yxv = 0.f;
   if (wave == 0 && lane < gamma) {
     x = draft[(size_t)b * gamma + lane];
     rv = r[(size_t)b * gamma + lane];
+    zxv = rt[rt_zx(gamma, lane)];
+    yxv = rt[rt_yx(gamma, lane)];
   }
   for (int i = threadIdx.x; i <= gamma; i += TPB) {
-    rc.lz[i] = rt[i];
-    if (i < gamma) rc.ly[i] = rt[(gamma + 1) + i];
+    rc.lz[i] = rt[rt_lz(gamma, i)];
+    if (i < gamma) rc.ly[i] = rt[rt_ly(gamma, i)];
   }
   if (threadIdx.x == 0) rc.flags = flags;
   {
     const int grp = threadIdx.x >> 4, j = threadIdx.x & 15;
     for (int t = grp; t < gamma; t += TPB / 16) {
       float ms;
-      const float ls = group_combine<16>(sstat + ((size_t)b * gamma + t) * C * 2, C, j, &ms);
+      const float ls = group_combine<16>(sstat + ((size_t)b * gamma + t) * cp * 2, cp, j, &ms);
       float zsum = 1.f;
       if (flags & RV_ACCEPT_TAIL_PRESERVE)
-        zsum = group16_sum(tstat + ((size_t)b * gamma + t) * C, C, j);
+        zsum = group16_sum(tstat + ((size_t)b * gamma + t) * cp, cp, j);
       if (j == 0) {
         rc.ls[t] = ls;
         rc.thr[t] = ms + kLog2Tenth;
@@ -528,21 +564,19 @@ __global__ __launch_bounds__(TPB) void decide_kernel(
   __syncthreads();
 
   if (wave == 0) {
-    // Round trip 2: the draft tokens' target and draft logits.
     bool bad = false, acc = true;
     float ratio = 0.f;
     if (lane < gamma) {
       bad = (x < 0 || x >= V);
       if (!bad) {
         float p, q, s2;
-        pq_s(z[((size_t)b * (gamma + 1) + lane) * V + x], y[((size_t)b * gamma + lane) * V + x],
-             invT2, eta2, rc.lz[lane], rc.ly[lane], p, q, s2);
+        pq_s(zxv, yxv, invT2, eta2, rc.lz[lane], rc.ly[lane], p, q, s2);
         const float ph = p_hat_entry(p, s2, lane, rc);
         ratio = fminf(1.0f, ph / q);
         acc = rv <= ratio;
       }
     }
-  const uint64_t badm = __ballot(bad);
+    const uint64_t badm = __ballot(bad);
     const uint64_t rej = __ballot(lane < gamma && !acc);
     int ts = rej ? (int)__ffsll((long long)rej) - 1 : gamma;
     if (badm) ts = -1;
@@ -556,7 +590,7 @@ __global__ __launch_bounds__(TPB) void decide_kernel(
   }
   __syncthreads();
   const int ts = sh_ts;
-  const int start = c * CH + threadIdx.x * PER;
+  const int start = c * kDrawChunk + threadIdx.x * PER;
 
   if (p_hat_out != nullptr) {
     for (int t = 0; t < gamma; ++t) {
@@ -589,24 +623,22 @@ __global__ __launch_bounds__(TPB) void decide_kernel(
       w1 += draw_weight(zx[e], yx[e], ts, gamma, 1, invT2, eta2, rc);
     }
   }
-  const float W0 = block_sum(w0);
-  const float W1 = block_sum(w1);
+  const float2 W = block_sum2(w0, w1);
   // Publish this chunk's draw weights, then count its arrival.  The
   // workgroup that arrives last draws the token: which workgroup that is
   // does not change what is drawn, and nothing ever waits for another
   // workgroup.
   __shared__ uint32_t sh_arrived;
   if (threadIdx.x == 0) {
-    wsum[((size_t)b * C + c) * 2 + 0] = W0;
-    wsum[((size_t)b * C + c) * 2 + 1] = W1;
+    wsum[((size_t)b * cd + c) * 2 + 0] = W.x;
+    wsum[((size_t)b * cd + c) * 2 + 1] = W.y;
     __threadfence();
     sh_arrived = atomicAdd(arrivals + b, 1u);
   }
   __syncthreads();
-  if (sh_arrived != (uint32_t)(C - 1)) return;  // uniform
+  if (sh_arrived != (uint32_t)(cd - 1)) return;  // uniform
   __threadfence();
-  extern __shared__ float wsh[];  // [C][2]
-  draw_row<VEC>(z, y, u, b, ts, gamma, V, invT2, eta2, C, rc, wsum, wsh, out_tokens);
+  draw_row<VEC>(z, y, u, b, ts, gamma, V, invT2, eta2, cd, rc, wsum, out_tokens);
 }
 
 template <bool VEC>
@@ -615,7 +647,6 @@ hipError_t launch_accept(const float* z, const float* y, const int32_t* draft, c
                          unsigned flags, const AcceptLayout& L, float* ws, int32_t* n_accept,
                          int32_t* out_tokens, float* ratio_out, float* p_hat_out,
                          hipStream_t s) {
-  const int C = L.chunks;
   float* zstat = ws + L.zstat;
   float* ystat = ws + L.ystat;
   float* sstat = ws + L.sstat;
@@ -623,16 +654,16 @@ hipError_t launch_accept(const float* z, const float* y, const int32_t* draft, c
   float* tstat = ws + L.tstat;
   float* wsm = ws + L.wsum;
   uint32_t* arrivals = reinterpret_cast<uint32_t*>(ws + L.arrivals);
-  hipLaunchKernelGGL((stats_kernel<VEC>), dim3(C, 2 * gamma + 1, B), dim3(TPB), 0, s, z, y, gamma,
-                     V, invT2, C, zstat, ystat, arrivals);
-  hipLaunchKernelGGL((phat_kernel<VEC>), dim3(C, gamma + 1, B), dim3(TPB), 0, s, z, y, gamma, V,
-                     invT2, eta2, C, zstat, ystat, sstat, rowtab);
+  hipLaunchKernelGGL((stats_kernel<VEC>), dim3(L.cs, 2 * gamma + 1, B), dim3(TPB), 0, s, z, y,
+                     gamma, V, invT2, L.cs, zstat, ystat, arrivals);
+  hipLaunchKernelGGL((phat_kernel<VEC>), dim3(L.cp, gamma + 1, B), dim3(TPB), 0, s, z, y, draft,
+                     gamma, V, invT2, eta2, L.cs, L.cp, zstat, ystat, sstat, rowtab);
   if (flags & RV_ACCEPT_TAIL_PRESERVE)
-    hipLaunchKernelGGL((tail_kernel<VEC>), dim3(C, gamma, B), dim3(TPB), 0, s, z, y, gamma, V,
-                       invT2, eta2, C, sstat, rowtab, tstat);
-  hipLaunchKernelGGL((decide_kernel<VEC>), dim3(C, B), dim3(TPB), (size_t)C * 2 * sizeof(float),
-                     s, z, y, draft, r, gamma, V, invT2, eta2, C, sstat, tstat, flags, rowtab,
-                     wsm, arrivals, u, n_accept, out_tokens, ratio_out, p_hat_out);
+    hipLaunchKernelGGL((tail_kernel<VEC>), dim3(L.cp, gamma, B), dim3(TPB), 0, s, z, y, gamma, V,
+                       invT2, eta2, L.cp, sstat, rowtab, tstat);
+  hipLaunchKernelGGL((decide_kernel<VEC>), dim3(L.cd, B), dim3(TPB), 0, s, z, y, draft, r, gamma,
+                     V, invT2, eta2, L.cp, L.cd, sstat, tstat, flags, rowtab, wsm, arrivals, u,
+                     n_accept, out_tokens, ratio_out, p_hat_out);
   return hipGetLastError();
 }
 

@@ -38,27 +38,43 @@ rv_status check_block(const void* q, const void* k_blk, const void* v_blk,
                       const int32_t* parent_host, int B, int Hq, int Hkv, int n, int d,
                       float sm_scale, const float* o_blk, const float* lse_blk, BlockMask* mask);
 
+rv_status check_block_merge(const void* q, const void* k_blk, const void* v_blk,
+                            const int32_t* parent_host, const float* o_part,
+                            const float* lse_part, int S, int B, int Hq, int Hkv, int n, int d,
+                            float sm_scale, const void* out, BlockMask* mask);
+
 rv_status check_merge(const float* o_part, const float* lse_part, int S, const float* o_blk,
                       const float* lse_blk, int B, int Hq, int n, int d, const void* out);
 
 // --- vocabulary pass --------------------------------------------------------
 
 constexpr int kVocabThreads = 256;
-constexpr int kVocabPerThread = 16;
-constexpr int kVocabChunk = kVocabThreads * kVocabPerThread;  // elements per workgroup
+// Elements per thread, hence chunk lengths, of the passes over the
+// vocabulary.  The statistics and p_hat passes run many rows at once and
+// take long chunks (fewer partials for the next pass to combine); the
+// decide/draw pass works on one row, so it takes short chunks to spread that
+// row's exp work over more workgroups, and its last workgroup re-evaluates
+// one whole chunk alone.
+constexpr int kStatPer = 16;
+constexpr int kPhatPer = 16;
+constexpr int kDrawPer = 4;
+constexpr int kStatChunk = kVocabThreads * kStatPer;  // 4096
+constexpr int kPhatChunk = kVocabThreads * kPhatPer;  // 4096
+constexpr int kDrawChunk = kVocabThreads * kDrawPer;  // 1024
 constexpr int kMaxVocab = 1 << 22;
 constexpr int kMaxGamma = 63;  // one wave decides the first-reject cut
 
 // Workspace layout of rapid_accept, in 4-byte words from the base.
 struct AcceptLayout {
-  int chunks;          // C = ceil(V / kVocabChunk)
-  size_t zstat;        // [B][gamma+1][C][2]  (max, sum) of z/T in log2 units
-  size_t ystat;        // [B][gamma][C][2]
-  size_t sstat;        // [B][gamma][C][2]    of s = z/T + eta (q - p)
-  size_t rowtab;       // [B][2][gamma+1]     base-2 LSE of z/T and y/T per row
-  size_t tstat;        // [B][gamma][C]       chunk sums of the tail-adjusted p_hat
-  size_t wsum;         // [B][C][2]           residual and p_hat weight per chunk
-  size_t arrivals;     // [B] uint32          chunks done with their draw weight
+  int cs, cp, cd;      // chunk counts: ceil(V / kStatChunk), kPhatChunk, kDrawChunk
+  size_t zstat;        // [B][gamma+1][cs][2]  (max, sum) of z/T in log2 units
+  size_t ystat;        // [B][gamma][cs][2]
+  size_t sstat;        // [B][gamma][cp][2]    of s = z/T + eta (q - p)
+  size_t rowtab;       // [B][4][gamma+1]      base-2 LSE of z/T and y/T per row,
+                       //                      then each draft token's z and y
+  size_t tstat;        // [B][gamma][cp]       chunk sums of the tail-adjusted p_hat
+  size_t wsum;         // [B][cd][2]           residual and p_hat weight per chunk
+  size_t arrivals;     // [B] uint32           chunks done with their draw weight
   size_t words;        // total
 };
 AcceptLayout accept_layout(int B, int gamma, int V);

@@ -56,17 +56,7 @@ rv_status check_prefix(const void* q, const void* k_cache, const void* v_cache,
   return RV_OK;
 }
 
-rv_status check_block(const void* q, const void* k_blk, const void* v_blk,
-                      const int32_t* parent_host, int B, int Hq, int Hkv, int n, int d,
-                      float sm_scale, const float* o_blk, const float* lse_blk, BlockMask* mask) {
-  if (!q || !k_blk || !v_blk || !o_blk || !lse_blk) return RV_ERR_NULL;
-  rv_status st = check_heads(B, Hq, Hkv, n, d);
-  if (st != RV_OK) return st;
-  if (!isfinite(sm_scale) || !(sm_scale > 0.0f)) return RV_ERR_VALUE;
-  if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(o_blk) ||
-      !aligned16(lse_blk))
-    return RV_ERR_ALIGNMENT;
-  if ((int64_t)B * Hq > 65535) return RV_ERR_UNSUPPORTED;  // grid dimension y
+static rv_status block_mask(const int32_t* parent_host, int n, BlockMask* mask) {
   BlockMask m;
   memset(&m, 0, sizeof(m));
   if (parent_host == nullptr) {
@@ -83,6 +73,36 @@ rv_status check_block(const void* q, const void* k_blk, const void* v_blk,
   }
   if (mask) *mask = m;
   return RV_OK;
+}
+
+rv_status check_block(const void* q, const void* k_blk, const void* v_blk,
+                      const int32_t* parent_host, int B, int Hq, int Hkv, int n, int d,
+                      float sm_scale, const float* o_blk, const float* lse_blk, BlockMask* mask) {
+  if (!q || !k_blk || !v_blk || !o_blk || !lse_blk) return RV_ERR_NULL;
+  rv_status st = check_heads(B, Hq, Hkv, n, d);
+  if (st != RV_OK) return st;
+  if (!isfinite(sm_scale) || !(sm_scale > 0.0f)) return RV_ERR_VALUE;
+  if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(o_blk) ||
+      !aligned16(lse_blk))
+    return RV_ERR_ALIGNMENT;
+  if ((int64_t)B * Hq > 65535) return RV_ERR_UNSUPPORTED;  // grid dimension y
+  return block_mask(parent_host, n, mask);
+}
+
+rv_status check_block_merge(const void* q, const void* k_blk, const void* v_blk,
+                            const int32_t* parent_host, const float* o_part,
+                            const float* lse_part, int S, int B, int Hq, int Hkv, int n, int d,
+                            float sm_scale, const void* out, BlockMask* mask) {
+  if (!q || !k_blk || !v_blk || !o_part || !lse_part || !out) return RV_ERR_NULL;
+  rv_status st = check_heads(B, Hq, Hkv, n, d);
+  if (st != RV_OK) return st;
+  if (S < 1) return RV_ERR_SHAPE;
+  if (!isfinite(sm_scale) || !(sm_scale > 0.0f)) return RV_ERR_VALUE;
+  if (!aligned16(q) || !aligned16(k_blk) || !aligned16(v_blk) || !aligned16(o_part) ||
+      !aligned16(lse_part) || !aligned16(out))
+    return RV_ERR_ALIGNMENT;
+  if ((int64_t)B * Hq * n > 0x7fffffff / 4) return RV_ERR_UNSUPPORTED;  // one row per workgroup
+  return block_mask(parent_host, n, mask);
 }
 
 rv_status check_merge(const float* o_part, const float* lse_part, int S, const float* o_blk,
@@ -102,23 +122,25 @@ static size_t round_words(size_t w) { return (w + 63) & ~(size_t)63; }  // 256-b
 
 AcceptLayout accept_layout(int B, int gamma, int V) {
   AcceptLayout L;
-  L.chunks = ceil_div(V, kVocabChunk);
-  size_t C = (size_t)L.chunks;
+  L.cs = ceil_div(V, kStatChunk);
+  L.cp = ceil_div(V, kPhatChunk);
+  L.cd = ceil_div(V, kDrawChunk);
+  const size_t Bz = (size_t)B, g = (size_t)gamma;
   size_t off = 0;
   L.zstat = off;
-  off += round_words((size_t)B * (gamma + 1) * C * 2);
+  off += round_words(Bz * (g + 1) * L.cs * 2);
   L.ystat = off;
-  off += round_words((size_t)B * gamma * C * 2);
+  off += round_words(Bz * g * L.cs * 2);
   L.sstat = off;
-  off += round_words((size_t)B * gamma * C * 2);
+  off += round_words(Bz * g * L.cp * 2);
   L.rowtab = off;
-  off += round_words((size_t)B * 2 * (gamma + 1));
+  off += round_words(Bz * 4 * (g + 1));
   L.tstat = off;
-  off += round_words((size_t)B * gamma * C);
+  off += round_words(Bz * g * L.cp);
   L.wsum = off;
-  off += round_words((size_t)B * C * 2);
+  off += round_words(Bz * L.cd * 2);
   L.arrivals = off;
-  off += round_words((size_t)B);
+  off += round_words(Bz);
   L.words = off;
   return L;
 }

@@ -50,6 +50,9 @@ def load_library():
     lib.spec_attn_block.restype = i32
     lib.lse_merge.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.lse_merge.restype = i32
+    lib.spec_attn_block_merge.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                          f32, vp, vp, vp]
+    lib.spec_attn_block_merge.restype = i32
     lib.rapid_accept_workspace_size.argtypes = [i32, i32, i32]
     lib.rapid_accept_workspace_size.restype = sz
     lib.rapid_accept.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp, vp, vp, vp,
@@ -167,6 +170,36 @@ def lse_merge(o_part, lse_part, o_blk, lse_blk, out, lse_out=None, stream=None):
     _check(load_library().lse_merge(
         _ptr(o_part), _ptr(lse_part), S, _ptr(o_blk), _ptr(lse_blk), B, Hq, n, d, _ptr(out),
         _ptr(lse_out), _stream(stream)), "lse_merge")
+
+
+def spec_attn_block_merge(q, k_blk, v_blk, parent, o_part, lse_part, out, lse_out=None,
+                          sm_scale=1.0, stream=None):
+    """Block pass and merge in one launch.  Shapes as spec_attn_block and
+    lse_merge; out bf16 [B,Hq,n,d]; lse_out fp32 [B,Hq,n] or None."""
+    import torch
+    _need(q, "q", torch.bfloat16)
+    B, Hq, n, d = q.shape
+    _need(k_blk, "k_blk", torch.bfloat16)
+    Hkv = k_blk.shape[1]
+    _need(k_blk, "k_blk", torch.bfloat16, (B, Hkv, n, d))
+    _need(v_blk, "v_blk", torch.bfloat16, (B, Hkv, n, d))
+    _need(o_part, "o_part", torch.float32)
+    S = o_part.shape[3]
+    _need(o_part, "o_part", torch.float32, (B, Hq, n, S, d))
+    _need(lse_part, "lse_part", torch.float32, (B, Hq, n, S))
+    _need(out, "out", torch.bfloat16, (B, Hq, n, d))
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, (B, Hq, n))
+    par = None
+    if parent is not None:
+        vals = [int(x) for x in parent]
+        if len(vals) != n:
+            raise ValueError("parent must have n entries")
+        par = (ctypes.c_int32 * n)(*vals)
+    _check(load_library().spec_attn_block_merge(
+        _ptr(q), _ptr(k_blk), _ptr(v_blk), ctypes.cast(par, ctypes.c_void_p) if par else None,
+        _ptr(o_part), _ptr(lse_part), S, B, Hq, Hkv, n, d, float(sm_scale), _ptr(out),
+        _ptr(lse_out), _stream(stream)), "spec_attn_block_merge")
 
 
 def rapid_accept_workspace_size(B, gamma, V):

@@ -78,13 +78,19 @@ class VerifyStep:
             self.p_hat = (torch.empty((Bv, self.gamma, V), dtype=f32, device=device)
                           if want_p_hat else None)
 
-    def attention(self, k_cache=None, v_cache=None, stream=None):
-        """The three attention calls; k_cache/v_cache override the resident
-        cache (same shape), e.g. to rotate copies when timing."""
+    def attention(self, k_cache=None, v_cache=None, stream=None, fused=False):
+        """The attention calls; k_cache/v_cache override the resident cache
+        (same shape), e.g. to rotate copies when timing.  fused: the block
+        pass and the merge as one spec_attn_block_merge call (o_blk and
+        lse_blk are then left untouched)."""
         kc = self.k_cache if k_cache is None else k_cache
         vc = self.v_cache if v_cache is None else v_cache
         rv.spec_attn_prefix(self.q, kc, vc, self.seq_lens, self.max_seq_len, self.split_len,
                             self.num_splits, self.o_part, self.lse_part, self.sm_scale, stream)
+        if fused:
+            rv.spec_attn_block_merge(self.q, self.k_blk, self.v_blk, self.parent, self.o_part,
+                                     self.lse_part, self.out, self.lse_out, self.sm_scale, stream)
+            return
         rv.spec_attn_block(self.q, self.k_blk, self.v_blk, self.parent, self.o_blk, self.lse_blk,
                            self.sm_scale, stream)
         rv.lse_merge(self.o_part, self.lse_part, self.o_blk, self.lse_blk, self.out, self.lse_out,
@@ -101,8 +107,8 @@ class VerifyStep:
             rv.rapid_accept(z, y, self.draft, self.r, self.u, self.T, self.eta, self.n_accept,
                             self.out_tokens, self.workspace, self.ratio, self.p_hat, stream)
 
-    def run(self, stream=None):
+    def run(self, stream=None, fused=False):
         if self.attn is not None:
-            self.attention(stream=stream)
+            self.attention(stream=stream, fused=fused)
         if self.vocab is not None:
             self.accept(stream=stream)

@@ -37,8 +37,9 @@ def declared_functions():
 
 def test_header_declares_the_four_calls():
     names = declared_functions()
-    for n in ("spec_attn_prefix", "spec_attn_block", "lse_merge", "rapid_accept",
-              "rapid_accept_workspace_size", "rv_status_string", "rv_prefix_default_split"):
+    for n in ("spec_attn_prefix", "spec_attn_block", "lse_merge", "spec_attn_block_merge",
+              "rapid_accept", "rapid_accept_ex", "rapid_accept_workspace_size",
+              "rv_status_string", "rv_prefix_default_split"):
         assert n in names
 
 
@@ -130,6 +131,36 @@ def test_merge_validation(lib):
     assert _merge(lib, n=0) == RV_ERR_SHAPE
     assert _merge(lib, d=256) == RV_ERR_UNSUPPORTED
     assert _merge(lib, ob=MIS) == RV_ERR_ALIGNMENT
+
+
+def _block_merge(lib, parent=None, **kw):
+    a = dict(q=P, k=P, v=P, o=P, l=P, S=4, B=1, Hq=8, Hkv=2, n=5, d=64, scale=1.0, out=P, lo=P)
+    a.update(kw)
+    par = None
+    if parent is not None:
+        arr = (ctypes.c_int32 * len(parent))(*parent)
+        par = ctypes.cast(arr, ctypes.c_void_p)
+    return lib.spec_attn_block_merge(a["q"], a["k"], a["v"], par, a["o"], a["l"], a["S"], a["B"],
+                                     a["Hq"], a["Hkv"], a["n"], a["d"], a["scale"], a["out"],
+                                     a["lo"], None)
+
+
+def test_block_merge_validation(lib):
+    assert _block_merge(lib, q=None) == RV_ERR_NULL
+    assert _block_merge(lib, k=None) == RV_ERR_NULL
+    assert _block_merge(lib, o=None) == RV_ERR_NULL
+    assert _block_merge(lib, out=None) == RV_ERR_NULL
+    assert _block_merge(lib, S=0) == RV_ERR_SHAPE
+    assert _block_merge(lib, n=0) == RV_ERR_SHAPE
+    assert _block_merge(lib, Hq=7) == RV_ERR_SHAPE
+    assert _block_merge(lib, n=65) == RV_ERR_UNSUPPORTED
+    assert _block_merge(lib, d=96) == RV_ERR_UNSUPPORTED
+    assert _block_merge(lib, parent=[0, 0, 1, 2, 3]) == RV_ERR_VALUE
+    assert _block_merge(lib, parent=[-1, 0, 2, 1, 0]) == RV_ERR_VALUE
+    assert _block_merge(lib, scale=0.0) == RV_ERR_VALUE
+    assert _block_merge(lib, scale=float("inf")) == RV_ERR_VALUE
+    assert _block_merge(lib, l=MIS) == RV_ERR_ALIGNMENT
+    assert _block_merge(lib, out=MIS) == RV_ERR_ALIGNMENT
 
 
 def _accept(lib, **kw):

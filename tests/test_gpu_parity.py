@@ -73,15 +73,24 @@ def test_attention_small(case):
     ai, split = _make_case(case)
     announce("attention %s shape=%s lens=%s split=%s" % (case[0], ai.shape, list(ai.seq_lens), split))
     st = VerifyStep(ai, None, split=split)
-    st.attention()
-    out, lse = _attn_outputs(st)
     O_ref, L_ref = attn_ref(ai.q, ai.k_cache, ai.v_cache, ai.k_blk, ai.v_blk, ai.seq_lens,
                             ai.parent, ai.sm_scale)
-    err = attn_row_errors(out, O_ref)
-    dl = np.abs(lse - L_ref).max()
-    announce("  max row rel err %.3e, max |dLSE| %.3e" % (err.max(), dl))
-    assert err.max() <= ATTN_ROW_TOL
-    assert dl <= 1e-2
+    res = {}
+    for fused in (False, True):
+        st.out.zero_()
+        st.lse_out.zero_()
+        st.attention(fused=fused)
+        out, lse = _attn_outputs(st)
+        err = attn_row_errors(out, O_ref)
+        dl = np.abs(lse - L_ref).max()
+        announce("  %s: max row rel err %.3e, max |dLSE| %.3e"
+                 % ("block_merge" if fused else "block+merge", err.max(), dl))
+        assert err.max() <= ATTN_ROW_TOL
+        assert dl <= 1e-2
+        res[fused] = (out, lse)
+    # the fused call differs from the two calls only in fp32 rounding order
+    assert attn_row_errors(res[True][0], res[False][0]).max() <= 1e-2
+    assert np.abs(res[True][1] - res[False][1]).max() <= 1e-4
 
 
 def test_prefix_and_block_partials_match_split_oracle():
@@ -269,8 +278,12 @@ def test_step_is_bit_deterministic():
         st = VerifyStep(ai, vi, want_p_hat=True)
         st.run()
         torch.cuda.synchronize()
-        outs.append([t.cpu().clone() for t in (st.out.view(torch.int16), st.lse_out, st.o_part,
-                                               st.n_accept, st.out_tokens, st.ratio, st.p_hat)])
+        res = [t.cpu().clone() for t in (st.out.view(torch.int16), st.lse_out, st.o_part,
+                                         st.n_accept, st.out_tokens, st.ratio, st.p_hat)]
+        st.attention(fused=True)
+        torch.cuda.synchronize()
+        res += [st.out.view(torch.int16).cpu().clone(), st.lse_out.cpu().clone()]
+        outs.append(res)
     for a, b in zip(*outs):
         assert torch.equal(a, b)
 
@@ -294,19 +307,26 @@ def _config_attention_check(name):
     out, lse = _attn_outputs(st)
     lse_part = st.lse_part.cpu().numpy()
     lse_blk = st.lse_blk.cpu().numpy()
+    st.attention(fused=True)  # the benchmark's step runs the fused block + merge
+    out_f, lse_f = _attn_outputs(st)
     # properties at any size
-    assert np.isfinite(out).all() and np.isfinite(lse).all()
-    assert np.all(lse >= np.maximum(lse_part.max(axis=-1), lse_blk) - 1e-4)
+    for o, l in ((out, lse), (out_f, lse_f)):
+        assert np.isfinite(o).all() and np.isfinite(l).all()
+        assert np.all(l >= np.maximum(lse_part.max(axis=-1), lse_blk) - 1e-4)
+    assert attn_row_errors(out_f, out).max() <= 1e-2
+    assert np.abs(lse_f - lse).max() <= 1e-4
     pairs = _sample_pairs(ai, name)
     announce("  oracle on sampled heads %s" % pairs)
     O_ref, L_ref = attn_ref(ai.q, ai.k_cache, ai.v_cache, ai.k_blk, ai.v_blk, ai.seq_lens,
                             ai.parent, ai.sm_scale, pairs=pairs)
     for i, (b, h) in enumerate(pairs):
-        err = attn_row_errors(out[b, h], O_ref[i])
-        dl = np.abs(lse[b, h] - L_ref[i]).max()
-        announce("  (b=%d,h=%d) max row rel err %.3e |dLSE| %.3e" % (b, h, err.max(), dl))
-        assert err.max() <= ATTN_ROW_TOL
-        assert dl <= 1e-2
+        for tag, o, l in (("block+merge", out, lse), ("block_merge", out_f, lse_f)):
+            err = attn_row_errors(o[b, h], O_ref[i])
+            dl = np.abs(l[b, h] - L_ref[i]).max()
+            announce("  %s (b=%d,h=%d) max row rel err %.3e |dLSE| %.3e"
+                     % (tag, b, h, err.max(), dl))
+            assert err.max() <= ATTN_ROW_TOL
+            assert dl <= 1e-2
 
 
 @pytest.mark.parametrize("name", ["tiny", "llama8b", "llama70b", "qwen7b_ragged"])
