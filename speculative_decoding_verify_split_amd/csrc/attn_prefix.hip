@@ -314,8 +314,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
   for (int mt = 0; mt < MT; ++mt) l_run[mt] = row_sum4(l_run[mt]);
 
   // Each wave parks its state (running max, row sum, unnormalised O) in its
-  // own LDS slot; after one barrier all threads merge the four slots per
-  // row in wave order and write the normalised partial.
+  // own LDS slot.  After a barrier one thread per row turns the four
+  // (max, sum) pairs into the row's LSE and per-wave weights
+  // 2^(m_w - M) / l; after a second barrier every thread forms its share of
+  // the normalised partial with all of its LDS reads in one unrolled batch.
   __syncthreads();  // V tiles are dead; the buffer becomes the merge slots
   float* obuf = reinterpret_cast<float*>(smem);
   {
@@ -334,33 +336,47 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
   }
   __syncthreads();
 
-  for (int idx = threadIdx.x; idx < rows_here * (D / 4); idx += NW * 64) {
-    const int row = idx / (D / 4);
-    const int c4 = idx - row * (D / 4);
+  auto out_row = [&](int row) {  // (b, h, i) index of local row `row`
+    const int grow = row0 + row;
+    const int gq = grow / n;
+    const int i = grow - gq * n;
+    return ((int64_t)b * Hq + kvh * G + gq) * n + i;
+  };
+  if ((int)threadIdx.x < rows_here) {
+    const int row = threadIdx.x;
     float mw[NW], M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
       mw[w] = m_lds[w][row];
       M = fmaxf(M, mw[w]);
     }
-    float l = 0.f;
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    float a[NW], l = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float a = (mw[w] == -INFINITY) ? 0.f : exp2_hw(mw[w] - M);
-      l += a * l_lds[w][row];
-      o += a * *reinterpret_cast<const f32x4*>(obuf + (w * MT * 16 + row) * OROW + c4 * 4);
+      a[w] = (mw[w] == -INFINITY) ? 0.f : exp2_hw(mw[w] - M);
+      l += a[w] * l_lds[w][row];
     }
-    const f32x4 res = l > 0.f ? o / l : f32x4{0.f, 0.f, 0.f, 0.f};
-    const int grow = row0 + row;
-    const int gq = grow / n;
-    const int i = grow - gq * n;
-    const int h = kvh * G + gq;
-    float* dst = o_part + ((((int64_t)b * Hq + h) * n + i) * S + s) * D + c4 * 4;
-    *reinterpret_cast<f32x4*>(dst) = res;
-    if (c4 == 0) {
-      lse_part[(((int64_t)b * Hq + h) * n + i) * S + s] =
-          l > 0.f ? (M + log2_hw(l)) * kLn2 : -INFINITY;
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) m_lds[w][row] = a[w] * inv;  // this row's weights
+    lse_part[out_row(row) * S + s] = l > 0.f ? (M + log2_hw(l)) * kLn2 : -INFINITY;
+  }
+  __syncthreads();
+
+  constexpr int ITEMS = MT * 16 * (D / 4);  // f32x4 items of the partial
+  constexpr int PER_T = (ITEMS + NW * 64 - 1) / (NW * 64);
+#pragma unroll
+  for (int j = 0; j < PER_T; ++j) {
+    const int idx = threadIdx.x + j * NW * 64;
+    const int row = idx / (D / 4);
+    const int c4 = idx - row * (D / 4);
+    if (row < rows_here) {
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+        o += m_lds[w][row] * *reinterpret_cast<const f32x4*>(obuf + (w * MT * 16 + row) * OROW +
+                                                             c4 * 4);
+      *reinterpret_cast<f32x4*>(o_part + (out_row(row) * S + s) * D + c4 * 4) = o;
     }
   }
 }
