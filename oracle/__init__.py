@@ -31,6 +31,10 @@ What it computes, and from which passage:
 All floating point is IEEE binary64.  bf16 inputs arrive as raw uint16 bit
 patterns and are widened exactly; fp32 inputs are widened exactly.
 
+* ``window`` -- the drafter's sliding-window self-attention with attention-
+  sink anchors over its constant-size ring cache (LongSpec summary, sections
+  2.1 and 2.2), written as the definition over the visible positions.
+
 Blog section 2.4 also prints a tail-preserving adjustment of p_hat and a
 different residual; both are available as options of ``rapid_accept_ref``
 (off by default) with the readings stated in ``rapid``.
@@ -47,6 +51,11 @@ from .attention import (  # noqa: F401
     attn_ref,
     attn_keys_ref,
     lse_merge_ref,
+)
+from .window import (  # noqa: F401
+    ring_slot,
+    window_attn_ref,
+    window_positions,
 )
 from .rapid import (  # noqa: F401
     softmax_ref,

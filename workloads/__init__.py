@@ -207,6 +207,42 @@ def make_attention(seed, B, Hq, Hkv, d, n, L, L_max=None, parent=None,
                       seq_lens=seq_lens, parent=parent, sm_scale=1.0)
 
 
+@dataclass
+class WindowInputs:
+    q: np.ndarray       # uint16 bf16 bits [B, Hq, n, d]; row i is position pos[b] + i
+    k_ring: np.ndarray  # uint16 [B, Hkv, cap, d]
+    v_ring: np.ndarray  # uint16 [B, Hkv, cap, d]
+    pos: np.ndarray     # int32 [B]
+    cap: int
+    sink: int
+    window: int
+    sm_scale: float = 1.0
+
+
+def make_window(seed, B, Hq, Hkv, d, n, pos, cap, sink, window, pad_bits=0x7FC0, threads=None):
+    """Drafter self-attention inputs: queries of n consecutive positions and a
+    ring cache of cap slots.  Positions below cap occupy slots 0..cap-1 in
+    order, so while the last query position is below cap - 1 the slots past
+    it have never been written and hold pad_bits (a NaN by default: any read
+    of them shows in the result); once the ring has wrapped every slot holds
+    data."""
+    threads = threads or _threads()
+    ss = np.random.SeedSequence(seed).spawn(_N_SLOTS)
+    pos = np.broadcast_to(np.asarray(pos, dtype=np.int32), (B,)).copy()
+    q = np.empty((B, Hq, n, d), dtype=np.uint16)
+    _fill_normal_bf16(q.reshape(-1), ss[_S_Q], 1.0 / math.sqrt(d), threads)
+    k = np.empty((B, Hkv, cap, d), dtype=np.uint16)
+    v = np.empty((B, Hkv, cap, d), dtype=np.uint16)
+    _fill_normal_bf16(k.reshape(-1), ss[_S_K], 1.0, threads)
+    _fill_normal_bf16(v.reshape(-1), ss[_S_V], 1.0, threads)
+    for b in range(B):
+        written = min(cap, int(pos[b]) + n)
+        k[b, :, written:] = pad_bits
+        v[b, :, written:] = pad_bits
+    return WindowInputs(q=q, k_ring=k, v_ring=v, pos=pos, cap=int(cap), sink=int(sink),
+                        window=int(window))
+
+
 def _uniform_f32(seed_seq, shape):
     g = np.random.Generator(np.random.PCG64(seed_seq))
     bits = g.integers(0, 1 << 32, size=shape, dtype=np.uint64).astype(np.uint32)
