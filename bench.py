@@ -90,6 +90,113 @@ def _calibrate_copy(n_bytes, reps):
     print(json.dumps({"calibration_copy_bytes": n_bytes, "reps": reps}))
 
 
+def _timed_loop(step, K, warmup):
+    import torch
+    for i in range(warmup):
+        step(i)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    return evs, time.perf_counter() - t0
+
+
+def run_drafter(args):
+    """The LongSpec drafter's decode-step attention: cross-attention of one
+    query row per head over the target's cache (spec_attn_prefix at n = 1,
+    history-only lse_merge) and the sliding-window self-attention over the
+    drafter's ring cache (spec_attn_window)."""
+    import numpy as np
+    import torch
+    from oracle import attn_keys_ref, bf16_bits_to_f64, window_attn_ref
+    from speculative_decoding_verify_split_amd import rapid_verify as rv
+    from speculative_decoding_verify_split_amd.step import VerifyStep, WindowStep
+    from workloads import DRAFTER_CONFIGS, config_drafter
+
+    cfg = DRAFTER_CONFIGS[args.workload]
+    cross, win = config_drafter(args.workload)
+    st = VerifyStep(cross, None)
+    ws = WindowStep(win)
+    R = max(1, args.rotate)
+    kvs = [(st.k_cache, st.v_cache)] + [(st.k_cache.clone(), st.v_cache.clone())
+                                        for _ in range(R - 1)]
+
+    def step(i, ev=None):
+        kc, vc = kvs[i % R]
+        if ev is not None:
+            ev[0].record()
+        rv.spec_attn_prefix(st.q, kc, vc, st.seq_lens, st.max_seq_len, st.split_len,
+                            st.num_splits, st.o_part, st.lse_part, st.sm_scale)
+        if ev is not None:
+            ev[1].record()
+        rv.lse_merge(st.o_part, st.lse_part, None, None, st.out, st.lse_out)
+        if ev is not None:
+            ev[2].record()
+        rv.spec_attn_window(ws.q, ws.k_ring, ws.v_ring, ws.pos, ws.sink, ws.window, ws.out,
+                            ws.lse_out, ws.sm_scale)
+        if ev is not None:
+            ev[3].record()
+
+    K = args.steps
+    evs, elapsed = _timed_loop(step, K, args.warmup)
+    prefix_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    merge_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    win_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    L = int(np.max(cross.seq_lens))
+    kv_bytes = int(2 * st.Hkv * st.d * 2 * int(np.sum(cross.seq_lens)))
+    prefix_s = float(np.mean(prefix_ms)) / 1e3
+    achieved = kv_bytes / prefix_s / 1e9
+    line = {
+        "metric": "drafter decode steps/s + KV-stream HBM GB/s, 8B-shaped, 128K ctx, n=1",
+        "value": K / elapsed, "unit": "steps/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / K, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "dtype_detail": "cross-attention: bf16 K/V/Q on MFMA, fp32 accumulation and softmax; "
+                        "window: bf16 inputs, fp32 vector ALU",
+        "data": "synthetic (seeded; K/V/Q ~ N(0,1) bf16)",
+        "config": {"workload": cfg["desc"], "batch": st.B, "q_heads": st.Hq, "kv_heads": st.Hkv,
+                   "head_dim": st.d, "kv_tokens": L, "query_rows": 1,
+                   "window": ws.window, "sink": ws.sink, "split_len": st.split_len,
+                   "num_splits": st.num_splits, "rotated_copies": R,
+                   "parallelism": "single GPU"},
+        "kernels_us": {"spec_attn_prefix": prefix_s * 1e6,
+                       "lse_merge": float(np.mean(merge_ms)) * 1e3,
+                       "spec_attn_window": float(np.mean(win_ms)) * 1e3,
+                       "device_step": float(np.mean(step_ms)) * 1e3},
+        "device_step_us": {"median": float(np.median(step_ms)) * 1e3,
+                           "p10": float(np.percentile(step_ms, 10)) * 1e3,
+                           "p90": float(np.percentile(step_ms, 90)) * 1e3},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "spec_attn_prefix (cross-attention, n=1)",
+                     "algorithmic_bytes_per_launch": kv_bytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        threads = len(os.sched_getaffinity(0))
+        reps, t0 = 0, time.perf_counter()
+        G = st.Hq // st.Hkv
+        while True:
+            for h in range(st.Hq):
+                attn_keys_ref(bf16_bits_to_f64(cross.q[0, h]),
+                              bf16_bits_to_f64(cross.k_cache[0, h // G, :L]),
+                              bf16_bits_to_f64(cross.v_cache[0, h // G, :L]),
+                              np.ones((1, L), bool), 1.0)
+            window_attn_ref(win.q, win.k_ring, win.v_ring, win.pos, win.cap, win.sink, win.window)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= args.cpu_budget or reps >= 20:
+                break
+        line["cpu_baseline"] = {"value": reps / el, "unit": "steps/s", "cores": threads,
+                                "kind": "oracle",
+                                "sample": "%d full drafter step(s) (all %d heads over %d tokens + "
+                                          "window), %.1f s" % (reps, st.Hq, L, el)}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +232,10 @@ def main():
     if args.calibrate_copy:
         _calibrate_copy(args.calibrate_copy, max(1, args.steps))
         return
+
+    from workloads import DRAFTER_CONFIGS
+    if args.workload in DRAFTER_CONFIGS:
+        return run_drafter(args)
 
     from speculative_decoding_verify_split_amd import rapid_verify as rv
     from speculative_decoding_verify_split_amd.step import VerifyStep

@@ -146,9 +146,14 @@ rv_status spec_attn_block(const void* q, const void* k_blk, const void* v_blk,
  * Partials with LSE = -inf have weight 0.
  *
  *   o_part, lse_part  fp32 [B, Hq, n, S, d], [B, Hq, n, S]
- *   o_blk, lse_blk    fp32 [B, Hq, n, d],    [B, Hq, n]
+ *   o_blk, lse_blk    fp32 [B, Hq, n, d],    [B, Hq, n], or both NULL to
+ *                     merge the history partials alone (e.g. a drafter's
+ *                     cross-attention over the target's cache, LongSpec
+ *                     summary section 2.1); one NULL without the other is
+ *                     RV_ERR_NULL
  *   out               bf16 [B, Hq, n, d]  (round to nearest even)
  *   lse_out           fp32 [B, Hq, n] or NULL
+ * A row with no visible key at all gets out = 0 and lse_out = -inf.
  */
 rv_status lse_merge(const float* o_part, const float* lse_part, int S, const float* o_blk,
                     const float* lse_blk, int B, int Hq, int n, int d, void* out,
@@ -171,6 +176,37 @@ rv_status spec_attn_block_merge(const void* q, const void* k_blk, const void* v_
                                 const int32_t* parent_host, const float* o_part,
                                 const float* lse_part, int S, int B, int Hq, int Hkv, int n,
                                 int d, float sm_scale, void* out, float* lse_out, void* stream);
+
+/*
+ * spec_attn_window -- the drafter's sliding-window self-attention with
+ * attention-sink anchors over its constant-size ring cache (LongSpec
+ * summary, section 2.1: the drafter's self-attention sees only the latest
+ * `window` tokens, so its own cache does not grow with the context; section
+ * 2.2: the first tokens are kept as anchors).
+ *
+ *   q        bf16 [B, Hq, n, d]   row i of sequence b is the token at
+ *                                 position pos[b] + i
+ *   k_ring, v_ring bf16 [B, Hkv, cap, d]  the drafter's cache: position p
+ *                                 is in slot p if p < sink, else in slot
+ *                                 sink + (p - sink) mod (cap - sink); the
+ *                                 caller has written every position up to
+ *                                 pos[b] + n - 1
+ *   pos      device int32 [B]     clamped on the device to [0, 2^30]
+ *   cap, sink, window             1 <= window, 0 <= sink,
+ *                                 cap - sink >= window + n - 1 (so every
+ *                                 visible position is still resident), else
+ *                                 RV_ERR_SHAPE
+ *   sm_scale finite and > 0
+ *   out      bf16 [B, Hq, n, d]   (round to nearest even)
+ *   lse_out  fp32 [B, Hq, n] or NULL  natural-log sum exp of the scores
+ * The row at position P sees positions p <= P with p < sink or
+ * p > P - window (the window includes the row itself).  Query head h reads
+ * kv head h / (Hq / Hkv).  Supports d in {64, 128}, 1 <= n <= 64.
+ */
+rv_status spec_attn_window(const void* q, const void* k_ring, const void* v_ring,
+                           const int32_t* pos, int B, int Hq, int Hkv, int n, int d, int cap,
+                           int sink, int window, float sm_scale, void* out, float* lse_out,
+                           void* stream);
 
 /* Bytes of device workspace rapid_accept needs for (B, gamma, V). */
 size_t rapid_accept_workspace_size(int B, int gamma, int V);

@@ -3,6 +3,8 @@
 // the outputs of the two parts are combined with the log-sum-exp trick).
 // With M = max_k LSE_k and a_k = exp(LSE_k - M):
 //   O = sum_k a_k O_k / sum_k a_k,   LSE = M + log sum_k a_k.
+// Without a block partial (o_blk = lse_blk = NULL) the history partials are
+// merged alone, as for a drafter's cross-attention over the target cache.
 //
 // One 4-wave workgroup per output row; the row's S partials are contiguous
 // ([row][S][d]).  Wave w folds splits w, w + 4, ... (each step one 4*d-byte
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
   float M = -INFINITY;
   for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[s]);
   M = wave_max(M);
-  const float lb = lse_blk[row];
+  const float lb = lse_blk != nullptr ? lse_blk[row] : -INFINITY;  // no block part: weight 0
   M = fmaxf(M, lb);
   float acc[PER];
 #pragma unroll
@@ -104,7 +106,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
     const int c = lane * PER + e;
     res[e] = ((part[0][c] + part[1][c]) + part[2][c]) + part[3][c];
   }
-  if (M != -INFINITY) {
+  if (M != -INFINITY && lse_blk != nullptr) {
     const float a = exp2_hw((lb - M) * kLog2e);
     tot += a;
     const float* bp = o_blk + (size_t)row * D + lane * PER;

@@ -43,6 +43,14 @@ rv_status check_block_merge(const void* q, const void* k_blk, const void* v_blk,
                             const float* lse_part, int S, int B, int Hq, int Hkv, int n, int d,
                             float sm_scale, const void* out, BlockMask* mask);
 
+// Largest first-row position spec_attn_window accepts (device values above
+// it are clamped), so that positions of a block's rows stay in int range.
+constexpr int kMaxWindowPos = 1 << 30;
+
+rv_status check_window(const void* q, const void* k_ring, const void* v_ring,
+                       const int32_t* pos, int B, int Hq, int Hkv, int n, int d, int cap,
+                       int sink, int window, float sm_scale, const void* out);
+
 rv_status check_merge(const float* o_part, const float* lse_part, int S, const float* o_blk,
                       const float* lse_blk, int B, int Hq, int n, int d, const void* out);
 

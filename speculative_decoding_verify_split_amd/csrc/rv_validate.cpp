@@ -105,16 +105,32 @@ rv_status check_block_merge(const void* q, const void* k_blk, const void* v_blk,
   return block_mask(parent_host, n, mask);
 }
 
+rv_status check_window(const void* q, const void* k_ring, const void* v_ring,
+                       const int32_t* pos, int B, int Hq, int Hkv, int n, int d, int cap,
+                       int sink, int window, float sm_scale, const void* out) {
+  if (!q || !k_ring || !v_ring || !pos || !out) return RV_ERR_NULL;
+  rv_status st = check_heads(B, Hq, Hkv, n, d);
+  if (st != RV_OK) return st;
+  if (window < 1 || sink < 0 || cap < 1) return RV_ERR_SHAPE;
+  // every position a row of the block sees must still be in the ring
+  if ((int64_t)cap - sink < (int64_t)window + n - 1) return RV_ERR_SHAPE;
+  if (!isfinite(sm_scale) || !(sm_scale > 0.0f)) return RV_ERR_VALUE;
+  if (!aligned16(q) || !aligned16(k_ring) || !aligned16(v_ring) || !aligned16(out))
+    return RV_ERR_ALIGNMENT;
+  if ((int64_t)B * Hq * n > 0x7fffffff / 4) return RV_ERR_UNSUPPORTED;  // one row per workgroup
+  return RV_OK;
+}
+
 rv_status check_merge(const float* o_part, const float* lse_part, int S, const float* o_blk,
                       const float* lse_blk, int B, int Hq, int n, int d, const void* out) {
-  if (!o_part || !lse_part || !o_blk || !lse_blk || !out) return RV_ERR_NULL;
+  if (!o_part || !lse_part || !out) return RV_ERR_NULL;
+  if ((o_blk == nullptr) != (lse_blk == nullptr)) return RV_ERR_NULL;  // both or neither
   if (B < 1 || Hq < 1 || n < 1 || S < 1) return RV_ERR_SHAPE;
   if (n > RV_MAX_BLOCK_ROWS) return RV_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return RV_ERR_UNSUPPORTED;
   if ((int64_t)B * Hq * n > 0x7fffffff / 4) return RV_ERR_UNSUPPORTED;
-  if (!aligned16(o_part) || !aligned16(lse_part) || !aligned16(o_blk) || !aligned16(lse_blk) ||
-      !aligned16(out))
-    return RV_ERR_ALIGNMENT;
+  if (!aligned16(o_part) || !aligned16(lse_part) || !aligned16(out)) return RV_ERR_ALIGNMENT;
+  if (o_blk && (!aligned16(o_blk) || !aligned16(lse_blk))) return RV_ERR_ALIGNMENT;
   return RV_OK;
 }
 

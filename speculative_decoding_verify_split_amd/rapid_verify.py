@@ -53,6 +53,9 @@ def load_library():
     lib.spec_attn_block_merge.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                           f32, vp, vp, vp]
     lib.spec_attn_block_merge.restype = i32
+    lib.spec_attn_window.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32,
+                                     vp, vp, vp]
+    lib.spec_attn_window.restype = i32
     lib.rapid_accept_workspace_size.argtypes = [i32, i32, i32]
     lib.rapid_accept_workspace_size.restype = sz
     lib.rapid_accept.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp, vp, vp, vp,
@@ -157,13 +160,17 @@ def spec_attn_block(q, k_blk, v_blk, parent, o_blk, lse_blk, sm_scale=1.0, strea
 
 
 def lse_merge(o_part, lse_part, o_blk, lse_blk, out, lse_out=None, stream=None):
-    """Merge.  out bf16 [B,Hq,n,d]; lse_out fp32 [B,Hq,n] or None."""
+    """Merge.  out bf16 [B,Hq,n,d]; lse_out fp32 [B,Hq,n] or None; o_blk and
+    lse_blk both None to merge the history partials alone."""
     import torch
     _need(o_part, "o_part", torch.float32)
     B, Hq, n, S, d = o_part.shape
     _need(lse_part, "lse_part", torch.float32, (B, Hq, n, S))
-    _need(o_blk, "o_blk", torch.float32, (B, Hq, n, d))
-    _need(lse_blk, "lse_blk", torch.float32, (B, Hq, n))
+    if (o_blk is None) != (lse_blk is None):
+        raise ValueError("o_blk and lse_blk must both be given or both be None")
+    if o_blk is not None:
+        _need(o_blk, "o_blk", torch.float32, (B, Hq, n, d))
+        _need(lse_blk, "lse_blk", torch.float32, (B, Hq, n))
     _need(out, "out", torch.bfloat16, (B, Hq, n, d))
     if lse_out is not None:
         _need(lse_out, "lse_out", torch.float32, (B, Hq, n))
@@ -200,6 +207,27 @@ def spec_attn_block_merge(q, k_blk, v_blk, parent, o_part, lse_part, out, lse_ou
         _ptr(q), _ptr(k_blk), _ptr(v_blk), ctypes.cast(par, ctypes.c_void_p) if par else None,
         _ptr(o_part), _ptr(lse_part), S, B, Hq, Hkv, n, d, float(sm_scale), _ptr(out),
         _ptr(lse_out), _stream(stream)), "spec_attn_block_merge")
+
+
+def spec_attn_window(q, k_ring, v_ring, pos, sink, window, out, lse_out=None, sm_scale=1.0,
+                     stream=None):
+    """Drafter self-attention.  q bf16 [B,Hq,n,d]; k_ring/v_ring bf16
+    [B,Hkv,cap,d]; pos int32 [B]; out bf16 [B,Hq,n,d]; lse_out fp32 [B,Hq,n]."""
+    import torch
+    _need(q, "q", torch.bfloat16)
+    B, Hq, n, d = q.shape
+    _need(k_ring, "k_ring", torch.bfloat16)
+    Hkv, cap = k_ring.shape[1], k_ring.shape[2]
+    _need(k_ring, "k_ring", torch.bfloat16, (B, Hkv, cap, d))
+    _need(v_ring, "v_ring", torch.bfloat16, (B, Hkv, cap, d))
+    _need(pos, "pos", torch.int32, (B,))
+    _need(out, "out", torch.bfloat16, (B, Hq, n, d))
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, (B, Hq, n))
+    _check(load_library().spec_attn_window(
+        _ptr(q), _ptr(k_ring), _ptr(v_ring), _ptr(pos), B, Hq, Hkv, n, d, cap, int(sink),
+        int(window), float(sm_scale), _ptr(out), _ptr(lse_out), _stream(stream)),
+        "spec_attn_window")
 
 
 def rapid_accept_workspace_size(B, gamma, V):

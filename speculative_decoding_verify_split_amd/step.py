@@ -78,15 +78,19 @@ class VerifyStep:
             self.p_hat = (torch.empty((Bv, self.gamma, V), dtype=f32, device=device)
                           if want_p_hat else None)
 
-    def attention(self, k_cache=None, v_cache=None, stream=None, fused=False):
+    def attention(self, k_cache=None, v_cache=None, stream=None, fused=False, block=True):
         """The attention calls; k_cache/v_cache override the resident cache
         (same shape), e.g. to rotate copies when timing.  fused: the block
         pass and the merge as one spec_attn_block_merge call (o_blk and
-        lse_blk are then left untouched)."""
+        lse_blk are then left untouched).  block=False: no draft block, the
+        history partials are merged alone (a drafter's cross-attention)."""
         kc = self.k_cache if k_cache is None else k_cache
         vc = self.v_cache if v_cache is None else v_cache
         rv.spec_attn_prefix(self.q, kc, vc, self.seq_lens, self.max_seq_len, self.split_len,
                             self.num_splits, self.o_part, self.lse_part, self.sm_scale, stream)
+        if not block:
+            rv.lse_merge(self.o_part, self.lse_part, None, None, self.out, self.lse_out, stream)
+            return
         if fused:
             rv.spec_attn_block_merge(self.q, self.k_blk, self.v_blk, self.parent, self.o_part,
                                      self.lse_part, self.out, self.lse_out, self.sm_scale, stream)
@@ -112,3 +116,24 @@ class VerifyStep:
             self.attention(stream=stream, fused=fused)
         if self.vocab is not None:
             self.accept(stream=stream)
+
+
+class WindowStep:
+    """Device copies of a workloads.WindowInputs-like object and the output
+    buffers of spec_attn_window."""
+
+    def __init__(self, win, device="cuda"):
+        import torch
+        self.win = win
+        B, Hq, n, d = win.q.shape
+        self.q = bf16_to_device(win.q, device)
+        self.k_ring = bf16_to_device(win.k_ring, device)
+        self.v_ring = bf16_to_device(win.v_ring, device)
+        self.pos = to_device(np.asarray(win.pos, dtype=np.int32), device)
+        self.sink, self.window, self.sm_scale = int(win.sink), int(win.window), float(win.sm_scale)
+        self.out = torch.empty((B, Hq, n, d), dtype=torch.bfloat16, device=device)
+        self.lse_out = torch.empty((B, Hq, n), dtype=torch.float32, device=device)
+
+    def run(self, stream=None):
+        rv.spec_attn_window(self.q, self.k_ring, self.v_ring, self.pos, self.sink, self.window,
+                            self.out, self.lse_out, self.sm_scale, stream)

@@ -38,6 +38,7 @@ def declared_functions():
 def test_header_declares_the_four_calls():
     names = declared_functions()
     for n in ("spec_attn_prefix", "spec_attn_block", "lse_merge", "spec_attn_block_merge",
+              "spec_attn_window",
               "rapid_accept", "rapid_accept_ex", "rapid_accept_workspace_size",
               "rv_status_string", "rv_prefix_default_split"):
         assert n in names
@@ -131,6 +132,9 @@ def test_merge_validation(lib):
     assert _merge(lib, n=0) == RV_ERR_SHAPE
     assert _merge(lib, d=256) == RV_ERR_UNSUPPORTED
     assert _merge(lib, ob=MIS) == RV_ERR_ALIGNMENT
+    assert _merge(lib, ob=None) == RV_ERR_NULL   # block partial: both or neither
+    assert _merge(lib, lb=None) == RV_ERR_NULL
+    assert _merge(lib, ob=None, lb=None, S=0) == RV_ERR_SHAPE  # neither: accepted shape-wise
 
 
 def _block_merge(lib, parent=None, **kw):
@@ -161,6 +165,32 @@ def test_block_merge_validation(lib):
     assert _block_merge(lib, scale=float("inf")) == RV_ERR_VALUE
     assert _block_merge(lib, l=MIS) == RV_ERR_ALIGNMENT
     assert _block_merge(lib, out=MIS) == RV_ERR_ALIGNMENT
+
+
+def _window(lib, **kw):
+    a = dict(q=P, k=P, v=P, pos=P, B=1, Hq=8, Hkv=2, n=1, d=128, cap=516, sink=4, window=512,
+             scale=1.0, out=P, lo=P)
+    a.update(kw)
+    return lib.spec_attn_window(a["q"], a["k"], a["v"], a["pos"], a["B"], a["Hq"], a["Hkv"],
+                                a["n"], a["d"], a["cap"], a["sink"], a["window"], a["scale"],
+                                a["out"], a["lo"], None)
+
+
+def test_window_validation(lib):
+    assert _window(lib, q=None) == RV_ERR_NULL
+    assert _window(lib, pos=None) == RV_ERR_NULL
+    assert _window(lib, out=None) == RV_ERR_NULL
+    assert _window(lib, Hq=7) == RV_ERR_SHAPE
+    assert _window(lib, d=96) == RV_ERR_UNSUPPORTED
+    assert _window(lib, n=65) == RV_ERR_UNSUPPORTED
+    assert _window(lib, window=0) == RV_ERR_SHAPE
+    assert _window(lib, sink=-1) == RV_ERR_SHAPE
+    assert _window(lib, cap=515) == RV_ERR_SHAPE          # window + sink no longer resident
+    assert _window(lib, n=3, cap=517) == RV_ERR_SHAPE     # a block needs window + n - 1 slots
+    assert _window(lib, scale=0.0) == RV_ERR_VALUE
+    assert _window(lib, scale=float("nan")) == RV_ERR_VALUE
+    assert _window(lib, k=MIS) == RV_ERR_ALIGNMENT
+    assert _window(lib, out=MIS) == RV_ERR_ALIGNMENT
 
 
 def _accept(lib, **kw):

@@ -60,6 +60,17 @@ CONFIGS = {
                    etas=(0.5,), seed=500),
 }
 
+# LongSpec drafter workloads: the drafter's decode step, one query row per
+# head cross-attending over the target's cache, and its sliding-window
+# self-attention with sink anchors over its own ring cache of sink + window
+# slots, for the token at position L.
+DRAFTER_CONFIGS = {
+    "drafter8b": dict(desc="LongSpec drafter decode step at the LLaMA-3.1-8B shape: one query "
+                           "row per head over the target's 128K cache (32/8 heads, d=128) + "
+                           "512-token sliding window with 4 anchors",
+                      B=1, Hq=32, Hkv=8, d=128, L=131072, window=512, sink=4, seed=600),
+}
+
 # child-stream slots of SeedSequence(seed).spawn(...)
 _S_LENS, _S_Q, _S_K, _S_V, _S_KB, _S_VB, _S_TREE, _S_Z, _S_Y, _S_G, _S_R, _S_U = range(12)
 _N_SLOTS = 12
@@ -293,3 +304,15 @@ def config_vocab(name, eta=None, B_override=None, V_override=None):
     B = B_override or c["B"]
     V = V_override or c["V"]
     return make_vocab(c["seed"], B, c["gamma"], V, c["z_sigma"], c["noise"], c["T"], eta)
+
+
+def config_drafter(name, threads=None):
+    """(cross-attention inputs with n = 1, window inputs) of a drafter workload.
+    The cross-attention inputs' block tensors are unused (no draft block)."""
+    c = DRAFTER_CONFIGS[name]
+    cross = make_attention(c["seed"], c["B"], c["Hq"], c["Hkv"], c["d"], 1, c["L"],
+                           threads=threads)
+    win = make_window(c["seed"] + 1, c["B"], c["Hq"], c["Hkv"], c["d"], 1, pos=c["L"],
+                      cap=c["sink"] + c["window"], sink=c["sink"], window=c["window"],
+                      threads=threads)
+    return cross, win
