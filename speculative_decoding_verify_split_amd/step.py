@@ -137,3 +137,40 @@ class WindowStep:
     def run(self, stream=None):
         rv.spec_attn_window(self.q, self.k_ring, self.v_ring, self.pos, self.sink, self.window,
                             self.out, self.lse_out, self.sm_scale, stream)
+
+
+class ModelStep:
+    """Every attention layer of a model's verify step, then one acceptance
+    pass.  Layer inputs are generated on the device by workloads'
+    make_layer_device; the split partials are reused from layer to layer
+    (stream order keeps each merge ahead of the next layer's history pass);
+    each layer keeps its own output."""
+
+    def __init__(self, layers, B, Hq, Hkv, d, n, L, seed, vocab=None, device="cuda"):
+        import torch
+        from workloads import make_layer_device
+        self.B, self.Hq, self.Hkv, self.d, self.n, self.L = B, Hq, Hkv, d, n, L
+        self.seed = seed
+        self.layer_inputs = [make_layer_device(seed, l, B, Hq, Hkv, d, n, L, device)
+                             for l in range(layers)]
+        self.seq_lens = torch.full((B,), L, dtype=torch.int32, device=device)
+        self.split_len, self.num_splits = rv.rv_prefix_default_split(L, B, Hq, Hkv, n, d)
+        S = self.num_splits
+        f32 = torch.float32
+        self.o_part = torch.empty((B, Hq, n, S, d), dtype=f32, device=device)
+        self.lse_part = torch.empty((B, Hq, n, S), dtype=f32, device=device)
+        self.out = torch.empty((layers, B, Hq, n, d), dtype=torch.bfloat16, device=device)
+        self.lse_out = torch.empty((layers, B, Hq, n), dtype=f32, device=device)
+        self.vocab = VerifyStep(None, vocab, want_ratio=False, device=device) if vocab else None
+
+    def attention(self, stream=None):
+        for l, (q, k, v, kb, vb) in enumerate(self.layer_inputs):
+            rv.spec_attn_prefix(q, k, v, self.seq_lens, self.L, self.split_len, self.num_splits,
+                                self.o_part, self.lse_part, 1.0, stream)
+            rv.spec_attn_block_merge(q, kb, vb, None, self.o_part, self.lse_part, self.out[l],
+                                     self.lse_out[l], 1.0, stream)
+
+    def run(self, stream=None):
+        self.attention(stream)
+        if self.vocab is not None:
+            self.vocab.accept(stream=stream)

@@ -316,3 +316,38 @@ def config_drafter(name, threads=None):
                       cap=c["sink"] + c["window"], sink=c["sink"], window=c["window"],
                       threads=threads)
     return cross, win
+
+
+# Whole-model verify step: every attention layer of the 8B-shaped model at
+# 128K tokens (32 layers, 17.2 GB of bf16 K/V), then one acceptance pass.
+MODEL_CONFIGS = {
+    "llama8b_model": dict(desc="LLaMA-3.1-8B-shaped model verify step: 32 attention layers "
+                               "(32/8 heads, d=128, 128K cache, gamma=10) + one acceptance "
+                               "pass over vocab 128256",
+                          layers=32, layer_config="llama8b", seed=700),
+}
+
+
+def make_layer_device(seed, layer, B, Hq, Hkv, d, n, L, device="cuda"):
+    """One layer's attention inputs generated on the device (the host cannot
+    hold a 32-layer cache quickly): a torch generator seeded with
+    (seed, layer) draws N(0, 1) fp32 per tensor in a fixed order, rounded to
+    bf16 (nearest-even); Q is scaled by 1/sqrt(d) before rounding, so the
+    attention scale is 1.  Returns (q, k_cache, v_cache, k_blk, v_blk) as
+    torch bf16 tensors."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1000003 + int(layer))
+
+    def draw(shape, scale=1.0):
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        if scale != 1.0:
+            x *= scale
+        return x.to(torch.bfloat16)
+
+    q = draw((B, Hq, n, d), 1.0 / math.sqrt(d))
+    kb = draw((B, Hkv, n, d))
+    vb = draw((B, Hkv, n, d))
+    k = draw((B, Hkv, L, d))
+    v = draw((B, Hkv, L, d))
+    return q, k, v, kb, vb
