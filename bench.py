@@ -34,6 +34,37 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "spec_attn_prefix_llama8b_traffic.
 PREFIX_SRC = os.path.join(ROOT, "speculative_decoding_verify_split_amd", "csrc", "attn_prefix.hip")
 
 
+class _HipEvents:
+    """Raw HIP events (the runtime torch already loaded), for
+    spec_attn_prefix_ev: recorded on the kernel's own dispatch."""
+
+    def __init__(self, count):
+        import ctypes
+        self._c = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.ev = []
+        for _ in range(count):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.ev.append(e)
+
+    def record(self, idx, stream):
+        if self.hip.hipEventRecord(self.ev[idx], self._c.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        ms = self._c.c_float()
+        if self.hip.hipEventElapsedTime(self._c.byref(ms), self.ev[a], self.ev[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
+
+
 def _src_sha():
     return hashlib.sha256(open(PREFIX_SRC, "rb").read()).hexdigest()
 
@@ -330,15 +361,23 @@ def main():
                                         for _ in range(R - 1)]
     logits = [(st.z, st.y)] + [(st.z.clone(), st.y.clone()) for _ in range(R - 1)]
 
-    def step(i, ev=None):
+    K = args.steps
+    # four raw HIP events per timed step: the history kernel's own dispatch
+    # start and end (spec_attn_prefix_ev), then after the block + merge and
+    # after the acceptance pass
+    hev = _HipEvents(4 * K)
+    sid = torch.cuda.current_stream().cuda_stream
+
+    def step(i, timed=False):
         kc, vc = kvs[i % R]
         z, y = logits[i % R]
-        if ev is not None:
-            ev[0].record()
-        rv.spec_attn_prefix(st.q, kc, vc, st.seq_lens, st.max_seq_len, st.split_len,
-                            st.num_splits, st.o_part, st.lse_part, st.sm_scale)
-        if ev is not None:
-            ev[1].record()
+        if timed:
+            rv.spec_attn_prefix_ev(st.q, kc, vc, st.seq_lens, st.max_seq_len, st.split_len,
+                                   st.num_splits, st.o_part, st.lse_part, hev.ev[4 * i],
+                                   hev.ev[4 * i + 1], st.sm_scale)
+        else:
+            rv.spec_attn_prefix(st.q, kc, vc, st.seq_lens, st.max_seq_len, st.split_len,
+                                st.num_splits, st.o_part, st.lse_part, st.sm_scale)
         if args.unfused:
             rv.spec_attn_block(st.q, st.k_blk, st.v_blk, st.parent, st.o_blk, st.lse_blk,
                                st.sm_scale)
@@ -346,21 +385,19 @@ def main():
         else:
             rv.spec_attn_block_merge(st.q, st.k_blk, st.v_blk, st.parent, st.o_part, st.lse_part,
                                      st.out, st.lse_out, st.sm_scale)
-        if ev is not None:
-            ev[2].record()
+        if timed:
+            hev.record(4 * i + 2, sid)
         rv.rapid_accept(z, y, st.draft, st.r, st.u, st.T, st.eta, st.n_accept, st.out_tokens,
                         st.workspace)
-        if ev is not None:
-            ev[3].record()
+        if timed:
+            hev.record(4 * i + 3, sid)
 
     for i in range(args.warmup):
         step(i)
-    K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(i, evs[i])
+        step(i, timed=True)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -393,10 +430,11 @@ def main():
                  "note": "same K steps replayed from HIP graphs (one per rotated copy), "
                          "after the timed eager region"}
 
-    prefix_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    attn_ms = [e[0].elapsed_time(e[2]) for e in evs]
-    acc_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    step_dev_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    prefix_ms = [hev.elapsed_ms(4 * i, 4 * i + 1) for i in range(K)]
+    attn_ms = [hev.elapsed_ms(4 * i, 4 * i + 2) for i in range(K)]
+    acc_ms = [hev.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(K)]
+    step_dev_ms = [hev.elapsed_ms(4 * i, 4 * i + 3) for i in range(K)]
+    hev.close()
     B, Hkv, d = st.B, st.Hkv, st.d
     kv_bytes = int(2 * Hkv * d * 2 * int(np.sum(ai.seq_lens)))  # K and V, bf16
     prefix_s = float(np.mean(prefix_ms)) / 1e3

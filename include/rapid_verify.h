@@ -119,6 +119,21 @@ rv_status spec_attn_prefix(const void* q, const void* k_cache, const void* v_cac
                            void* stream);
 
 /*
+ * spec_attn_prefix_ev -- spec_attn_prefix that also records two HIP events
+ * on the history kernel's own dispatch, for callers that time it:
+ * start_event and stop_event are hipEvent_t created by the caller (either may
+ * be NULL) and take the kernel's start and end timestamps, so
+ * hipEventElapsedTime(start, stop) is the kernel's duration, without the
+ * marker packets a record before and after the call would add.  Everything
+ * else as spec_attn_prefix.
+ */
+rv_status spec_attn_prefix_ev(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* seq_lens, int64_t max_seq_len, int B, int Hq,
+                              int Hkv, int n, int d, int64_t L_max, float sm_scale,
+                              int64_t split_len, int num_splits, float* o_part, float* lse_part,
+                              void* stream, void* start_event, void* stop_event);
+
+/*
  * spec_attn_block -- attention of the block rows over the block's own keys
  * under the speculative mask (LongSpec summary, section 2.3: only the few
  * speculative tokens need a mask).

@@ -22,5 +22,6 @@ from .rapid_verify import (  # noqa: F401
     spec_attn_block,
     spec_attn_block_merge,
     spec_attn_prefix,
+    spec_attn_prefix_ev,
     spec_attn_window,
 )

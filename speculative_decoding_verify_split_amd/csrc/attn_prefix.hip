@@ -29,6 +29,8 @@
 // after one barrier, all threads merge them and write one normalised partial
 // (O, LSE) per row.
 
+#include <hip/hip_ext.h>
+
 #include "rv_device.h"
 #include "rv_internal.h"
 
@@ -381,28 +383,37 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
   }
 }
 
+// With start/stop events the launch records them on the kernel's own
+// dispatch (hipExtLaunchKernel), so their elapsed time is the kernel's.
 template <int D, int MT>
 hipError_t launch_attn(const void* q, const void* k, const void* v, const int32_t* seq_lens,
                        int B, int Hq, int Hkv, int n, int64_t L_max, float scale_log2,
                        int64_t split_len, int S, int RG, float* o_part, float* lse_part,
-                       hipStream_t stream) {
+                       hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
   dim3 grid((unsigned)S, (unsigned)(Hkv * RG), (unsigned)B);
-  hipLaunchKernelGGL((attn_kernel<D, MT>), grid, dim3(NW * 64), 0, stream,
-                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                     static_cast<const uint16_t*>(v), seq_lens, Hq, Hkv, n, L_max, scale_log2,
-                     split_len, S, RG, o_part, lse_part);
+  const uint16_t* qq = static_cast<const uint16_t*>(q);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const uint16_t* vv = static_cast<const uint16_t*>(v);
+  if (ev_start != nullptr || ev_stop != nullptr)
+    hipExtLaunchKernelGGL((attn_kernel<D, MT>), grid, dim3(NW * 64), 0, stream, ev_start,
+                          ev_stop, 0, qq, kk, vv, seq_lens, Hq, Hkv, n, L_max, scale_log2,
+                          split_len, S, RG, o_part, lse_part);
+  else
+    hipLaunchKernelGGL((attn_kernel<D, MT>), grid, dim3(NW * 64), 0, stream, qq, kk, vv,
+                       seq_lens, Hq, Hkv, n, L_max, scale_log2, split_len, S, RG, o_part,
+                       lse_part);
   return hipGetLastError();
 }
 
 rv_status dispatch_attn(int d, int MTW, const void* q, const void* k, const void* v,
                         const int32_t* seq_lens, int B, int Hq, int Hkv, int n, int64_t L_max,
                         float scale_log2, int64_t split_len, int S, int RG, float* o_part,
-                        float* lse_part, hipStream_t s) {
+                        float* lse_part, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   hipError_t e;
 #define RV_ATTN_CASE(DD, MM)                                                                 \
   if (d == DD && MTW == MM)                                                                  \
     e = launch_attn<DD, MM>(q, k, v, seq_lens, B, Hq, Hkv, n, L_max, scale_log2, split_len,  \
-                            S, RG, o_part, lse_part, s);
+                            S, RG, o_part, lse_part, s, e0, e1);
   RV_ATTN_CASE(64, 1)
   else RV_ATTN_CASE(64, 2) else RV_ATTN_CASE(64, 3) else RV_ATTN_CASE(64, 4)
   else RV_ATTN_CASE(128, 1) else RV_ATTN_CASE(128, 2) else RV_ATTN_CASE(128, 3)
@@ -430,5 +441,23 @@ extern "C" rv_status spec_attn_prefix(const void* q, const void* k_cache, const 
   const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
   return rv::dispatch_attn(d, rp.MTW, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, n, L_max,
                            scale_log2, split_len, num_splits, rp.RG, o_part, lse_part,
-                           static_cast<hipStream_t>(stream));
+                           static_cast<hipStream_t>(stream), nullptr, nullptr);
+}
+
+extern "C" rv_status spec_attn_prefix_ev(const void* q, const void* k_cache,
+                                         const void* v_cache, const int32_t* seq_lens,
+                                         int64_t max_seq_len, int B, int Hq, int Hkv, int n,
+                                         int d, int64_t L_max, float sm_scale, int64_t split_len,
+                                         int num_splits, float* o_part, float* lse_part,
+                                         void* stream, void* start_event, void* stop_event) {
+  rv_status st = rv::check_prefix(q, k_cache, v_cache, seq_lens, max_seq_len, B, Hq, Hkv, n, d,
+                                  L_max, sm_scale, split_len, num_splits, o_part, lse_part);
+  if (st != RV_OK) return st;
+  const rv::RowPlan rp = rv::row_plan(Hq, Hkv, n);
+  const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  return rv::dispatch_attn(d, rp.MTW, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, n, L_max,
+                           scale_log2, split_len, num_splits, rp.RG, o_part, lse_part,
+                           static_cast<hipStream_t>(stream),
+                           static_cast<hipEvent_t>(start_event),
+                           static_cast<hipEvent_t>(stop_event));
 }

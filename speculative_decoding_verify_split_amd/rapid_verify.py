@@ -46,6 +46,9 @@ def load_library():
     lib.spec_attn_prefix.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i64, f32, i64,
                                      i32, vp, vp, vp]
     lib.spec_attn_prefix.restype = i32
+    lib.spec_attn_prefix_ev.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i64, f32,
+                                        i64, i32, vp, vp, vp, vp, vp]
+    lib.spec_attn_prefix_ev.restype = i32
     lib.spec_attn_block.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, vp, vp, vp]
     lib.spec_attn_block.restype = i32
     lib.lse_merge.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, vp, vp, vp]
@@ -134,6 +137,28 @@ def spec_attn_prefix(q, k_cache, v_cache, seq_lens, max_seq_len, split_len, num_
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), int(max_seq_len), B, Hq, Hkv, n, d,
         L_max, float(sm_scale), int(split_len), int(num_splits), _ptr(o_part), _ptr(lse_part),
         _stream(stream)), "spec_attn_prefix")
+
+
+def spec_attn_prefix_ev(q, k_cache, v_cache, seq_lens, max_seq_len, split_len, num_splits,
+                        o_part, lse_part, start_event, stop_event, sm_scale=1.0, stream=None):
+    """spec_attn_prefix recording two caller-created hipEvent_t handles (ints
+    or ctypes pointers; None allowed) on the history kernel's own dispatch."""
+    import torch
+    _need(q, "q", torch.bfloat16)
+    B, Hq, n, d = q.shape
+    _need(k_cache, "k_cache", torch.bfloat16)
+    Hkv, L_max = k_cache.shape[1], k_cache.shape[2]
+    _need(k_cache, "k_cache", torch.bfloat16, (B, Hkv, L_max, d))
+    _need(v_cache, "v_cache", torch.bfloat16, (B, Hkv, L_max, d))
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    _need(o_part, "o_part", torch.float32, (B, Hq, n, num_splits, d))
+    _need(lse_part, "lse_part", torch.float32, (B, Hq, n, num_splits))
+    _check(load_library().spec_attn_prefix_ev(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), int(max_seq_len), B, Hq, Hkv, n, d,
+        L_max, float(sm_scale), int(split_len), int(num_splits), _ptr(o_part), _ptr(lse_part),
+        _stream(stream), ctypes.c_void_p(start_event) if isinstance(start_event, int) else start_event,
+        ctypes.c_void_p(stop_event) if isinstance(stop_event, int) else stop_event),
+        "spec_attn_prefix_ev")
 
 
 def spec_attn_block(q, k_blk, v_blk, parent, o_blk, lse_blk, sm_scale=1.0, stream=None):

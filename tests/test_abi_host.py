@@ -37,7 +37,8 @@ def declared_functions():
 
 def test_header_declares_the_four_calls():
     names = declared_functions()
-    for n in ("spec_attn_prefix", "spec_attn_block", "lse_merge", "spec_attn_block_merge",
+    for n in ("spec_attn_prefix", "spec_attn_prefix_ev", "spec_attn_block", "lse_merge",
+              "spec_attn_block_merge",
               "spec_attn_window",
               "rapid_accept", "rapid_accept_ex", "rapid_accept_workspace_size",
               "rv_status_string", "rv_prefix_default_split"):
@@ -91,6 +92,17 @@ def test_prefix_validation(lib):
     assert _prefix(lib, k=MIS) == RV_ERR_ALIGNMENT
     assert _prefix(lib, lse=MIS) == RV_ERR_ALIGNMENT
     assert _prefix(lib, L_max=1 << 24, max_seq_len=1 << 24, d=128, S=1 << 14) == RV_ERR_UNSUPPORTED
+
+
+def test_prefix_ev_validates_like_prefix(lib):
+    base = [P, P, P, P, 4096, 1, 8, 2, 5, 64, 4096, 1.0, 1024, 4, P, P, None]
+    assert lib.spec_attn_prefix_ev(None, *base[1:], None, None) == RV_ERR_NULL
+    bad = list(base)
+    bad[12] = 1000  # split_len not a multiple of the quantum
+    assert lib.spec_attn_prefix_ev(*bad, None, None) == RV_ERR_SHAPE
+    bad = list(base)
+    bad[11] = 0.0
+    assert lib.spec_attn_prefix_ev(*bad, None, None) == RV_ERR_VALUE
 
 
 def _block(lib, parent=None, **kw):

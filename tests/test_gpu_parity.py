@@ -133,6 +133,38 @@ def test_prefix_and_block_partials_match_split_oracle():
             assert np.abs(lse_blk[b, h] - l).max() <= 1e-2
 
 
+def test_prefix_ev_matches_prefix_and_records_the_kernel():
+    """spec_attn_prefix_ev writes the same partials as spec_attn_prefix and
+    its events bracket the kernel (positive elapsed time)."""
+    import ctypes
+    from speculative_decoding_verify_split_amd import rapid_verify as rv
+    ai, split = _make_case(ATTN_CASES[0])
+    announce("spec_attn_prefix_ev")
+    st = VerifyStep(ai, None, split=split)
+    st.attention()
+    torch.cuda.synchronize()
+    ref = (st.o_part.clone(), st.lse_part.clone())
+    st.o_part.zero_()
+    st.lse_part.zero_()
+    hip = ctypes.CDLL("libamdhip64.so")
+    evs = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in evs:
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+    try:
+        rv.spec_attn_prefix_ev(st.q, st.k_cache, st.v_cache, st.seq_lens, st.max_seq_len,
+                               st.split_len, st.num_splits, st.o_part, st.lse_part, evs[0],
+                               evs[1], st.sm_scale)
+        torch.cuda.synchronize()
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), evs[0], evs[1]) == 0
+        announce("  kernel %.2f us" % (ms.value * 1e3))
+        assert ms.value > 0
+    finally:
+        for e in evs:
+            hip.hipEventDestroy(e)
+    assert torch.equal(st.o_part, ref[0]) and torch.equal(st.lse_part, ref[1])
+
+
 def test_seq_lens_are_clamped_on_the_device():
     ai = make_attention(33, 3, 4, 2, 128, 4, [640, 640, 640], L_max=640)
     announce("seq_lens clamp")
