@@ -258,6 +258,25 @@ def test_accept_small(case):
     _check_accept(vi, st, name)
 
 
+@pytest.mark.timeout(300)
+def test_accept_max_vocab():
+    """V = 2^22, the largest vocabulary: 1024 statistics chunks and 4096
+    decide/draw chunks, so the draw's chunk scan runs over 16 blocks."""
+    vi = make_vocab(48, B=2, gamma=2, V=1 << 22, z_sigma=3.0, noise=1.0, T=1.0, eta=0.5)
+    announce("rapid_accept V=2^22 B=2 gamma=2")
+    st = _run_accept(vi, p_hat=False)
+    _check_accept(vi, st, "V=2^22")
+    vi.r = np.zeros_like(vi.r)  # every draft kept: the bonus draw over 2^22 ids
+    st = _run_accept(vi, p_hat=False)
+    _check_accept(vi, st, "V=2^22 all-accept")
+
+
+def test_accept_batch64():
+    vi = make_vocab(49, B=64, gamma=4, V=32000, z_sigma=3.0, noise=1.0, T=0.9, eta=1.0)
+    announce("rapid_accept B=64 gamma=4 V=32000")
+    _check_accept(vi, _run_accept(vi), "B=64")
+
+
 def test_accept_tiny_config():
     vi = config_vocab("tiny")
     announce("rapid_accept tiny config")
