@@ -428,15 +428,19 @@ template <bool VEC>
 __device__ void draw_row(const float* __restrict__ z, const float* __restrict__ y,
                          const float* __restrict__ u, int b, int ts, int gamma, int V,
                          float invT2, float eta2, int cd, const RowLse& rc,
-                         const float* __restrict__ wsum, int32_t* __restrict__ out_tokens) {
+                         float* __restrict__ wsum, int32_t* __restrict__ out_tokens) {
   __shared__ float sh_base;
-  // The chunk weights were published by the other workgroups before their
-  // arrival was counted; read them past the caches.
-  const float* ws = wsum + (size_t)b * cd * 2;
+  // The chunk weights were published by the other workgroups with
+  // device-scope atomic stores before their arrival was counted; read them
+  // with device-scope atomic loads, which do not return a stale copy from
+  // this workgroup's L2.
+  float* ws = wsum + (size_t)b * cd * 2;
   const float u_ts = u[(size_t)b * (gamma + 1) + ts];
   auto chunk_w = [&](int i) {
-    return i < cd ? make_float2(__builtin_nontemporal_load(ws + 2 * i),
-                                __builtin_nontemporal_load(ws + 2 * i + 1))
+    return i < cd ? make_float2(
+                        __hip_atomic_load(ws + 2 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                        __hip_atomic_load(ws + 2 * i + 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT))
                   : make_float2(0.f, 0.f);
   };
 
@@ -584,7 +588,10 @@ __global__ __launch_bounds__(TPB) void decide_kernel(
     if (c == 0) {
       if (ratio_out != nullptr && lane < gamma)
         ratio_out[(size_t)b * gamma + lane] = bad ? __builtin_nanf("") : ratio;
-      if (lane <= gamma) out_tokens[(size_t)b * (gamma + 1) + lane] = (lane < ts) ? x : -1;
+      // Slot ts belongs to the drawing workgroup alone (no two workgroups
+      // write one word: their L2s may write back in either order).
+      if (lane <= gamma && lane != ts)
+        out_tokens[(size_t)b * (gamma + 1) + lane] = (lane < ts) ? x : -1;
       if (lane == 0) n_accept[b] = ts;
     }
   }
@@ -627,17 +634,22 @@ __global__ __launch_bounds__(TPB) void decide_kernel(
   // Publish this chunk's draw weights, then count its arrival.  The
   // workgroup that arrives last draws the token: which workgroup that is
   // does not change what is drawn, and nothing ever waits for another
-  // workgroup.
+  // workgroup.  The weights are the only data another workgroup of this
+  // kernel reads, so they go out as device-scope atomic stores, and waiting
+  // for those stores to complete before the (device-scope) increment orders
+  // them ahead of it: the ordering of a release, without the write-back of
+  // the whole L2 that a release performs for ordinary stores.
   __shared__ uint32_t sh_arrived;
   if (threadIdx.x == 0) {
-    wsum[((size_t)b * cd + c) * 2 + 0] = W.x;
-    wsum[((size_t)b * cd + c) * 2 + 1] = W.y;
-    __threadfence();
-    sh_arrived = atomicAdd(arrivals + b, 1u);
+    float* wc = wsum + ((size_t)b * cd + c) * 2;
+    __hip_atomic_store(wc, W.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(wc + 1, W.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    sh_arrived = __hip_atomic_fetch_add(arrivals + b, 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (sh_arrived != (uint32_t)(cd - 1)) return;  // uniform
-  __threadfence();
   draw_row<VEC>(z, y, u, b, ts, gamma, V, invT2, eta2, cd, rc, wsum, out_tokens);
 }
 

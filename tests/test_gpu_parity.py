@@ -277,6 +277,29 @@ def test_accept_batch64():
     _check_accept(vi, _run_accept(vi), "B=64")
 
 
+def test_draw_slot_survives_repeated_calls():
+    """The drawn token's slot is written by the drawing workgroup alone: 100
+    back-to-back calls at the 8B vocabulary (126 decide workgroups spread
+    over the XCDs) all reproduce the first call's outputs."""
+    vi = config_vocab("llama8b", eta=0.5, B_override=4)
+    announce("rapid_accept x100, B=4, V=128256")
+    st = VerifyStep(None, vi, want_ratio=True)
+    st.accept()
+    torch.cuda.synchronize()
+    ref = (st.n_accept.clone(), st.out_tokens.clone())
+    assert (ref[0] >= 0).all()
+    for i in range(100):
+        st.out_tokens.fill_(-7)
+        st.accept()
+    torch.cuda.synchronize()
+    assert torch.equal(st.n_accept, ref[0]) and torch.equal(st.out_tokens, ref[1])
+    for i in range(20):  # and with each call checked on its own
+        st.out_tokens.fill_(-7)
+        st.accept()
+        torch.cuda.synchronize()
+        assert torch.equal(st.out_tokens, ref[1]), "call %d" % i
+
+
 def test_accept_tiny_config():
     vi = config_vocab("tiny")
     announce("rapid_accept tiny config")
