@@ -108,6 +108,27 @@ def _cpu_baseline(ai, vi, budget_s):
                       (reps, ai.q.shape[1], int(ai.seq_lens.max()), el)}
 
 
+def _copy_context(n_bytes=1 << 31, reps=5):
+    """A plain 2 GiB device-to-device copy_ on the same box, as context for
+    the 8 TB/s peak: (read + write bytes) / time."""
+    import torch
+    src = torch.empty(n_bytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / 1e3 / reps
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_copied": n_bytes, "GBps_read_plus_write": 2 * n_bytes / s / 1e9}
+
+
 def _calibrate_copy(n_bytes, reps):
     """A plain device copy of known size, for scaling HBM counters."""
     import torch
@@ -165,8 +186,7 @@ def run_drafter(args):
         rv.lse_merge(st.o_part, st.lse_part, None, None, st.out, st.lse_out)
         if ev is not None:
             ev[2].record()
-        rv.spec_attn_window(ws.q, ws.k_ring, ws.v_ring, ws.pos, ws.sink, ws.window, ws.out,
-                            ws.lse_out, ws.sm_scale)
+        ws.run()
         if ev is not None:
             ev[3].record()
 
@@ -479,8 +499,12 @@ def main():
                      "algorithmic_bytes_per_launch": kv_bytes},
         "mean_n_accept": float(np.mean(n_acc)),
         "graph_replay": graph,
+        "copy_context": None,
         "cpu_baseline": None,
     }
+    del kvs, logits
+    torch.cuda.empty_cache()
+    line["copy_context"] = _copy_context()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = _cpu_baseline(ai, vi, args.cpu_budget)
     print(json.dumps(line), flush=True)

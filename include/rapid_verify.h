@@ -214,14 +214,19 @@ rv_status spec_attn_block_merge(const void* q, const void* k_blk, const void* v_
  *   sm_scale finite and > 0
  *   out      bf16 [B, Hq, n, d]   (round to nearest even)
  *   lse_out  fp32 [B, Hq, n] or NULL  natural-log sum exp of the scores
+ *   workspace device scratch of spec_attn_window_workspace_size bytes
+ *            (16-byte aligned; no initial contents needed)
  * The row at position P sees positions p <= P with p < sink or
  * p > P - window (the window includes the row itself).  Query head h reads
- * kv head h / (Hq / Hkv).  Supports d in {64, 128}, 1 <= n <= 64.
+ * kv head h / (Hq / Hkv).  Two launches on `stream`: per-segment partials,
+ * then their log-sum-exp merge.  Supports d in {64, 128}, 1 <= n <= 64,
+ * B * n <= 65535.
  */
+size_t spec_attn_window_workspace_size(int B, int Hq, int n, int d, int sink, int window);
 rv_status spec_attn_window(const void* q, const void* k_ring, const void* v_ring,
                            const int32_t* pos, int B, int Hq, int Hkv, int n, int d, int cap,
                            int sink, int window, float sm_scale, void* out, float* lse_out,
-                           void* stream);
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace rapid_accept needs for (B, gamma, V). */
 size_t rapid_accept_workspace_size(int B, int gamma, int V);

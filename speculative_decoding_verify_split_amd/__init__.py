@@ -24,4 +24,5 @@ from .rapid_verify import (  # noqa: F401
     spec_attn_prefix,
     spec_attn_prefix_ev,
     spec_attn_window,
+    spec_attn_window_workspace_size,
 )

@@ -11,15 +11,14 @@
 // otherwise.  The window part of the key list is consecutive positions, so
 // its slots are consecutive modulo the ring and each row needs one modulo.
 //
-// At most sink + window keys per row (516 for the drafter) and G*n rows per
-// kv head: no contraction worth a matrix-core tile, so this runs on the
-// vector ALU in fp32.  One workgroup per row; its key list is cut into
-// 64-key chunks dealt to the four waves in turn.  In a chunk, lane j scores
-// key j (its K row against the query held in registers) while the lane's
-// d/64 output columns of all 64 V rows are requested at the same time (the
-// slots are known before any score); online softmax per wave, then a
-// log-sum-exp merge of the four waves through LDS in wave order, so the
-// result is bit-deterministic.
+// Split-K over the key list, then the log-sum-exp merge: one workgroup per
+// (sequence, kv head, row, 64-key segment of the row's list) stages the
+// segment's K and V once in LDS with coalesced loads, and its waves score
+// the G query heads of that kv head against it (vector ALU in fp32: with 64
+// keys and G rows there is no contraction worth a matrix-core tile), each
+// writing a normalised partial (O, LSE) per (row, segment); lse_merge
+// without a block part then merges the segments.  Fixed orders throughout,
+// so results are bit-deterministic.
 
 #include <type_traits>
 
@@ -29,162 +28,149 @@
 namespace rv {
 namespace {
 
-constexpr int WNW = 8;  // waves per workgroup
+constexpr int WSEG = 64;  // keys per segment
 
 __device__ __forceinline__ float bf16_at(uint32_t w, int e) {
   return __uint_as_float(e == 0 ? (w << 16) : (w & 0xffff0000u));
 }
 
+// grid (S, Hkv, B * n).  o_part [B, Hq, n, S, d], lse_part [B, Hq, n, S].
 template <int D>
-__global__ __launch_bounds__(WNW * 64) void window_kernel(
+__global__ __launch_bounds__(256) void window_part_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kr,
     const uint16_t* __restrict__ vr, const int32_t* __restrict__ pos, int Hq, int G, int n,
-    int cap, int sink, int window, float scale_log2, uint16_t* __restrict__ out,
-    float* __restrict__ lse_out) {
+    int cap, int sink, int window, float scale_log2, int S, float* __restrict__ o_part,
+    float* __restrict__ lse_part) {
   constexpr int PER = D / 64;  // output columns per lane
   constexpr int KQ = D / 8;    // 16-byte pieces per row
-  const int row = blockIdx.x;  // (b * Hq + h) * n + i
-  const int i = row % n;
-  const int bh = row / n;
-  const int b = bh / Hq;
-  const int h = bh - b * Hq;
+  constexpr int KROW = D * 2 + 16;  // padded K row in LDS: lane j reading row j hits distinct banks
+  constexpr int VROWB = D * 2;
+  __shared__ __attribute__((aligned(16))) unsigned char kt[WSEG * KROW];
+  __shared__ __attribute__((aligned(16))) unsigned char vt[WSEG * VROWB];
+  const int s = blockIdx.x, kvh = blockIdx.y;
+  const int b = blockIdx.z / n, i = blockIdx.z - (blockIdx.z / n) * n;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int Hkv = Hq / G;
 
   int P0 = pos[b];
   P0 = P0 < 0 ? 0 : (P0 > kMaxWindowPos ? kMaxWindowPos : P0);
   const int P = P0 + i;
-  const int ns = min(sink, P + 1);                   // sink keys
-  const int lo = max(sink, P - window + 1);          // first window position
-  const int K = ns + max(0, P - lo + 1);             // keys of this row (>= 1)
-  const int R = cap - sink;                          // circular slots
+  const int ns = min(sink, P + 1);           // sink keys
+  const int lo = max(sink, P - window + 1);  // first window position
+  const int K = ns + max(0, P - lo + 1);     // keys of this row (>= 1)
+  const int R = cap - sink;                  // circular slots
   const int base = (lo >= sink) ? (lo - sink) % R : 0;
+  // Slot of key idx of the row's list; indices past the list are clamped to
+  // its last key (a written slot), so every load is in bounds and finite.
   auto slot_of = [&](int idx) {
-    if (idx < ns) return idx;
+    idx = min(idx, K - 1);
     int u = base + (idx - ns);  // < 2R: idx - ns < window <= R
-    if (u >= R) u -= R;
-    return sink + u;
+    u -= (u >= R) ? R : 0;
+    return (idx < ns) ? idx : sink + u;
   };
-  const size_t kv0 = ((size_t)b * (Hq / G) + h / G) * (size_t)cap * D;
-  const uint16_t* kh = kr + kv0;
-  const uint16_t* vh = vr + kv0 + lane * PER;
+  const int c0 = s * WSEG;
+  const int nk = min(WSEG, K - c0);  // keys of this segment (<= 0: empty)
 
-  i32x4 qv[KQ];
-  {
-    const i32x4* qp = reinterpret_cast<const i32x4*>(q + (size_t)row * D);
-#pragma unroll
-    for (int c = 0; c < KQ; ++c) qv[c] = qp[c];
-  }
-  typedef typename std::conditional<PER == 2, uint32_t, uint16_t>::type vcol_t;
-
-  float m = -INFINITY, l = 0.f, o[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) o[e] = 0.f;
-  const int nchunks = (K + 63) / 64;
-  for (int c = wave; c < nchunks; c += WNW) {
-    const int c0 = c * 64;
-    const int idx = c0 + lane;
-    const bool valid = idx < K;
-    i32x4 kk[KQ];
-    if (valid) {
-      const i32x4* kp = reinterpret_cast<const i32x4*>(kh + (size_t)slot_of(idx) * D);
-#pragma unroll
-      for (int cc = 0; cc < KQ; ++cc) kk[cc] = kp[cc];
+  if (nk > 0) {
+    const size_t kv0 = ((size_t)b * Hkv + kvh) * (size_t)cap * D;
+    for (int pc = threadIdx.x; pc < WSEG * KQ; pc += 256) {
+      const int r = pc / KQ, col = pc - r * KQ;
+      const size_t off = kv0 + (size_t)slot_of(c0 + r) * D + col * 8;
+      const i32x4 kx = *reinterpret_cast<const i32x4*>(kr + off);
+      const i32x4 vx = *reinterpret_cast<const i32x4*>(vr + off);
+      *reinterpret_cast<i32x4*>(kt + r * KROW + col * 16) = kx;
+      *reinterpret_cast<i32x4*>(vt + r * VROWB + col * 16) = vx;
     }
-    vcol_t vv[64];
-#pragma unroll
-    for (int j = 0; j < 64; ++j)
-      vv[j] = (c0 + j < K) ? *reinterpret_cast<const vcol_t*>(vh + (size_t)slot_of(c0 + j) * D)
-                           : vcol_t(0);
-    float s = -INFINITY;
-    if (valid) {
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int cc = 0; cc < KQ; ++cc) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t a = (uint32_t)qv[cc][e], bb = (uint32_t)kk[cc][e];
-          acc[e] = fmaf(bf16_at(a, 0), bf16_at(bb, 0), acc[e]);
-          acc[e] = fmaf(bf16_at(a, 1), bf16_at(bb, 1), acc[e]);
-        }
-      }
-      s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * scale_log2;
-    }
-    const float mn = fmaxf(m, wave_max(s));  // finite: key c0 is valid
-    const float alpha = (m == -INFINITY) ? 0.f : exp2_hw(m - mn);
-    const float p = valid ? exp2_hw(s - mn) : 0.f;
-    l = fmaf(l, alpha, wave_sum(p));
-#pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] *= alpha;
-#pragma unroll
-    for (int j = 0; j < 64; ++j) {
-      const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), j));
-#pragma unroll
-      for (int e = 0; e < PER; ++e) {
-        const float v = PER == 2 ? bf16_at((uint32_t)vv[j], e) : bf16_at((uint32_t)vv[j], 0);
-        o[e] = fmaf(pj, v, o[e]);
-      }
-    }
-    m = mn;
   }
-
-  __shared__ float sm[WNW], sl[WNW];
-  __shared__ float so[WNW][D];
-  if (lane == 0) {
-    sm[wave] = m;
-    sl[wave] = l;
-  }
-#pragma unroll
-  for (int e = 0; e < PER; ++e) so[wave][lane * PER + e] = o[e];
   __syncthreads();
-  if (wave != 0) return;
-  float M = -INFINITY;
+
+  for (int g = wave; g < G; g += 4) {
+    const int h = kvh * G + g;
+    const size_t row = ((size_t)b * Hq + h) * n + i;
+    float* op = o_part + (row * S + s) * D + lane * PER;
+    if (nk <= 0) {  // uniform: an empty segment
 #pragma unroll
-  for (int w = 0; w < WNW; ++w) M = fmaxf(M, sm[w]);
-  float a[WNW], L = 0.f;
+      for (int e = 0; e < PER; ++e) op[e] = 0.f;
+      if (lane == 0) lse_part[row * S + s] = -INFINITY;
+      continue;
+    }
+    const i32x4* qp = reinterpret_cast<const i32x4*>(q + row * D);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int w = 0; w < WNW; ++w) {
-    a[w] = (sm[w] == -INFINITY) ? 0.f : exp2_hw(sm[w] - M);
-    L = fmaf(a[w], sl[w], L);
+    for (int cc = 0; cc < KQ; ++cc) {
+      const i32x4 qq = qp[cc];
+      const i32x4 kk = *reinterpret_cast<const i32x4*>(kt + lane * KROW + cc * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] = fmaf(bf16_at((uint32_t)qq[e], 0), bf16_at((uint32_t)kk[e], 0), acc[e]);
+        acc[e] = fmaf(bf16_at((uint32_t)qq[e], 1), bf16_at((uint32_t)kk[e], 1), acc[e]);
+      }
+    }
+    const float sc = lane < nk ? ((acc[0] + acc[1]) + (acc[2] + acc[3])) * scale_log2 : -INFINITY;
+    const float m = wave_max(sc);  // finite: key c0 is in the list
+    const float p = lane < nk ? exp2_hw(sc - m) : 0.f;
+    const float l = wave_sum(p);
+    float o[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < WSEG; ++j) {
+      const float pj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(p), j));
+      if (PER == 2) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(vt + j * VROWB + lane * 4);
+        o[0] = fmaf(pj, bf16_at(w, 0), o[0]);
+        o[PER - 1] = fmaf(pj, bf16_at(w, 1), o[PER - 1]);
+      } else {
+        const uint32_t w = *reinterpret_cast<const uint16_t*>(vt + j * VROWB + lane * 2);
+        o[0] = fmaf(pj, bf16_at(w, 0), o[0]);
+      }
+    }
+    const float inv = 1.0f / l;  // l >= 1: the maximum contributes 2^0
+#pragma unroll
+    for (int e = 0; e < PER; ++e) op[e] = o[e] * inv;
+    if (lane == 0) lse_part[row * S + s] = (m + log2_hw(l)) * kLn2;
   }
-  const float inv = 1.0f / L;  // L >= 1: the wave holding the maximum contributes 2^0
-  uint16_t* dst = out + (size_t)row * D + lane * PER;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int col = lane * PER + e;
-    float acc = 0.f;
-#pragma unroll
-    for (int w = 0; w < WNW; ++w) acc = fmaf(a[w], so[w][col], acc);
-    dst[e] = f32_to_bf16_bits(acc * inv);
-  }
-  if (lse_out != nullptr && lane == 0) lse_out[row] = (M + log2_hw(L)) * kLn2;
 }
 
 }  // namespace
 }  // namespace rv
 
+extern "C" size_t spec_attn_window_workspace_size(int B, int Hq, int n, int d, int sink,
+                                                  int window) {
+  if (B < 1 || Hq < 1 || n < 1 || (d != 64 && d != 128) || sink < 0 || window < 1) return 0;
+  const size_t S = rv::window_segments(sink, window);
+  const size_t rows = (size_t)B * Hq * n;
+  return rv::window_workspace_words(rows, S, d) * 4;
+}
+
 extern "C" rv_status spec_attn_window(const void* q, const void* k_ring, const void* v_ring,
                                       const int32_t* pos, int B, int Hq, int Hkv, int n, int d,
                                       int cap, int sink, int window, float sm_scale, void* out,
-                                      float* lse_out, void* stream) {
+                                      float* lse_out, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
   rv_status st = rv::check_window(q, k_ring, v_ring, pos, B, Hq, Hkv, n, d, cap, sink, window,
-                                  sm_scale, out);
+                                  sm_scale, out, workspace, workspace_bytes);
   if (st != RV_OK) return st;
   const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  dim3 grid((unsigned)(B * Hq * n));
+  const int S = rv::window_segments(sink, window);
+  const size_t rows = (size_t)B * Hq * n;
+  float* o_part = static_cast<float*>(workspace);
+  float* lse_part = o_part + rv::window_o_words(rows, S, d);
+  dim3 grid((unsigned)S, (unsigned)Hkv, (unsigned)(B * n));
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(k_ring);
   const uint16_t* vv = static_cast<const uint16_t*>(v_ring);
-  uint16_t* o16 = static_cast<uint16_t*>(out);
   if (d == 64)
-    hipLaunchKernelGGL((rv::window_kernel<64>), grid, dim3(rv::WNW * 64), 0, s, qq, kk, vv, pos,
-                       Hq, Hq / Hkv, n, cap, sink, window, scale_log2, o16, lse_out);
+    hipLaunchKernelGGL((rv::window_part_kernel<64>), grid, dim3(256), 0, s, qq, kk, vv, pos, Hq,
+                       Hq / Hkv, n, cap, sink, window, scale_log2, S, o_part, lse_part);
   else
-    hipLaunchKernelGGL((rv::window_kernel<128>), grid, dim3(rv::WNW * 64), 0, s, qq, kk, vv, pos,
-                       Hq, Hq / Hkv, n, cap, sink, window, scale_log2, o16, lse_out);
+    hipLaunchKernelGGL((rv::window_part_kernel<128>), grid, dim3(256), 0, s, qq, kk, vv, pos, Hq,
+                       Hq / Hkv, n, cap, sink, window, scale_log2, S, o_part, lse_part);
   if (hipGetLastError() != hipSuccess) {
     (void)hipGetLastError();
     return RV_ERR_HIP;
   }
-  return RV_OK;
+  // the segments' partials merge exactly like history splits, with no block
+  return lse_merge(o_part, lse_part, S, nullptr, nullptr, B, Hq, n, d, out, lse_out, stream);
 }

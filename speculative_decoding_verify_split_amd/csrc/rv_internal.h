@@ -47,9 +47,20 @@ rv_status check_block_merge(const void* q, const void* k_blk, const void* v_blk,
 // it are clamped), so that positions of a block's rows stay in int range.
 constexpr int kMaxWindowPos = 1 << 30;
 
+// spec_attn_window's key list is cut into 64-key segments; its workspace is
+// the segments' partials, o [B*Hq*n][S][d] then lse [B*Hq*n][S] (fp32).
+inline int window_segments(int sink, int window) { return (sink + window + 63) / 64; }
+inline size_t window_o_words(size_t rows, size_t S, int d) {
+  return (rows * S * (size_t)d + 63) & ~(size_t)63;
+}
+inline size_t window_workspace_words(size_t rows, size_t S, int d) {
+  return window_o_words(rows, S, d) + ((rows * S + 63) & ~(size_t)63);
+}
+
 rv_status check_window(const void* q, const void* k_ring, const void* v_ring,
                        const int32_t* pos, int B, int Hq, int Hkv, int n, int d, int cap,
-                       int sink, int window, float sm_scale, const void* out);
+                       int sink, int window, float sm_scale, const void* out,
+                       const void* workspace, size_t workspace_bytes);
 
 rv_status check_merge(const float* o_part, const float* lse_part, int S, const float* o_blk,
                       const float* lse_blk, int B, int Hq, int n, int d, const void* out);

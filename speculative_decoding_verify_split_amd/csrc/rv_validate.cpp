@@ -107,8 +107,9 @@ rv_status check_block_merge(const void* q, const void* k_blk, const void* v_blk,
 
 rv_status check_window(const void* q, const void* k_ring, const void* v_ring,
                        const int32_t* pos, int B, int Hq, int Hkv, int n, int d, int cap,
-                       int sink, int window, float sm_scale, const void* out) {
-  if (!q || !k_ring || !v_ring || !pos || !out) return RV_ERR_NULL;
+                       int sink, int window, float sm_scale, const void* out,
+                       const void* workspace, size_t workspace_bytes) {
+  if (!q || !k_ring || !v_ring || !pos || !out || !workspace) return RV_ERR_NULL;
   rv_status st = check_heads(B, Hq, Hkv, n, d);
   if (st != RV_OK) return st;
   if (window < 1 || sink < 0 || cap < 1) return RV_ERR_SHAPE;
@@ -118,6 +119,11 @@ rv_status check_window(const void* q, const void* k_ring, const void* v_ring,
   if (!aligned16(q) || !aligned16(k_ring) || !aligned16(v_ring) || !aligned16(out))
     return RV_ERR_ALIGNMENT;
   if ((int64_t)B * Hq * n > 0x7fffffff / 4) return RV_ERR_UNSUPPORTED;  // one row per workgroup
+  if ((int64_t)B * n > 65535 || Hkv > 65535) return RV_ERR_UNSUPPORTED;  // grid dimensions
+  if (!aligned16(workspace)) return RV_ERR_ALIGNMENT;
+  const size_t rows = (size_t)B * Hq * n;
+  if (workspace_bytes < window_workspace_words(rows, window_segments(sink, window), d) * 4)
+    return RV_ERR_WORKSPACE;
   return RV_OK;
 }
 

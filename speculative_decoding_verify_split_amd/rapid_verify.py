@@ -56,8 +56,10 @@ def load_library():
     lib.spec_attn_block_merge.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                           f32, vp, vp, vp]
     lib.spec_attn_block_merge.restype = i32
+    lib.spec_attn_window_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.spec_attn_window_workspace_size.restype = sz
     lib.spec_attn_window.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32,
-                                     vp, vp, vp]
+                                     vp, vp, vp, sz, vp]
     lib.spec_attn_window.restype = i32
     lib.rapid_accept_workspace_size.argtypes = [i32, i32, i32]
     lib.rapid_accept_workspace_size.restype = sz
@@ -234,10 +236,15 @@ def spec_attn_block_merge(q, k_blk, v_blk, parent, o_part, lse_part, out, lse_ou
         _ptr(lse_out), _stream(stream)), "spec_attn_block_merge")
 
 
-def spec_attn_window(q, k_ring, v_ring, pos, sink, window, out, lse_out=None, sm_scale=1.0,
-                     stream=None):
+def spec_attn_window_workspace_size(B, Hq, n, d, sink, window):
+    return int(load_library().spec_attn_window_workspace_size(B, Hq, n, d, sink, window))
+
+
+def spec_attn_window(q, k_ring, v_ring, pos, sink, window, out, workspace, lse_out=None,
+                     sm_scale=1.0, stream=None):
     """Drafter self-attention.  q bf16 [B,Hq,n,d]; k_ring/v_ring bf16
-    [B,Hkv,cap,d]; pos int32 [B]; out bf16 [B,Hq,n,d]; lse_out fp32 [B,Hq,n]."""
+    [B,Hkv,cap,d]; pos int32 [B]; out bf16 [B,Hq,n,d]; lse_out fp32 [B,Hq,n];
+    workspace uint8 of spec_attn_window_workspace_size bytes."""
     import torch
     _need(q, "q", torch.bfloat16)
     B, Hq, n, d = q.shape
@@ -247,12 +254,13 @@ def spec_attn_window(q, k_ring, v_ring, pos, sink, window, out, lse_out=None, sm
     _need(v_ring, "v_ring", torch.bfloat16, (B, Hkv, cap, d))
     _need(pos, "pos", torch.int32, (B,))
     _need(out, "out", torch.bfloat16, (B, Hq, n, d))
+    _need(workspace, "workspace", torch.uint8)
     if lse_out is not None:
         _need(lse_out, "lse_out", torch.float32, (B, Hq, n))
     _check(load_library().spec_attn_window(
         _ptr(q), _ptr(k_ring), _ptr(v_ring), _ptr(pos), B, Hq, Hkv, n, d, cap, int(sink),
-        int(window), float(sm_scale), _ptr(out), _ptr(lse_out), _stream(stream)),
-        "spec_attn_window")
+        int(window), float(sm_scale), _ptr(out), _ptr(lse_out), _ptr(workspace),
+        workspace.numel(), _stream(stream)), "spec_attn_window")
 
 
 def rapid_accept_workspace_size(B, gamma, V):

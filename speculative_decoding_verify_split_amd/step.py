@@ -133,10 +133,12 @@ class WindowStep:
         self.sink, self.window, self.sm_scale = int(win.sink), int(win.window), float(win.sm_scale)
         self.out = torch.empty((B, Hq, n, d), dtype=torch.bfloat16, device=device)
         self.lse_out = torch.empty((B, Hq, n), dtype=torch.float32, device=device)
+        ws = rv.spec_attn_window_workspace_size(B, Hq, n, d, self.sink, self.window)
+        self.workspace = torch.empty((ws,), dtype=torch.uint8, device=device)
 
     def run(self, stream=None):
         rv.spec_attn_window(self.q, self.k_ring, self.v_ring, self.pos, self.sink, self.window,
-                            self.out, self.lse_out, self.sm_scale, stream)
+                            self.out, self.workspace, self.lse_out, self.sm_scale, stream)
 
 
 class ModelStep:

@@ -39,7 +39,7 @@ def test_header_declares_the_four_calls():
     names = declared_functions()
     for n in ("spec_attn_prefix", "spec_attn_prefix_ev", "spec_attn_block", "lse_merge",
               "spec_attn_block_merge",
-              "spec_attn_window",
+              "spec_attn_window", "spec_attn_window_workspace_size",
               "rapid_accept", "rapid_accept_ex", "rapid_accept_workspace_size",
               "rv_status_string", "rv_prefix_default_split"):
         assert n in names
@@ -181,11 +181,11 @@ def test_block_merge_validation(lib):
 
 def _window(lib, **kw):
     a = dict(q=P, k=P, v=P, pos=P, B=1, Hq=8, Hkv=2, n=1, d=128, cap=516, sink=4, window=512,
-             scale=1.0, out=P, lo=P)
+             scale=1.0, out=P, lo=P, ws=P, wsb=1 << 20)
     a.update(kw)
     return lib.spec_attn_window(a["q"], a["k"], a["v"], a["pos"], a["B"], a["Hq"], a["Hkv"],
                                 a["n"], a["d"], a["cap"], a["sink"], a["window"], a["scale"],
-                                a["out"], a["lo"], None)
+                                a["out"], a["lo"], a["ws"], a["wsb"], None)
 
 
 def test_window_validation(lib):
@@ -203,6 +203,12 @@ def test_window_validation(lib):
     assert _window(lib, scale=float("nan")) == RV_ERR_VALUE
     assert _window(lib, k=MIS) == RV_ERR_ALIGNMENT
     assert _window(lib, out=MIS) == RV_ERR_ALIGNMENT
+    assert _window(lib, ws=None) == RV_ERR_NULL
+    assert _window(lib, ws=MIS) == RV_ERR_ALIGNMENT
+    need = rv.spec_attn_window_workspace_size(1, 8, 1, 128, 4, 512)
+    assert need == (((8 * 9 * 128 + 63) // 64) * 64 + ((8 * 9 + 63) // 64) * 64) * 4  # 9 segments
+    assert _window(lib, wsb=need - 1) == RV_ERR_WORKSPACE
+    assert rv.spec_attn_window_workspace_size(1, 8, 1, 96, 4, 512) == 0
 
 
 def _accept(lib, **kw):
