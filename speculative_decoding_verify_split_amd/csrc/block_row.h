@@ -31,12 +31,15 @@ __device__ __forceinline__ void block_row_attention(const uint16_t* __restrict__
                                                     float (&o)[D / 64], float& lse2) {
   constexpr int PER = D / 64;
   const int lane = threadIdx.x & 63;
-  // V columns of this lane for the first 8 keys, requested up front.
+  // V columns of this lane for the first kPre keys (a chain of up to 15
+  // drafts), requested up front with the K rows, so the row costs one round
+  // trip.
+  constexpr int kPre = 16;
   const uint16_t* vcol = vh + lane * PER;
   typedef uint16_t u16xP __attribute__((ext_vector_type(PER)));
-  u16xP vpre[8];
+  u16xP vpre[kPre];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int j = 0; j < kPre; ++j)
     vpre[j] = (j < n) ? *reinterpret_cast<const u16xP*>(vcol + (size_t)j * D) : u16xP{};
 
   float s = -INFINITY;
@@ -64,13 +67,13 @@ __device__ __forceinline__ void block_row_attention(const uint16_t* __restrict__
 #pragma unroll
   for (int e = 0; e < PER; ++e) o[e] = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < kPre; ++j) {
     const float pj = __shfl(p, j < n ? j : 0, 64);
 #pragma unroll
     for (int e = 0; e < PER; ++e)
       o[e] = fmaf(j < n ? pj : 0.f, __uint_as_float((uint32_t)vpre[j][e] << 16), o[e]);
   }
-  for (int j0 = 8; j0 < n; j0 += 8) {
+  for (int j0 = kPre; j0 < n; j0 += 8) {
     u16xP vv[8];
     float pj[8];
 #pragma unroll
