@@ -175,27 +175,39 @@ def run_drafter(args):
     kvs = [(st.k_cache, st.v_cache)] + [(st.k_cache.clone(), st.v_cache.clone())
                                         for _ in range(R - 1)]
 
-    def step(i, ev=None):
-        kc, vc = kvs[i % R]
-        if ev is not None:
-            ev[0].record()
-        rv.spec_attn_prefix(st.q, kc, vc, st.seq_lens, st.max_seq_len, st.split_len,
-                            st.num_splits, st.o_part, st.lse_part, st.sm_scale)
-        if ev is not None:
-            ev[1].record()
-        rv.lse_merge(st.o_part, st.lse_part, None, None, st.out, st.lse_out)
-        if ev is not None:
-            ev[2].record()
-        ws.run()
-        if ev is not None:
-            ev[3].record()
-
     K = args.steps
-    evs, elapsed = _timed_loop(step, K, args.warmup)
-    prefix_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    merge_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    win_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    step_ms = [e[0].elapsed_time(e[3]) for e in evs]
+    hev = _HipEvents(4 * K)  # history kernel's own dispatch, then after merge and window
+    sid = torch.cuda.current_stream().cuda_stream
+
+    def step(i, timed=False):
+        kc, vc = kvs[i % R]
+        if timed:
+            rv.spec_attn_prefix_ev(st.q, kc, vc, st.seq_lens, st.max_seq_len, st.split_len,
+                                   st.num_splits, st.o_part, st.lse_part, hev.ev[4 * i],
+                                   hev.ev[4 * i + 1], st.sm_scale)
+        else:
+            rv.spec_attn_prefix(st.q, kc, vc, st.seq_lens, st.max_seq_len, st.split_len,
+                                st.num_splits, st.o_part, st.lse_part, st.sm_scale)
+        rv.lse_merge(st.o_part, st.lse_part, None, None, st.out, st.lse_out)
+        if timed:
+            hev.record(4 * i + 2, sid)
+        ws.run()
+        if timed:
+            hev.record(4 * i + 3, sid)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, timed=True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prefix_ms = [hev.elapsed_ms(4 * i, 4 * i + 1) for i in range(K)]
+    merge_ms = [hev.elapsed_ms(4 * i + 1, 4 * i + 2) for i in range(K)]
+    win_ms = [hev.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(K)]
+    step_ms = [hev.elapsed_ms(4 * i, 4 * i + 3) for i in range(K)]
+    hev.close()
     L = int(np.max(cross.seq_lens))
     kv_bytes = int(2 * st.Hkv * st.d * 2 * int(np.sum(cross.seq_lens)))
     prefix_s = float(np.mean(prefix_ms)) / 1e3

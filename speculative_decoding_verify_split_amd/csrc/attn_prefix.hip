@@ -25,9 +25,11 @@
 //   * V is staged per wave in LDS in its natural [key][d] layout (row pitch
 //     2d + 32 bytes) and read back transposed for the A operand of
 //     O^T += V^T P^T with ds_read_b64_tr_b16, two reads per 16 columns.
-// The four waves park their (max, sum, O) states in per-wave LDS slots and,
-// after one barrier, all threads merge them and write one normalised partial
-// (O, LSE) per row.
+// The four waves park their (max, sum, O) states in per-wave LDS slots; one
+// thread per row turns the four (max, sum) pairs into the row's LSE and wave
+// weights, and then all threads form and write one normalised partial
+// (O, LSE) per row, with non-temporal stores (the merge reads it once, as a
+// rule from another XCD).
 
 #include <hip/hip_ext.h>
 
@@ -378,7 +380,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
       for (int w = 0; w < NW; ++w)
         o += m_lds[w][row] * *reinterpret_cast<const f32x4*>(obuf + (w * MT * 16 + row) * OROW +
                                                              c4 * 4);
-      *reinterpret_cast<f32x4*>(o_part + (out_row(row) * S + s) * D + c4 * 4) = o;
+      __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(o_part + (out_row(row) * S + s) * D +
+                                                          c4 * 4));
     }
   }
 }
