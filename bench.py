@@ -81,6 +81,27 @@ def _traffic_per_launch():
     return rec.get("hbm_bytes_per_launch")
 
 
+def _host_info():
+    """The host the oracle ran on: CPU model, visible cores, affinity, BLAS threads."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [{"api": i.get("internal_api"), "threads": i.get("num_threads")}
+                for i in threadpool_info()]
+    except Exception:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0)), "blas": blas}
+
+
 def _cpu_baseline(ai, vi, budget_s):
     """Time the fp64 oracle on the host: full unsplit attention over every
     head plus the step-by-step acceptance, repeated within the budget."""
@@ -105,7 +126,8 @@ def _cpu_baseline(ai, vi, budget_s):
     return {"value": reps / el, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
             "sample": "%d full verify step(s) of the same workload (all %d query heads over "
                       "%d history tokens + vocabulary pass), %.1f s" %
-                      (reps, ai.q.shape[1], int(ai.seq_lens.max()), el)}
+                      (reps, ai.q.shape[1], int(ai.seq_lens.max()), el),
+            "host": _host_info()}
 
 
 def _copy_context(n_bytes=1 << 31, reps=5):
