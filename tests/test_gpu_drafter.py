@@ -36,8 +36,12 @@ WINDOW_CASES = [
     ("block-n5-wrap", 63, 2, 8, 2, 128, 5, [1000, 517], 520, 4, 512),
     ("no-sink-d64", 64, 2, 4, 1, 64, 3, [77, 5000], 66, 0, 64),
     ("small-window-many-rows", 65, 1, 16, 4, 128, 16, [300], 40, 2, 23),
-    ("window-1", 66, 1, 4, 2, 64, 2, [9, 0][:1], 6, 4, 1),
+    ("window-1", 66, 1, 4, 2, 64, 2, [9], 6, 4, 1),
     ("keys-not-multiple-of-64", 67, 2, 4, 2, 128, 1, [130, 70], 134, 4, 130),
+    # query heads per kv head other than 4: the waves loop over the G rows
+    ("g7-two-rows-per-wave", 70, 1, 28, 4, 128, 1, [100000], 516, 4, 512),
+    ("g1-mha-d64", 71, 2, 4, 4, 64, 2, [600, 50], 517, 4, 512),
+    ("g8-block-n3", 72, 1, 16, 2, 128, 3, [9999], 518, 4, 512),
 ]
 
 
