@@ -95,11 +95,15 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
   constexpr int KS = Gm::KS, NB = Gm::NB, VCH = Gm::VCH, VROW = Gm::VROW, OROW = Gm::OROW;
   constexpr int VBYTES = NW * Gm::VTILE;
   constexpr int OBYTES = NW * MT * 16 * OROW * 4;  // one merge slot per wave
-  constexpr int SMEM = VBYTES > OBYTES ? VBYTES : OBYTES;
   // The widest shape keeps its query fragments in LDS to stay within 512
   // registers per lane; the others keep them in registers.
   constexpr bool kQLds = (D == 128 && MT == 4);
   constexpr int QLDS_BYTES = kQLds ? MT * KS * 64 * 16 : 16;
+  // Merge slots get LDS of their own where it fits next to the V tiles, so a
+  // wave parks its state as soon as its own stream ends; otherwise they
+  // reuse the V tiles' LDS after a barrier.
+  constexpr bool kOwnSlots = VBYTES + OBYTES + QLDS_BYTES <= 150 * 1024;
+  constexpr int SMEM = kOwnSlots ? VBYTES + OBYTES : (VBYTES > OBYTES ? VBYTES : OBYTES);
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   __shared__ __attribute__((aligned(16))) bf16x8 q_lds[QLDS_BYTES / 16];
   __shared__ float m_lds[NW][MT * 16];
@@ -322,8 +326,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
   // (max, sum) pairs into the row's LSE and per-wave weights
   // 2^(m_w - M) / l; after a second barrier every thread forms its share of
   // the normalised partial with all of its LDS reads in one unrolled batch.
-  __syncthreads();  // V tiles are dead; the buffer becomes the merge slots
-  float* obuf = reinterpret_cast<float*>(smem);
+  if constexpr (!kOwnSlots) __syncthreads();  // V tiles dead: their LDS becomes the slots
+  float* obuf = reinterpret_cast<float*>(smem + (kOwnSlots ? VBYTES : 0));
   {
     float* slot = obuf + wave * (MT * 16 * OROW);
 #pragma unroll
