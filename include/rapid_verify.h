@@ -10,10 +10,18 @@
  *    LongSpec summary (gist.science, "LongSpec", section 2.3 "Fast Tree
  *    Attention"), it is computed in two parts and merged:
  *      spec_attn_prefix  -- unmasked attention over the history cache, split
- *                           along the sequence into partial results (O, LSE);
+ *                           along the sequence into partial results (O, LSE)
+ *                           (spec_attn_prefix_ev also records timing events
+ *                           on its kernel);
  *      spec_attn_block   -- attention among the draft rows under the causal
  *                           or tree mask;
- *      lse_merge         -- log-sum-exp merge of all partials.
+ *      lse_merge         -- log-sum-exp merge of all partials;
+ *      spec_attn_block_merge -- the last two in one launch.
+ *    The LongSpec drafter's own attention (same summary, sections 2.1-2.2)
+ *    uses spec_attn_prefix at n = 1 with lse_merge and no block for its
+ *    cross-attention over the target's cache, and
+ *      spec_attn_window  -- sliding-window self-attention with anchor tokens
+ *                           over the drafter's constant-size ring cache.
  *
  * 2. RAPID's acceptance over the vocabulary (RAPID blog post,
  *    leeon-k.github.io, sections 2.1, 2.3, 2.4; abeam.tech RAPID article,
@@ -24,7 +32,9 @@
  *                           at the first rejection a token is drawn from
  *                           norm(max(p_hat - q, 0)) by inverse CDF with the
  *                           caller's uniform; if every draft is kept, a bonus
- *                           token is drawn from the last row's p.
+ *                           token is drawn from the last row's p;
+ *      rapid_accept_ex   -- the same with section 2.4's tail-preserving rule
+ *                           and/or its printed residual as options.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -44,7 +54,11 @@
  *   to [0, L_max]; a draft id outside [0, V) makes rapid_accept report
  *   n_accept = -1 for that sequence; non-finite logits give unspecified
  *   tokens but never an out-of-bounds access.
- * - Results are bit-deterministic: no atomics, fixed reduction orders.
+ * - Results are bit-deterministic: every reduction has a fixed order; the
+ *   one atomic (rapid_accept's per-sequence arrival counter) only decides
+ *   which workgroup performs the draw, not what is drawn.
+ * - Workspaces (rapid_accept, spec_attn_window) are caller-owned device
+ *   scratch; they need no initial contents and hold nothing between calls.
  *
  * Notation: B batch, Hq query heads, Hkv kv heads (Hq % Hkv == 0, query head
  * h reads kv head h / (Hq/Hkv)), n block rows (gamma+1 for a chain, the node
