@@ -137,7 +137,9 @@ __global__ __launch_bounds__(256) void window_part_kernel(
 
 extern "C" size_t spec_attn_window_workspace_size(int B, int Hq, int n, int d, int sink,
                                                   int window) {
-  if (B < 1 || Hq < 1 || n < 1 || (d != 64 && d != 128) || sink < 0 || window < 1) return 0;
+  if (B < 1 || Hq < 1 || n < 1 || (d != 64 && d != 128) || sink < 0 || window < 1 ||
+      sink > rv::kMaxWindowKeys || window > rv::kMaxWindowKeys)
+    return 0;
   const size_t S = rv::window_segments(sink, window);
   const size_t rows = (size_t)B * Hq * n;
   return rv::window_workspace_words(rows, S, d) * 4;

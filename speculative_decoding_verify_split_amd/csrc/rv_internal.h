@@ -47,9 +47,15 @@ rv_status check_block_merge(const void* q, const void* k_blk, const void* v_blk,
 // it are clamped), so that positions of a block's rows stay in int range.
 constexpr int kMaxWindowPos = 1 << 30;
 
+// Largest window or sink spec_attn_window accepts (keeps key counts and
+// segment counts far from int overflow; a drafter's window is ~10^3).
+constexpr int kMaxWindowKeys = 1 << 24;
+
 // spec_attn_window's key list is cut into 64-key segments; its workspace is
 // the segments' partials, o [B*Hq*n][S][d] then lse [B*Hq*n][S] (fp32).
-inline int window_segments(int sink, int window) { return (sink + window + 63) / 64; }
+inline int window_segments(int sink, int window) {
+  return (int)(((int64_t)sink + window + 63) / 64);
+}
 inline size_t window_o_words(size_t rows, size_t S, int d) {
   return (rows * S * (size_t)d + 63) & ~(size_t)63;
 }

@@ -12,13 +12,16 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int ceil_div(int a, int b) { return (a + b - 1) / b; }
+int ceil_div(int a, int b) { return (int)(((int64_t)a + b - 1) / b); }
 
 }  // namespace
 
+// Callers validate (Hq/Hkv)*n <= RV_MAX_GROUP_ROWS first; larger groups are
+// clamped here only so the arithmetic stays defined.
 RowPlan row_plan(int Hq, int Hkv, int n) {
   RowPlan p;
-  p.M = (Hq / Hkv) * n;
+  const int64_t M = (int64_t)(Hq / Hkv) * n;
+  p.M = (int)(M < RV_MAX_GROUP_ROWS ? M : RV_MAX_GROUP_ROWS);
   p.MT = ceil_div(p.M, 16);
   p.RG = ceil_div(p.MT, kMaxTilesPerWave);
   p.MTW = ceil_div(p.MT, p.RG);
@@ -28,6 +31,7 @@ RowPlan row_plan(int Hq, int Hkv, int n) {
 static rv_status check_heads(int B, int Hq, int Hkv, int n, int d) {
   if (B < 1 || Hq < 1 || Hkv < 1 || n < 1) return RV_ERR_SHAPE;
   if (Hq % Hkv != 0) return RV_ERR_SHAPE;
+  if (B > 65535 || Hq > 65535) return RV_ERR_UNSUPPORTED;  // grid dimensions
   if (n > RV_MAX_BLOCK_ROWS) return RV_ERR_UNSUPPORTED;
   if ((int64_t)(Hq / Hkv) * n > RV_MAX_GROUP_ROWS) return RV_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return RV_ERR_UNSUPPORTED;
@@ -43,7 +47,7 @@ rv_status check_prefix(const void* q, const void* k_cache, const void* v_cache,
   if (st != RV_OK) return st;
   if (L_max < 0 || max_seq_len < 0 || max_seq_len > L_max) return RV_ERR_SHAPE;
   // buffer offsets inside one (sequence, kv-head) slab are 32-bit
-  if (L_max * (int64_t)d * 2 > (int64_t)0x7fffffff) return RV_ERR_UNSUPPORTED;
+  if (L_max > (int64_t)0x7fffffff / (2 * d)) return RV_ERR_UNSUPPORTED;
   if (split_len <= 0 || split_len % kSplitQuantum != 0) return RV_ERR_SHAPE;
   if (num_splits < 1 || num_splits > 65535) return RV_ERR_SHAPE;
   if ((max_seq_len + split_len - 1) / split_len > num_splits) return RV_ERR_SHAPE;
@@ -113,6 +117,7 @@ rv_status check_window(const void* q, const void* k_ring, const void* v_ring,
   rv_status st = check_heads(B, Hq, Hkv, n, d);
   if (st != RV_OK) return st;
   if (window < 1 || sink < 0 || cap < 1) return RV_ERR_SHAPE;
+  if (window > kMaxWindowKeys || sink > kMaxWindowKeys) return RV_ERR_UNSUPPORTED;
   // every position a row of the block sees must still be in the ring
   if ((int64_t)cap - sink < (int64_t)window + n - 1) return RV_ERR_SHAPE;
   if (!isfinite(sm_scale) || !(sm_scale > 0.0f)) return RV_ERR_VALUE;
@@ -132,7 +137,7 @@ rv_status check_merge(const float* o_part, const float* lse_part, int S, const f
   if (!o_part || !lse_part || !out) return RV_ERR_NULL;
   if ((o_blk == nullptr) != (lse_blk == nullptr)) return RV_ERR_NULL;  // both or neither
   if (B < 1 || Hq < 1 || n < 1 || S < 1) return RV_ERR_SHAPE;
-  if (n > RV_MAX_BLOCK_ROWS) return RV_ERR_UNSUPPORTED;
+  if (n > RV_MAX_BLOCK_ROWS || B > 65535 || Hq > 65535) return RV_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return RV_ERR_UNSUPPORTED;
   if ((int64_t)B * Hq * n > 0x7fffffff / 4) return RV_ERR_UNSUPPORTED;
   if (!aligned16(o_part) || !aligned16(lse_part) || !aligned16(out)) return RV_ERR_ALIGNMENT;
@@ -207,12 +212,19 @@ rv_status rv_prefix_default_split(int64_t max_seq_len, int B, int Hq, int Hkv, i
   if (!split_len || !num_splits) return RV_ERR_NULL;
   if (B < 1 || Hq < 1 || Hkv < 1 || n < 1 || Hq % Hkv != 0 || max_seq_len < 0)
     return RV_ERR_SHAPE;
+  if (B > 65535 || max_seq_len > ((int64_t)1 << 40)) return RV_ERR_UNSUPPORTED;
+  if (n > RV_MAX_BLOCK_ROWS || (int64_t)(Hq / Hkv) * n > RV_MAX_GROUP_ROWS)
+    return RV_ERR_UNSUPPORTED;
   (void)d;
   const int64_t q = rv::kSplitQuantum;
   rv::RowPlan rp = rv::row_plan(Hq, Hkv, n);
   const int64_t groups = (int64_t)B * Hkv * rp.RG;
   const int64_t target_groups = 256;  // one 4-wave workgroup per compute unit
-  int64_t per = (max_seq_len * groups + target_groups - 1) / target_groups;
+  // with at least one group per compute unit every group takes its whole
+  // sequence as one split (and the product below could overflow)
+  int64_t per = groups >= target_groups
+                    ? max_seq_len
+                    : (max_seq_len * groups + target_groups - 1) / target_groups;
   int64_t len = ((per + q - 1) / q) * q;
   const int64_t min_len = 8 * q;  // at least 8 tiles per wave
   if (len < min_len) len = min_len;
