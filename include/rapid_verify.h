@@ -60,6 +60,9 @@
  * - Workspaces (rapid_accept, spec_attn_window) are caller-owned device
  *   scratch; they need no initial contents and hold nothing between calls.
  *
+ * - Sizes beyond the launch grid's reach (B or Hq above 65535, a window or
+ *   sink above 2^24) return RV_ERR_UNSUPPORTED.
+ *
  * Notation: B batch, Hq query heads, Hkv kv heads (Hq % Hkv == 0, query head
  * h reads kv head h / (Hq/Hkv)), n block rows (gamma+1 for a chain, the node
  * count for a tree), d head dim, L_max cache capacity per sequence, S number
