@@ -25,13 +25,18 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I" + INCLUDE, "-I" + CSRC]
 DEVICE = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The history pass takes row maxima of MFMA scores with fmaxf; allowing the
+# compiler to assume no NaN drops the quieting v_max that IEEE mode puts in
+# front of every such max (a third of the softmax's VALU work).  The kernels
+# compare only against -inf, never against NaN.
+PER_SOURCE = {"attn_prefix.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src):
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
     if src.endswith(".hip"):
-        cmd = [HIPCC, "-x", "hip"] + DEVICE + COMMON + ["-c", path, "-o", obj]
+        cmd = [HIPCC, "-x", "hip"] + DEVICE + COMMON + PER_SOURCE.get(src, []) + ["-c", path, "-o", obj]
     else:
         cmd = [HIPCC, "-x", "c++"] + COMMON + ["-c", path, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)

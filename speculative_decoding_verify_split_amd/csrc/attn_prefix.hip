@@ -4,13 +4,16 @@
 // to a plain fast attention pass whose result is later merged by log-sum-exp).
 //
 // Work decomposition (gfx950, 64-wide waves):
-//   grid  = (split s, kv-head x row-group, sequence b); 4 waves per workgroup.
-//   A workgroup owns one split of one (b, kv-head).  The G = Hq/Hkv query
-//   heads of that kv-head share every K/V byte, so their G*n rows are stacked
-//   into 16-row MFMA tiles (up to 4 per wave; larger groups use several row
-//   groups).  Wave w streams the split's 32-key tiles w, w+4, w+8, ...
+//   grid  = (split s, kv-head, sequence b).  A workgroup owns one split of
+//   one (b, kv-head).  The G = Hq/Hkv query heads of that kv-head share every
+//   K/V byte, so their G*n rows are stacked into 16-row MFMA tiles, and one
+//   workgroup takes all of them, so every byte of the split is read once.
+//   Up to 4 row tiles (64 rows): attn_kernel below, 4 waves, wave w streams
+//   the split's 32-key tiles w, w+4, w+8, ... through its own registers.
+//   More rows: attn_wide_kernel further down, which stages K/V in LDS for
+//   all waves (its own notes describe it).
 //
-// Per tile:
+// attn_kernel, per tile:
 //   * K and V arrive by non-temporal 16-byte buffer loads (read once; range-
 //     checked, so keys past the split read as zero), one tile ahead of use.
 //   * Scores are computed transposed, S^T = K Q^T, on
@@ -32,6 +35,8 @@
 // rule from another XCD).
 
 #include <hip/hip_ext.h>
+
+#include <utility>
 
 #include "rv_device.h"
 #include "rv_internal.h"
@@ -89,7 +94,7 @@ template <int D, int MT>
 __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ seq_lens, int Hq, int Hkv,
-    int n, int64_t L_max, float scale_log2, int64_t split_len, int S, int RG,
+    int n, int64_t L_max, float scale_log2, int64_t split_len, int S,
     float* __restrict__ o_part, float* __restrict__ lse_part) {
   using Gm = PrefixGeom<D>;
   constexpr int KS = Gm::KS, NB = Gm::NB, VCH = Gm::VCH, VROW = Gm::VROW, OROW = Gm::OROW;
@@ -110,8 +115,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
   __shared__ float l_lds[NW][MT * 16];
 
   const int s = blockIdx.x;
-  const int kvh = blockIdx.y / RG;
-  const int rg = blockIdx.y - kvh * RG;
+  const int kvh = blockIdx.y;
   const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -119,8 +123,6 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
   const int lg = lane >> 4;
   const int G = Hq / Hkv;
   const int M = G * n;
-  const int row0 = rg * MT * 16;
-  const int rows_here = min(MT * 16, M - row0);
 
   int64_t L = seq_lens[b];
   L = L < 0 ? 0 : (L > L_max ? L_max : L);
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
   bf16x8 qf[kQLds ? 1 : MT][KS];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    const int row = row0 + mt * 16 + lr;
+    const int row = mt * 16 + lr;
     bf16x8 frag[KS];
     if (row < M) {
       const int gq = row / n;
@@ -345,12 +347,11 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
   __syncthreads();
 
   auto out_row = [&](int row) {  // (b, h, i) index of local row `row`
-    const int grow = row0 + row;
-    const int gq = grow / n;
-    const int i = grow - gq * n;
+    const int gq = row / n;
+    const int i = row - gq * n;
     return ((int64_t)b * Hq + kvh * G + gq) * n + i;
   };
-  if ((int)threadIdx.x < rows_here) {
+  if ((int)threadIdx.x < M) {
     const int row = threadIdx.x;
     float mw[NW], M = -INFINITY;
 #pragma unroll
@@ -378,7 +379,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
     const int idx = threadIdx.x + j * NW * 64;
     const int row = idx / (D / 4);
     const int c4 = idx - row * (D / 4);
-    if (row < rows_here) {
+    if (row < M) {
       f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < NW; ++w)
@@ -390,41 +391,459 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
   }
 }
 
+// History pass for wide groups (more than 64 rows per kv head: 64/8 heads
+// with 11 verify rows, a 32-node tree over 4 heads per kv head).  One
+// workgroup takes every row of the group, so each K/V byte of the split
+// leaves HBM once, and each wave runs every key against its own row tiles
+// mt = wave, wave + 4, ... (MTW of them; a tile past the group's rows holds
+// zero queries and is never written).  A wave holds complete rows, so it
+// normalises and writes its own partials.
+//
+// K/V move HBM -> LDS with gfx950's 16-byte buffer loads into LDS (no
+// register staging), in 64-key stages through a ring of kBufs LDS buffers:
+// while stage st is computed, stages st + 1 .. st + kBufs - 1 are in flight.
+// Each 1 KB load instruction lands in one contiguous 1 KB LDS block (lane L
+// at 16 L) and reads whole 128-byte lines: 8 keys x 128 bytes (half a key
+// row at d = 128), lane L taking row L / 8.  Within a row the eight 16-byte
+// chunks are stored permuted, chunk c at slot c ^ f(row), so that the MFMA
+// operand reads spread over all LDS banks:
+//   * K (A operand, ds_read_b128 of 16 keys x 16 bytes): f = r ^ (g & 1)
+//     for row r of 8-row group g;
+//   * V (ds_read_b64_tr_b16 of 4 keys x 32 bytes per 16 lanes):
+//     f = 2 ((r1 ^ r2) << 1 | (r0 ^ r2)) over the bits r2 r1 r0 of r.
+// (Loads of 16 keys x 64 bytes, one operand per instruction, leave half of
+// every line to another wave's instruction and stream ~15% slower.)
+// Every load reads a key inside the split (keys past its end are clamped to
+// its last key, whose scores are then masked), so no padding is ever read.
+// The pipeline's waits are explicit: a wave waits for its own loads of
+// stage st (vmcnt counts them in issue order), then a barrier makes the
+// whole stage visible and frees stage st - 1's buffer for reuse.
+// s_waitcnt encoding (gfx9 family) for vmcnt(0), expcnt and lgkmcnt at
+// their maxima (no wait on them).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+template <int N, typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
+// Chunk permutation of the V rows (see the layout note above).
+__device__ __forceinline__ int swz_v(int r) {
+  const int r0 = r & 1, r1 = (r >> 1) & 1, r2 = (r >> 2) & 1;
+  return 2 * (((r1 ^ r2) << 1) | (r0 ^ r2));
+}
+
+template <int D, int NWV>
+struct WideGeom {
+  static constexpr int KS = D / 32, NB = D / 16;
+  static constexpr int SK = 64;                  // keys per stage
+  static constexpr int HALVES = D / 64;          // 128-byte lines per key row
+  static constexpr int KBLK = (SK / 8) * HALVES; // 1 KB K blocks per stage (8 keys x 128 B)
+  static constexpr int VBLK = KBLK;              // and V blocks
+  static constexpr int NI = KBLK + VBLK;         // 1 KB loads per stage
+  static constexpr int PW = NI / NWV;            // of which each wave issues
+  static constexpr int KPW = KBLK / NWV;         // the first KPW of a wave's loads are K
+  static constexpr int STAGE = NI * 1024;
+  static constexpr int kBufs = (128 * 1024) / STAGE;
+  static_assert(KBLK % NWV == 0 && VBLK % NWV == 0, "loads must split evenly over the waves");
+  static_assert(kBufs >= 2 && (kBufs - 2) * PW <= 63, "vmcnt range");
+};
+
+typedef __attribute__((address_space(3))) const unsigned char lds_cu8;
+
+// ds_read_b64_tr_b16 issued from inline asm.  The compiler treats the
+// builtin as a possible reader of every pending LDS-DMA write and waits for
+// all of them (vmcnt(0)) in front of it, which would drain the load
+// pipeline every tile; here the pipeline's explicit waits already order it.
+// The result is valid only after lds_wait().
+template <int OFF>
+__device__ __forceinline__ s16x4 ds_read_tr16_asm(uint32_t lds_addr) {
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "n"(OFF));
+  return r;
+}
+
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Wait until at most N of this wave's vector-memory loads are outstanding,
+// then meet the workgroup at a barrier.  LDS reads of earlier stages are
+// complete too (lgkmcnt), so the buffer they used may be refilled.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int PW, int K>
+__device__ __forceinline__ void wait_stage(int ahead) {
+  if constexpr (K == 0) {
+    wait_vm_barrier<0>();
+  } else {
+    if (ahead >= K) wait_vm_barrier<K * PW>();
+    else wait_stage<PW, K - 1>(ahead);
+  }
+}
+
+// KP key phases: 4 * KP waves; wave w computes the tiles tt of each stage
+// with tt % KP == w / 4 (its phase) for a contiguous run of the group's row
+// tiles (at most MTW).  With KP = 2 two waves share every SIMD (waves w and
+// w + 4), so one wave's MFMA and LDS latencies hide behind the other's
+// softmax, and the two phases of a row tile merge at the end.  The runs are
+// sized so that the two waves of a SIMD together hold as even a share of
+// the 2 MT (row tile, phase) units as possible: phase 0 gives the extra
+// tiles to its first waves, phase 1 to its last.
+template <int D, int MTW, int KP>
+__global__ __launch_bounds__(NW * KP * 64, 1) void attn_wide_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, const int32_t* __restrict__ seq_lens, int Hq, int Hkv,
+    int n, int64_t L_max, float scale_log2, int64_t split_len, int S,
+    float* __restrict__ o_part, float* __restrict__ lse_part) {
+  constexpr int NWV = NW * KP;
+  using W = WideGeom<D, NWV>;
+  constexpr int KS = W::KS, NB = W::NB, SK = W::SK, PW = W::PW, KPW = W::KPW;
+  constexpr int STAGE = W::STAGE, NBUF = W::kBufs;
+  constexpr int TPS = SK / KT;  // 32-key tiles per stage
+  static_assert(TPS % KP == 0, "each phase takes whole tiles of a stage");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NBUF * STAGE];
+
+  const int s = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rgw = wave % NW;    // row-tile owner
+  const int phase = wave / NW;  // key phase
+  const int lr = lane & 15;
+  const int lg = lane >> 4;
+  const int G = Hq / Hkv;
+  const int M = G * n;
+  const int MT = (M + 15) / 16;
+  const int tbase = MT / NW, textra = MT - (MT / NW) * NW;
+  const int tcnt = phase == 0 ? tbase + (rgw < textra) : tbase + (rgw >= NW - textra);
+  const int tfirst = phase == 0 ? rgw * tbase + min(rgw, textra)
+                                : rgw * tbase + max(0, rgw - (NW - textra));
+
+  int64_t L = seq_lens[b];
+  L = L < 0 ? 0 : (L > L_max ? L_max : L);
+  const int64_t kbeg = (int64_t)s * split_len;
+  int64_t kend = kbeg + split_len;
+  if (kend > L) kend = L;
+  const int nkeys = kend > kbeg ? (int)(kend - kbeg) : 0;
+  const int nst = (nkeys + SK - 1) / SK;
+
+  // Query fragments (B operand of S^T = K Q^T) of this wave's row tiles.
+  bf16x8 qf[MTW][KS];
+#pragma unroll
+  for (int j = 0; j < MTW; ++j) {
+    const int row = (tfirst + j) * 16 + lr;
+    if (j < tcnt && row < M) {
+      const int gq = row / n;
+      const int i = row - gq * n;
+      const uint16_t* qp = q + (((int64_t)b * Hq + kvh * G + gq) * n + i) * D + lg * 8;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[j][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[j][ks] = bf16x8{};
+    }
+  }
+
+  const size_t slab = ((size_t)b * Hkv + kvh) * (size_t)L_max * D + (size_t)kbeg * D;
+  const uint32_t nbytes = (uint32_t)nkeys * D * 2;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kc + slab, nbytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vc + slab, nbytes);
+
+  // This wave issues loads i = wave + NWV j (j < PW) of every stage; loads
+  // below KBLK are K blocks, the rest V blocks.  Per lane: the key within
+  // the stage and the byte offset within the key's row.
+  constexpr int HALVES = W::HALVES;
+  const int r8 = lane >> 3;  // row of the lane within its load's 8 keys
+  int key_l[PW], col_b[PW];
+#pragma unroll
+  for (int j = 0; j < PW; ++j) {
+    const int i = wave + NWV * j;
+    const int blk = j < KPW ? i : i - W::KBLK;
+    const int g = blk / HALVES, h = blk - (blk / HALVES) * HALVES;
+    const int f = j < KPW ? (r8 ^ (g & 1)) : swz_v(r8);
+    key_l[j] = 8 * g + r8;
+    col_b[j] = 128 * h + 16 * ((lane & 7) ^ f);
+  }
+  // Per-lane LDS offsets of the operand reads within a tile's blocks.
+  // K, k-step ks: row lr of the 16-key block, chunk 4 (ks & 1) + lg.
+  const int kx = lg ^ (lr & 7) ^ (lr >> 3);
+  const uint32_t krow = (uint32_t)((lr >> 3) * HALVES * 1024 + (lr & 7) * 128);
+  const uint32_t kofs[2] = {krow + 16u * (uint32_t)kx, krow + 16u * (uint32_t)(kx ^ 4)};
+  // V, 16-column group nb: source lane 4 e + c4 of 16-lane group lg reads
+  // key 4 lg + e of the 16-key block, columns 16 nb + 4 c4 .. + 3, i.e.
+  // chunk 2 (nb % 4) + c4 / 2 of line nb / 4, byte 8 (c4 & 1).
+  const int vr = 4 * (lg & 1) + ((lane & 15) >> 2);
+  const int vy = ((lane & 3) >> 1) | swz_v(vr);
+  const uint32_t vrow = (uint32_t)((lg >> 1) * HALVES * 1024 + vr * 128 + 8 * (lane & 1));
+  uint32_t vofs[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) vofs[m] = vrow + 16u * (uint32_t)((2 * m) ^ vy);
+  auto issue_stage = [&](int st) {
+    unsigned char* buf = smem + (st % NBUF) * STAGE;
+#pragma unroll
+    for (int j = 0; j < PW; ++j) {
+      const int i = wave + NWV * j;
+      const int key = min(st * SK + key_l[j], nkeys - 1);
+      const uint32_t off = (uint32_t)key * (D * 2) + (uint32_t)col_b[j];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          j < KPW ? krs : vrs, (__attribute__((address_space(3))) void*)(buf + i * 1024), 16,
+          off, 0, 0, 2);
+    }
+  };
+
+  f32x4 oacc[NB][MTW];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int j = 0; j < MTW; ++j) oacc[nb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[MTW], l_run[MTW];
+#pragma unroll
+  for (int j = 0; j < MTW; ++j) {
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.f;
+  }
+
+  // One 32-key tile t; kt: the stage's K blocks of its two 16-key blocks,
+  // vt: their V blocks.  Score layout, online softmax and P V product as
+  // in the per-wave streaming kernel above.
+  auto compute_tile = [&](const unsigned char* kt, const unsigned char* vt, int t) {
+    bf16x8 kf[2][KS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kf[kb][ks] = *reinterpret_cast<const bf16x8*>(
+            kt + kofs[ks & 1] + (2 * kb * HALVES + (ks >> 1)) * 1024);
+    f32x4 sacc[2][MTW];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < MTW; ++j) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (j == 0 || j < tcnt) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][ks], qf[j][ks], acc, 0, 0, 0);
+        }
+        sacc[kb][j] = acc;
+      }
+    // V operands next (after the K reads the score MFMAs wait for): their
+    // LDS latency hides behind the scores and the softmax.
+    s16x4 vlo[NB], vhi[NB];
+    const uint32_t vbase = (uint32_t)(uintptr_t)(lds_cu8*)vt;
+    uint32_t va[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) va[m] = vbase + vofs[m];
+    static_for<NB>([&](auto nb) {
+      vlo[nb] = ds_read_tr16_asm<(nb / 4) * 1024>(va[nb % 4]);
+      vhi[nb] = ds_read_tr16_asm<(2 * HALVES + nb / 4) * 1024>(va[nb % 4]);
+    });
+
+    if ((t + 1) * KT > nkeys) {
+      const int key0 = t * KT + lg * 4;
+#pragma unroll
+      for (int j = 0; j < MTW; ++j)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            if (key0 + kb * 16 + v >= nkeys) sacc[kb][j][v] = -INFINITY;
+          }
+    }
+
+    bf16x8 pf[MTW];
+#pragma unroll
+    for (int j = 0; j < MTW; ++j) {
+      pf[j] = bf16x8{};
+      if (j > 0 && j >= tcnt) continue;
+      float mx = fmaxf(fmaxf(fmaxf(sacc[0][j][0], sacc[0][j][1]),
+                             fmaxf(sacc[0][j][2], sacc[0][j][3])),
+                       fmaxf(fmaxf(sacc[1][j][0], sacc[1][j][1]),
+                             fmaxf(sacc[1][j][2], sacc[1][j][3])));
+      mx = row_max4(mx);
+      const float m_tile = mx * scale_log2;
+      const bool raise = m_tile > m_run[j] + kRescaleSlack;
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        const float m_new = raise ? m_tile : m_run[j];
+        const float alpha = exp2_hw(m_run[j] - m_new);
+        l_run[j] *= alpha;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) oacc[nb][j] *= alpha;
+        m_run[j] = m_new;
+      }
+      const float neg_m = (m_run[j] == -INFINITY) ? 0.f : -m_run[j];
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float p = exp2_hw(fmaf(sacc[kb][j][v], scale_log2, neg_m));
+          ps += p;
+          pf[j][kb * 4 + v] = (__bf16)p;
+        }
+      l_run[j] += ps;
+    }
+
+    lds_wait();
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const bf16x8 va = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(vlo[nb], vhi[nb], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int j = 0; j < MTW; ++j)
+        if (j == 0 || j < tcnt)
+          oacc[nb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[j], oacc[nb][j], 0, 0, 0);
+    }
+  };
+
+  // The query loads complete before the first stage is issued, so the
+  // compiler's wait for them does not also wait for the stages.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  // nst is the same for every wave of the workgroup, so every thread
+  // reaches every barrier.
+  for (int st = 0; st < nst && st < NBUF - 1; ++st) issue_stage(st);
+  for (int st = 0; st < nst; ++st) {
+    // stages issued after st and still possibly in flight
+    const int ahead = min(NBUF - 2, nst - 1 - st);
+    wait_stage<PW, NBUF - 2>(ahead);
+    if (st + NBUF - 1 < nst) issue_stage(st + NBUF - 1);  // into stage st - 1's buffer
+    const unsigned char* buf = smem + (st % NBUF) * STAGE;
+#pragma unroll
+    for (int u = 0; u < TPS / KP; ++u) {
+      const int tt = u * KP + phase;
+      const int t = st * TPS + tt;
+      if (t * KT >= nkeys) break;
+      compute_tile(buf + tt * 4 * HALVES * 1024, buf + (W::KBLK + tt * 4 * HALVES) * 1024, t);
+    }
+  }
+
+  float l_row[MTW];
+#pragma unroll
+  for (int j = 0; j < MTW; ++j) l_row[j] = row_sum4(l_run[j]);
+
+  if constexpr (KP == 2) {
+    // Phase 1 parks (max, sum, O) of its row tiles in LDS slots indexed by
+    // row tile (the stage ring is idle once every wave has passed the
+    // barrier); the phase-0 owner of each tile folds them into its own
+    // state, lane by lane: both hold the same (row, column) positions.
+    constexpr int OROW = D + 4;  // floats per parked row (bank spread)
+    float* obuf = reinterpret_cast<float*>(smem);
+    float* mbuf = obuf + NW * MTW * 16 * OROW;
+    float* lbuf = mbuf + NW * MTW * 16;
+    static_assert((NW * MTW * 16 * (OROW + 2)) * 4 <= NBUF * STAGE, "merge slots fit the ring");
+    __syncthreads();
+    if (phase == 1) {
+#pragma unroll
+      for (int j = 0; j < MTW; ++j) {
+        if (j >= tcnt) break;
+        const int slot = (tfirst + j) * 16 + lr;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          *reinterpret_cast<f32x4*>(obuf + slot * OROW + nb * 16 + lg * 4) = oacc[nb][j];
+        if (lg == 0) {
+          mbuf[slot] = m_run[j];
+          lbuf[slot] = l_row[j];
+        }
+      }
+    }
+    __syncthreads();
+    if (phase == 1) return;
+#pragma unroll
+    for (int j = 0; j < MTW; ++j) {
+      if (j >= tcnt) break;
+      const int slot = (tfirst + j) * 16 + lr;
+      const float m1 = mbuf[slot], l1 = lbuf[slot];
+      const float mm = fmaxf(m_run[j], m1);
+      const float a0 = m_run[j] == -INFINITY ? 0.f : exp2_hw(m_run[j] - mm);
+      const float a1 = m1 == -INFINITY ? 0.f : exp2_hw(m1 - mm);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        oacc[nb][j] = a0 * oacc[nb][j] +
+                      a1 * *reinterpret_cast<const f32x4*>(obuf + slot * OROW + nb * 16 + lg * 4);
+      l_row[j] = a0 * l_row[j] + a1 * l1;
+      m_run[j] = mm;
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < MTW; ++j) {
+    const float l = l_row[j];
+    const int row = (tfirst + j) * 16 + lr;
+    if (j < tcnt && row < M) {
+      const int gq = row / n;
+      const int i = row - gq * n;
+      const int64_t orow = ((int64_t)b * Hq + kvh * G + gq) * n + i;
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      float* op = o_part + (orow * S + s) * D + lg * 4;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        __builtin_nontemporal_store(oacc[nb][j] * inv, reinterpret_cast<f32x4*>(op + nb * 16));
+      if (lg == 0) lse_part[orow * S + s] = l > 0.f ? (m_run[j] + log2_hw(l)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
 // With start/stop events the launch records them on the kernel's own
 // dispatch (hipExtLaunchKernel), so their elapsed time is the kernel's.
-template <int D, int MT>
-hipError_t launch_attn(const void* q, const void* k, const void* v, const int32_t* seq_lens,
-                       int B, int Hq, int Hkv, int n, int64_t L_max, float scale_log2,
-                       int64_t split_len, int S, int RG, float* o_part, float* lse_part,
-                       hipStream_t stream, hipEvent_t ev_start, hipEvent_t ev_stop) {
-  dim3 grid((unsigned)S, (unsigned)(Hkv * RG), (unsigned)B);
+template <typename Kernel>
+hipError_t launch_attn(Kernel kernel, int waves, const void* q, const void* k, const void* v,
+                       const int32_t* seq_lens, int B, int Hq, int Hkv, int n, int64_t L_max,
+                       float scale_log2, int64_t split_len, int S, float* o_part,
+                       float* lse_part, hipStream_t stream, hipEvent_t ev_start,
+                       hipEvent_t ev_stop) {
+  dim3 grid((unsigned)S, (unsigned)Hkv, (unsigned)B);
+  const dim3 block((unsigned)(waves * 64));
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   if (ev_start != nullptr || ev_stop != nullptr)
-    hipExtLaunchKernelGGL((attn_kernel<D, MT>), grid, dim3(NW * 64), 0, stream, ev_start,
-                          ev_stop, 0, qq, kk, vv, seq_lens, Hq, Hkv, n, L_max, scale_log2,
-                          split_len, S, RG, o_part, lse_part);
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev_start, ev_stop, 0, qq, kk,
+                          vv, seq_lens, Hq, Hkv, n, L_max, scale_log2, split_len, S, o_part,
+                          lse_part);
   else
-    hipLaunchKernelGGL((attn_kernel<D, MT>), grid, dim3(NW * 64), 0, stream, qq, kk, vv,
-                       seq_lens, Hq, Hkv, n, L_max, scale_log2, split_len, S, RG, o_part,
-                       lse_part);
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, qq, kk, vv, seq_lens, Hq, Hkv,
+                       n, L_max, scale_log2, split_len, S, o_part, lse_part);
   return hipGetLastError();
 }
 
-rv_status dispatch_attn(int d, int MTW, const void* q, const void* k, const void* v,
+rv_status dispatch_attn(int d, const RowPlan& rp, const void* q, const void* k, const void* v,
                         const int32_t* seq_lens, int B, int Hq, int Hkv, int n, int64_t L_max,
-                        float scale_log2, int64_t split_len, int S, int RG, float* o_part,
+                        float scale_log2, int64_t split_len, int S, float* o_part,
                         float* lse_part, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   hipError_t e;
-#define RV_ATTN_CASE(DD, MM)                                                                 \
-  if (d == DD && MTW == MM)                                                                  \
-    e = launch_attn<DD, MM>(q, k, v, seq_lens, B, Hq, Hkv, n, L_max, scale_log2, split_len,  \
-                            S, RG, o_part, lse_part, s, e0, e1);
-  RV_ATTN_CASE(64, 1)
-  else RV_ATTN_CASE(64, 2) else RV_ATTN_CASE(64, 3) else RV_ATTN_CASE(64, 4)
-  else RV_ATTN_CASE(128, 1) else RV_ATTN_CASE(128, 2) else RV_ATTN_CASE(128, 3)
-  else RV_ATTN_CASE(128, 4) else return RV_ERR_UNSUPPORTED;
+#define RV_ATTN_CASE(DD, MM, KERNEL, WAVES)                                                     \
+  if (d == DD && rp.MTW == MM)                                                                 \
+    e = launch_attn(KERNEL, WAVES, q, k, v, seq_lens, B, Hq, Hkv, n, L_max, scale_log2,       \
+                    split_len, S, o_part, lse_part, s, e0, e1);
+  // Up to 4 row tiles: the per-wave streaming kernel.  5..8 tiles: the
+  // shared-stage kernel with two key phases (8 waves, 2 tiles each); wider
+  // groups: one phase (4 waves, 3 or 4 tiles each).
+  if (!rp.wide) {
+    RV_ATTN_CASE(64, 1, (attn_kernel<64, 1>), NW)
+    else RV_ATTN_CASE(64, 2, (attn_kernel<64, 2>), NW)
+    else RV_ATTN_CASE(64, 3, (attn_kernel<64, 3>), NW)
+    else RV_ATTN_CASE(64, 4, (attn_kernel<64, 4>), NW)
+    else RV_ATTN_CASE(128, 1, (attn_kernel<128, 1>), NW)
+    else RV_ATTN_CASE(128, 2, (attn_kernel<128, 2>), NW)
+    else RV_ATTN_CASE(128, 3, (attn_kernel<128, 3>), NW)
+    else RV_ATTN_CASE(128, 4, (attn_kernel<128, 4>), NW)
+    else return RV_ERR_UNSUPPORTED;
+  } else {
+    RV_ATTN_CASE(64, 2, (attn_wide_kernel<64, 2, 2>), 2 * NW)
+    else RV_ATTN_CASE(64, 3, (attn_wide_kernel<64, 3, 1>), NW)
+    else RV_ATTN_CASE(64, 4, (attn_wide_kernel<64, 4, 1>), NW)
+    else RV_ATTN_CASE(128, 2, (attn_wide_kernel<128, 2, 2>), 2 * NW)
+    else RV_ATTN_CASE(128, 3, (attn_wide_kernel<128, 3, 1>), NW)
+    else RV_ATTN_CASE(128, 4, (attn_wide_kernel<128, 4, 1>), NW)
+    else return RV_ERR_UNSUPPORTED;
+  }
 #undef RV_ATTN_CASE
   if (e != hipSuccess) {
     (void)hipGetLastError();
@@ -446,8 +865,8 @@ extern "C" rv_status spec_attn_prefix(const void* q, const void* k_cache, const 
   if (st != RV_OK) return st;
   const rv::RowPlan rp = rv::row_plan(Hq, Hkv, n);
   const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
-  return rv::dispatch_attn(d, rp.MTW, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, n, L_max,
-                           scale_log2, split_len, num_splits, rp.RG, o_part, lse_part,
+  return rv::dispatch_attn(d, rp, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, n, L_max,
+                           scale_log2, split_len, num_splits, o_part, lse_part,
                            static_cast<hipStream_t>(stream), nullptr, nullptr);
 }
 
@@ -462,8 +881,8 @@ extern "C" rv_status spec_attn_prefix_ev(const void* q, const void* k_cache,
   if (st != RV_OK) return st;
   const rv::RowPlan rp = rv::row_plan(Hq, Hkv, n);
   const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
-  return rv::dispatch_attn(d, rp.MTW, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, n, L_max,
-                           scale_log2, split_len, num_splits, rp.RG, o_part, lse_part,
+  return rv::dispatch_attn(d, rp, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, n, L_max,
+                           scale_log2, split_len, num_splits, o_part, lse_part,
                            static_cast<hipStream_t>(stream),
                            static_cast<hipEvent_t>(start_event),
                            static_cast<hipEvent_t>(stop_event));

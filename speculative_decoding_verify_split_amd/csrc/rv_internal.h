@@ -18,9 +18,13 @@ constexpr int kMaxTilesPerWave = 4; // 16-row MFMA tiles a wave keeps in registe
 constexpr int kSplitQuantum = kKeysPerTile * kWavesPerGroup;  // split_len granularity
 
 // How the rows of one (sequence, kv-head) group are spread over workgroups:
-// M = (Hq/Hkv)*n rows, MT = ceil(M/16) row tiles, RG row groups of MTW tiles.
+// M = (Hq/Hkv)*n rows in MT = ceil(M/16) row tiles.  Up to kMaxTilesPerWave
+// tiles every wave keeps all of them (MTW = MT) and streams its own share of
+// the keys; wider groups go to the shared-stage kernel, where wave w keeps
+// tiles w, w + 4, ... (MTW = ceil(MT/4) of them) and sees every key.
 struct RowPlan {
-  int M, MT, RG, MTW;
+  int M, MT, MTW;
+  bool wide;
 };
 RowPlan row_plan(int Hq, int Hkv, int n);
 

@@ -23,8 +23,8 @@ RowPlan row_plan(int Hq, int Hkv, int n) {
   const int64_t M = (int64_t)(Hq / Hkv) * n;
   p.M = (int)(M < RV_MAX_GROUP_ROWS ? M : RV_MAX_GROUP_ROWS);
   p.MT = ceil_div(p.M, 16);
-  p.RG = ceil_div(p.MT, kMaxTilesPerWave);
-  p.MTW = ceil_div(p.MT, p.RG);
+  p.wide = p.MT > kMaxTilesPerWave;
+  p.MTW = p.wide ? ceil_div(p.MT, kWavesPerGroup) : p.MT;
   return p;
 }
 
@@ -55,8 +55,7 @@ rv_status check_prefix(const void* q, const void* k_cache, const void* v_cache,
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o_part) ||
       !aligned16(lse_part))
     return RV_ERR_ALIGNMENT;
-  RowPlan rp = row_plan(Hq, Hkv, n);
-  if ((int64_t)Hkv * rp.RG > 65535 || B > 65535) return RV_ERR_UNSUPPORTED;
+  if (Hkv > 65535) return RV_ERR_UNSUPPORTED;  // grid dimension
   return RV_OK;
 }
 
@@ -217,8 +216,7 @@ rv_status rv_prefix_default_split(int64_t max_seq_len, int B, int Hq, int Hkv, i
     return RV_ERR_UNSUPPORTED;
   (void)d;
   const int64_t q = rv::kSplitQuantum;
-  rv::RowPlan rp = rv::row_plan(Hq, Hkv, n);
-  const int64_t groups = (int64_t)B * Hkv * rp.RG;
+  const int64_t groups = (int64_t)B * Hkv;
   const int64_t target_groups = 256;  // one 4-wave workgroup per compute unit
   // with at least one group per compute unit every group takes its whole
   // sequence as one split (and the product below could overflow)

@@ -43,7 +43,7 @@ def _attn_outputs(st):
 ATTN_CASES = [
     # name, seed, B, Hq, Hkv, d, n, lengths, L_max, parent, split
     ("d128-g4-n11-ragged", 21, 2, 8, 2, 128, 11, [3000, 1777], 3072, None, (512, 6)),
-    ("d128-g8-n11-two-rowgroups", 22, 1, 16, 2, 128, 11, [2500], None, None, None),
+    ("d128-g8-n11-wide", 22, 1, 16, 2, 128, 11, [2500], None, None, None),
     ("d128-g7-n11-b3-empty", 23, 3, 28, 4, 128, 11, [1500, 0, 2049], None, None, (256, 9)),
     ("d128-g4-tree32", 24, 1, 8, 2, 128, 32, [2000], None, "tree", None),
     ("d128-g8-tree32-256rows", 25, 1, 16, 2, 128, 32, [700], None, "tree", (128, 6)),
@@ -54,6 +54,13 @@ ATTN_CASES = [
     ("empty-history", 30, 2, 4, 2, 128, 5, [0, 0], 128, None, (128, 1)),
     ("short-lengths", 31, 5, 4, 2, 128, 3, [1, 31, 32, 33, 129], None, None, (128, 2)),
     ("d64-g3-n5-many-splits", 32, 1, 6, 2, 64, 5, [5000], None, None, (128, 40)),
+    # more than 64 rows per kv head: the shared-stage kernel, 2, 3 and 4 row
+    # tiles per wave, stages cut by the split end and by the history end
+    ("d64-g8-n16-wide", 33, 2, 16, 2, 64, 16, [3000, 130], None, None, (256, 12)),
+    ("d64-g12-tree16-wide3", 34, 1, 12, 1, 64, 16, [999], None, "tree", None),
+    ("d128-g5-tree32-wide3", 35, 1, 10, 2, 128, 32, [1234], None, "tree", (256, 5)),
+    ("d64-g16-n16-wide4", 36, 1, 16, 1, 64, 16, [777], None, "star", (384, 3)),
+    ("wide-short-lengths", 37, 5, 16, 2, 128, 11, [1, 127, 128, 129, 0], None, None, (128, 2)),
 ]
 
 
