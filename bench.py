@@ -527,6 +527,9 @@ def main():
         "device_step_us": {"median": float(np.median(step_dev_ms)) * 1e3,
                            "p10": float(np.percentile(step_dev_ms, 10)) * 1e3,
                            "p90": float(np.percentile(step_dev_ms, 90)) * 1e3},
+        "spec_attn_prefix_us": {"median": float(np.median(prefix_ms)) * 1e3,
+                                "p10": float(np.percentile(prefix_ms, 10)) * 1e3,
+                                "p90": float(np.percentile(prefix_ms, 90)) * 1e3},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": _traffic_per_launch(),
                      "kernel": "spec_attn_prefix (history pass)",

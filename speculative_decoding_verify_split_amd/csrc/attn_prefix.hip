@@ -603,12 +603,21 @@ __global__ __launch_bounds__(NW * KP * 64, 1) void attn_wide_kernel(
   for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
     for (int j = 0; j < MTW; ++j) oacc[nb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run[MTW], l_run[MTW];
+  // Running max (base 2), its negation as the exponent offset (0 while the
+  // row has seen no key), and the row sum as a 16-column MFMA accumulator
+  // of P against a ones operand: every lane then holds its row's full sum,
+  // taken over the same bf16-rounded p that multiply V.
+  float m_run[MTW], neg_m[MTW];
+  f32x4 lacc[MTW];
 #pragma unroll
   for (int j = 0; j < MTW; ++j) {
     m_run[j] = -INFINITY;
-    l_run[j] = 0.f;
+    neg_m[j] = 0.f;
+    lacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
 
   // One 32-key tile t; kt: the stage's K blocks of its two 16-key blocks,
   // vt: their V blocks.  Score layout, online softmax and P V product as
@@ -638,12 +647,12 @@ __global__ __launch_bounds__(NW * KP * 64, 1) void attn_wide_kernel(
     // LDS latency hides behind the scores and the softmax.
     s16x4 vlo[NB], vhi[NB];
     const uint32_t vbase = (uint32_t)(uintptr_t)(lds_cu8*)vt;
-    uint32_t va[4];
+    uint32_t vaddr[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) va[m] = vbase + vofs[m];
+    for (int m = 0; m < 4; ++m) vaddr[m] = vbase + vofs[m];
     static_for<NB>([&](auto nb) {
-      vlo[nb] = ds_read_tr16_asm<(nb / 4) * 1024>(va[nb % 4]);
-      vhi[nb] = ds_read_tr16_asm<(2 * HALVES + nb / 4) * 1024>(va[nb % 4]);
+      vlo[nb] = ds_read_tr16_asm<(nb / 4) * 1024>(vaddr[nb % 4]);
+      vhi[nb] = ds_read_tr16_asm<(2 * HALVES + nb / 4) * 1024>(vaddr[nb % 4]);
     });
 
     if ((t + 1) * KT > nkeys) {
@@ -658,11 +667,13 @@ __global__ __launch_bounds__(NW * KP * 64, 1) void attn_wide_kernel(
           }
     }
 
-    bf16x8 pf[MTW];
+    // Row tile by row tile: softmax, then its P V and row-sum MFMAs, which
+    // run on the matrix core while the next tile's softmax is on the VALU.
+    bf16x8 va[NB];
 #pragma unroll
     for (int j = 0; j < MTW; ++j) {
-      pf[j] = bf16x8{};
-      if (j > 0 && j >= tcnt) continue;
+      if (j > 0 && j >= tcnt) break;
+      bf16x8 pf;
       float mx = fmaxf(fmaxf(fmaxf(sacc[0][j][0], sacc[0][j][1]),
                              fmaxf(sacc[0][j][2], sacc[0][j][3])),
                        fmaxf(fmaxf(sacc[1][j][0], sacc[1][j][1]),
@@ -671,35 +682,31 @@ __global__ __launch_bounds__(NW * KP * 64, 1) void attn_wide_kernel(
       const float m_tile = mx * scale_log2;
       const bool raise = m_tile > m_run[j] + kRescaleSlack;
       if (__builtin_amdgcn_ballot_w64(raise)) {
+        // (a tile always holds a valid key, so m_tile and m_new are finite)
         const float m_new = raise ? m_tile : m_run[j];
         const float alpha = exp2_hw(m_run[j] - m_new);
-        l_run[j] *= alpha;
+        lacc[j] *= alpha;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) oacc[nb][j] *= alpha;
         m_run[j] = m_new;
+        neg_m[j] = -m_new;
       }
-      const float neg_m = (m_run[j] == -INFINITY) ? 0.f : -m_run[j];
-      float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float p = exp2_hw(fmaf(sacc[kb][j][v], scale_log2, neg_m));
-          ps += p;
-          pf[j][kb * 4 + v] = (__bf16)p;
-        }
-      l_run[j] += ps;
-    }
-
-    lds_wait();
+        for (int v = 0; v < 4; ++v)
+          pf[kb * 4 + v] = (__bf16)exp2_hw(fmaf(sacc[kb][j][v], scale_log2, neg_m[j]));
+      if (j == 0) {
+        lds_wait();
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const bf16x8 va = __builtin_bit_cast(
-          bf16x8, __builtin_shufflevector(vlo[nb], vhi[nb], 0, 1, 2, 3, 4, 5, 6, 7));
+        for (int nb = 0; nb < NB; ++nb)
+          va[nb] = __builtin_bit_cast(
+              bf16x8, __builtin_shufflevector(vlo[nb], vhi[nb], 0, 1, 2, 3, 4, 5, 6, 7));
+      }
 #pragma unroll
-      for (int j = 0; j < MTW; ++j)
-        if (j == 0 || j < tcnt)
-          oacc[nb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pf[j], oacc[nb][j], 0, 0, 0);
+      for (int nb = 0; nb < NB; ++nb)
+        oacc[nb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[nb], pf, oacc[nb][j], 0, 0, 0);
+      lacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf, lacc[j], 0, 0, 0);
     }
   };
 
@@ -726,7 +733,7 @@ __global__ __launch_bounds__(NW * KP * 64, 1) void attn_wide_kernel(
 
   float l_row[MTW];
 #pragma unroll
-  for (int j = 0; j < MTW; ++j) l_row[j] = row_sum4(l_run[j]);
+  for (int j = 0; j < MTW; ++j) l_row[j] = lacc[j][0];
 
   if constexpr (KP == 2) {
     // Phase 1 parks (max, sum, O) of its row tiles in LDS slots indexed by
