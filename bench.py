@@ -30,7 +30,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "verify steps/s + KV-stream HBM GB/s, 8B-shaped layer, 128K ctx, gamma=10"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "spec_attn_prefix_llama8b_traffic.json")
+# HBM bytes per history-kernel launch, from rocprofv3 FETCH_SIZE/WRITE_SIZE
+# passes on this workload (one file per workload).
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "spec_attn_prefix_%s_traffic.json")
 PREFIX_SRC = os.path.join(ROOT, "speculative_decoding_verify_split_amd", "csrc", "attn_prefix.hip")
 
 
@@ -69,11 +71,12 @@ def _src_sha():
     return hashlib.sha256(open(PREFIX_SRC, "rb").read()).hexdigest()
 
 
-def _traffic_per_launch():
+def _traffic_per_launch(workload):
     """HBM bytes per history-kernel launch from the committed counter
-    summary, or None if it is missing or was taken on other kernel source."""
+    summary of this workload, or None if it is missing or was taken on
+    other kernel source."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(TRAFFIC_FILE % workload))
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_sha256") != _src_sha():
@@ -531,7 +534,7 @@ def main():
                                 "p10": float(np.percentile(prefix_ms, 10)) * 1e3,
                                 "p90": float(np.percentile(prefix_ms, 90)) * 1e3},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": _traffic_per_launch(),
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": _traffic_per_launch(args.workload),
                      "kernel": "spec_attn_prefix (history pass)",
                      "algorithmic_bytes_per_launch": kv_bytes},
         "mean_n_accept": float(np.mean(n_acc)),
