@@ -224,7 +224,7 @@ __global__ __launch_bounds__(TPB) void stats_kernel(const float* __restrict__ z,
   const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
   // The decide kernel counts chunk arrivals per sequence; start from zero on
   // every call (the workspace is not assumed to be initialised).
-  if (c == 0 && r == 0 && threadIdx.x == 0) arrivals[b] = 0u;
+  if (c == 0 && r == 0 && threadIdx.x == 0) arrivals[(size_t)b * kArrivalStride] = 0u;
   const float* row;
   float* dst;
   if (r <= gamma) {
@@ -645,7 +645,7 @@ __global__ __launch_bounds__(TPB) void decide_kernel(
     __hip_atomic_store(wc, W.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(wc + 1, W.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    sh_arrived = __hip_atomic_fetch_add(arrivals + b, 1u, __ATOMIC_RELAXED,
+    sh_arrived = __hip_atomic_fetch_add(arrivals + (size_t)b * kArrivalStride, 1u, __ATOMIC_RELAXED,
                                         __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();

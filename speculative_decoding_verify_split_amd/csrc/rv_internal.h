@@ -90,6 +90,9 @@ constexpr int kDrawPer = 4;
 constexpr int kStatChunk = kVocabThreads * kStatPer;  // 4096
 constexpr int kPhatChunk = kVocabThreads * kPhatPer;  // 4096
 constexpr int kDrawChunk = kVocabThreads * kDrawPer;  // 1024
+// Words between two sequences' arrival counters: one 256-byte line each, so
+// the atomics of different sequences never queue on one cache line.
+constexpr int kArrivalStride = 64;
 constexpr int kMaxVocab = 1 << 22;
 constexpr int kMaxGamma = 63;  // one wave decides the first-reject cut
 
@@ -103,7 +106,7 @@ struct AcceptLayout {
                        //                      then each draft token's z and y
   size_t tstat;        // [B][gamma][cp]       chunk sums of the tail-adjusted p_hat
   size_t wsum;         // [B][cd][2]           residual and p_hat weight per chunk
-  size_t arrivals;     // [B] uint32           chunks done with their draw weight
+  size_t arrivals;     // [B][kArrivalStride] uint32: chunks done with their draw weight
   size_t words;        // total
 };
 AcceptLayout accept_layout(int B, int gamma, int V);

@@ -166,7 +166,7 @@ AcceptLayout accept_layout(int B, int gamma, int V) {
   L.wsum = off;
   off += round_words(Bz * L.cd * 2);
   L.arrivals = off;
-  off += round_words(Bz);
+  off += round_words(Bz * kArrivalStride);
   L.words = off;
   return L;
 }
