@@ -497,6 +497,8 @@ def main():
     prefix_s = float(np.mean(prefix_ms)) / 1e3
     attn_s = float(np.mean(attn_ms)) / 1e3
     achieved = kv_bytes / prefix_s / 1e9
+    logits_bytes = int(B * (2 * st.gamma + 1) * st.V * 4)
+    acc_s = float(np.mean(acc_ms)) / 1e3
     n_acc = st.n_accept.cpu().numpy()
 
     line = {
@@ -522,6 +524,11 @@ def main():
                    "spec_attn_block_merge", "parallelism": "single GPU"},
         "kv_stream_GBps": kv_bytes / attn_s / 1e9,
         "kv_stream_frac_of_peak": kv_bytes / attn_s / 1e9 / HBM_PEAK_GBPS,
+        # one read of z [B, gamma+1, V] and y [B, gamma, V] (fp32) over the
+        # acceptance pass's event time (a latency-bound pass at B = 1)
+        "logits_bytes": logits_bytes,
+        "logits_stream_GBps": logits_bytes / acc_s / 1e9,
+        "logits_stream_frac_of_peak": logits_bytes / acc_s / 1e9 / HBM_PEAK_GBPS,
         "kernels_us": {"spec_attn_prefix": prefix_s * 1e6,
                        ("spec_attn_block+lse_merge" if args.unfused else
                         "spec_attn_block_merge"): (attn_s - prefix_s) * 1e6,

@@ -262,7 +262,7 @@ def test_workspace_size_host_arithmetic(lib):
 @pytest.mark.parametrize("L,B,Hq,Hkv,n,d", [(131072, 1, 32, 8, 11, 128), (122880, 1, 64, 8, 11, 128),
                                             (131072, 8, 28, 4, 11, 128), (1048576, 1, 32, 8, 32, 128),
                                             (4096, 1, 8, 2, 5, 64), (0, 1, 8, 2, 5, 64),
-                                            (1, 3, 4, 4, 1, 128)])
+                                            (1, 3, 4, 4, 1, 128), (131072, 1, 4, 1, 11, 128)])
 def test_default_split_covers_the_sequence(lib, L, B, Hq, Hkv, n, d):
     split_len, S = rv.rv_prefix_default_split(L, B, Hq, Hkv, n, d)
     assert split_len % 128 == 0 and split_len > 0
@@ -271,3 +271,7 @@ def test_default_split_covers_the_sequence(lib, L, B, Hq, Hkv, n, d):
     if L == 131072 and B == 1 and Hq == 32:
         # 8 kv heads x 32 splits: one 4-wave workgroup per compute unit
         assert (split_len, S) == (4096, 32)
+    if L == 131072 and B == 1 and Hkv == 1:
+        # one kv head (a GPU's share under 8-way head parallelism): splits of
+        # 8 tiles per wave, 128 workgroups
+        assert (split_len, S) == (1024, 128)

@@ -53,6 +53,14 @@ CONFIGS = {
                                "8 sequences with 32K..128K caches, gamma=10",
                           B=8, Hq=28, Hkv=4, d=128, L=(32768, 131072), gamma=10,
                           V=152064, z_sigma=3.0, noise=0.5, T=1.0, etas=(0.5,), seed=400),
+    # One GPU's share of the 8B-shaped layer under 8-way head parallelism
+    # (one kv head and its 4 query heads per GPU); the acceptance pass stays
+    # whole, as every rank needs the same decision.
+    "llama8b_tp8": dict(desc="one GPU's share of the LLaMA-3.1-8B-shaped layer under 8-way "
+                             "head parallelism: 4/1 heads, d=128, 128K cache, gamma=10, "
+                             "vocab 128256",
+                        B=1, Hq=4, Hkv=1, d=128, L=131072, gamma=10, V=128256,
+                        z_sigma=3.0, noise=1.0, T=1.0, etas=(0.5,), seed=210),
     "tree1m": dict(desc="tree verify at 1M tokens: 32/8 heads, d=128, 32-node tree "
                         "of depth <= 6, chain 0..6",
                    B=1, Hq=32, Hkv=8, d=128, L=1048576, gamma=6, V=128256,
