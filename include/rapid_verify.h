@@ -109,6 +109,21 @@ rv_status rv_prefix_default_split(int64_t max_seq_len, int B, int Hq, int Hkv, i
                                   int d, int64_t* split_len, int* num_splits);
 
 /*
+ * The same choice from the batch's own lengths, for callers that know them
+ * on the host (a serving loop does: it manages the cache).  seq_lens_host is
+ * HOST int32 [B], each >= 0 (else RV_ERR_VALUE); num_cus is the device's
+ * compute-unit count.  Writes the shortest split_len (a multiple of 128, at
+ * least 1024) for which the splits that hold keys, Hkv * sum_b
+ * ceil(L_b / split_len), all fit on the compute units at once, and
+ * S = ceil(max_b L_b / split_len); when even one split per sequence does not
+ * fit, one split per sequence.  A ragged batch then keeps every compute unit
+ * busy, where a split chosen from the longest sequence alone leaves the units
+ * of the short sequences' empty splits idle.  Pure host arithmetic.
+ */
+rv_status rv_prefix_balanced_split(const int32_t* seq_lens_host, int B, int Hq, int Hkv, int n,
+                                   int d, int num_cus, int64_t* split_len, int* num_splits);
+
+/*
  * spec_attn_prefix -- unmasked attention of every block row over the history
  * cache, one normalised partial result per split (LongSpec summary, section
  * 2.3: the history part needs no mask; the partials are merged by

@@ -16,6 +16,7 @@ from .rapid_verify import (  # noqa: F401
     rapid_accept,
     rapid_accept_ex,
     rapid_accept_workspace_size,
+    rv_prefix_balanced_split,
     rv_prefix_default_split,
     rv_status_string,
     rv_version,

@@ -72,6 +72,90 @@ __device__ __forceinline__ float row_sum4(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Which (sequence b, kv head, split s) this workgroup takes.  The triples
+// whose split holds keys are numbered in (b, kv head, s) order and item w
+// goes to the workgroup of linear index w.  The hardware hands workgroups to
+// the 8 XCDs round-robin by linear index, so the busy workgroups spread
+// evenly over the XCDs and their compute units whatever the batch's lengths
+// (with the plain (s, kv head, b) grid a ragged batch can put more busy
+// workgroups on one XCD than it has units).  Workgroups past the last item
+// take the empty slots, in the same order, and write their empty partials.
+// Slot s of sequence b always covers keys [s * split_len, (s+1) * split_len).
+struct SplitItem {
+  int b, kvh, s;
+};
+
+__device__ __forceinline__ int64_t wave_incl_scan64(int64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t t = __shfl_up(v, d, 64);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+__device__ SplitItem split_item(const int32_t* __restrict__ seq_lens, int B, int Hkv, int S,
+                                int64_t L_max, int64_t split_len) {
+  // One sequence: the plain grid position (its busy splits are the first of
+  // every kv head's row of S, so they already spread over the XCDs), with
+  // no length load in front of the workgroup's first request.
+  if (B == 1) return SplitItem{0, (int)blockIdx.y, (int)blockIdx.x};
+  const int lane = threadIdx.x & 63;
+  const int64_t w =
+      blockIdx.x + (int64_t)S * (blockIdx.y + (int64_t)Hkv * (int64_t)blockIdx.z);
+  // splits of sequence b that hold keys (at most S)
+  auto busy = [&](int b) -> int {
+    int64_t L = seq_lens[b];
+    L = L < 0 ? 0 : (L > L_max ? L_max : L);
+    const int64_t p = (L + split_len - 1) / split_len;
+    return (int)(p < S ? p : S);
+  };
+  // number of busy triples (the first 64 sequences' counts stay in a
+  // register for the search below: one load round trip for B <= 64)
+  const int p_first = lane < B ? busy(lane) : 0;
+  int64_t N = __shfl(wave_incl_scan64(p_first), 63, 64);
+  for (int b0 = 64; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    const int64_t c = b < B ? (int64_t)busy(b) : 0;
+    N += __shfl(wave_incl_scan64(c), 63, 64);
+  }
+  N *= Hkv;
+  // item w among the busy triples, or w - N among the empty slots: find the
+  // sequence whose running count passes the target, then (kv head, s) in it
+  const bool empty = w >= N;
+  const int64_t target = empty ? w - N : w;
+  int64_t base = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    const int p = b0 == 0 ? p_first : (b < B ? busy(b) : 0);
+    const int per = b < B ? (empty ? S - p : p) : 0;  // slots per kv head
+    const int64_t c = (int64_t)per * Hkv;
+    const int64_t incl = base + wave_incl_scan64(c);
+    const uint64_t hit = __ballot(b < B && incl > target);
+    if (hit != 0) {
+      const int l = __ffsll((unsigned long long)hit) - 1;
+      const int64_t excl = __shfl(incl - c, l, 64);
+      const int pl = __shfl(p, l, 64);
+      const int perl = __shfl(per, l, 64);
+      const int64_t r = target - excl;  // < perl * Hkv
+      const int kvh = (int)(r / perl);
+      const int j = (int)(r - (int64_t)kvh * perl);
+      // (uniform across the wave: keep it in scalar registers)
+      SplitItem it;
+      it.b = __builtin_amdgcn_readfirstlane(b0 + l);
+      it.kvh = __builtin_amdgcn_readfirstlane(kvh);
+      it.s = __builtin_amdgcn_readfirstlane(empty ? pl + j : j);
+      return it;
+    }
+    base = __shfl(incl, 63, 64);
+  }
+  // unreachable for a grid of S * Hkv * B workgroups (every slot is either
+  // busy or empty); keep a defined answer
+  SplitItem it{B - 1, Hkv - 1, S - 1};
+  return it;
+}
+
 template <int D>
 struct PrefixGeom {
   static constexpr int KS = D / 32;             // MFMA k-steps over the head dim
@@ -114,9 +198,10 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
   __shared__ float m_lds[NW][MT * 16];
   __shared__ float l_lds[NW][MT * 16];
 
-  const int s = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  const SplitItem item = split_item(seq_lens, (int)gridDim.z, Hkv, S, L_max, split_len);
+  const int s = item.s;
+  const int kvh = item.kvh;
+  const int b = item.b;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int lr = lane & 15;
@@ -509,9 +594,10 @@ __global__ __launch_bounds__(NW * KP * 64, 1) void attn_wide_kernel(
   static_assert(TPS % KP == 0, "each phase takes whole tiles of a stage");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[NBUF * STAGE];
 
-  const int s = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  const SplitItem item = split_item(seq_lens, (int)gridDim.z, Hkv, S, L_max, split_len);
+  const int s = item.s;
+  const int kvh = item.kvh;
+  const int b = item.b;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rgw = wave % NW;    // row-tile owner

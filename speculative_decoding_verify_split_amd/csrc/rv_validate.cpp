@@ -234,4 +234,46 @@ rv_status rv_prefix_default_split(int64_t max_seq_len, int B, int Hq, int Hkv, i
   return RV_OK;
 }
 
+rv_status rv_prefix_balanced_split(const int32_t* seq_lens_host, int B, int Hq, int Hkv, int n,
+                                   int d, int num_cus, int64_t* split_len, int* num_splits) {
+  if (!seq_lens_host || !split_len || !num_splits) return RV_ERR_NULL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || n < 1 || Hq % Hkv != 0 || num_cus < 1) return RV_ERR_SHAPE;
+  if (B > 65535) return RV_ERR_UNSUPPORTED;
+  if (n > RV_MAX_BLOCK_ROWS || (int64_t)(Hq / Hkv) * n > RV_MAX_GROUP_ROWS)
+    return RV_ERR_UNSUPPORTED;
+  (void)d;
+  int64_t max_len = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t L = seq_lens_host[b];
+    if (L < 0) return RV_ERR_VALUE;
+    if (L > max_len) max_len = L;
+  }
+  const int64_t q = rv::kSplitQuantum;
+  const int64_t min_len = 8 * q;  // at least 8 tiles per wave
+  // Workgroups that get keys with splits of m quanta: Hkv * sum_b ceil(L_b / (m q)).
+  auto busy = [&](int64_t m) {
+    int64_t c = 0;
+    for (int b = 0; b < B; ++b) c += (seq_lens_host[b] + m * q - 1) / (m * q);
+    return c * Hkv;
+  };
+  int64_t lo = min_len / q;
+  int64_t hi = (max_len + q - 1) / q;  // one split per sequence
+  if (hi < lo) hi = lo;
+  if (busy(hi) <= num_cus) {
+    // smallest split whose non-empty workgroups fit on the compute units at once
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo) / 2;
+      if (busy(mid) <= num_cus) hi = mid;
+      else lo = mid + 1;
+    }
+  }
+  const int64_t len = hi * q;
+  int64_t S = (max_len + len - 1) / len;
+  if (S < 1) S = 1;
+  if (S > 65535) return RV_ERR_UNSUPPORTED;
+  *split_len = len;
+  *num_splits = (int)S;
+  return RV_OK;
+}
+
 }  // extern "C"

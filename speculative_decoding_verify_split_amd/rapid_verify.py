@@ -43,6 +43,9 @@ def load_library():
     lib.rv_prefix_default_split.argtypes = [i64, i32, i32, i32, i32, i32,
                                             ctypes.POINTER(i64), ctypes.POINTER(i32)]
     lib.rv_prefix_default_split.restype = i32
+    lib.rv_prefix_balanced_split.argtypes = [vp, i32, i32, i32, i32, i32, i32,
+                                             ctypes.POINTER(i64), ctypes.POINTER(i32)]
+    lib.rv_prefix_balanced_split.restype = i32
     lib.spec_attn_prefix.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i64, f32, i64,
                                      i32, vp, vp, vp]
     lib.spec_attn_prefix.restype = i32
@@ -118,6 +121,28 @@ def rv_prefix_default_split(max_seq_len, B, Hq, Hkv, n, d):
     _check(load_library().rv_prefix_default_split(int(max_seq_len), B, Hq, Hkv, n, d,
                                                   ctypes.byref(sl), ctypes.byref(ns)),
            "rv_prefix_default_split")
+    return sl.value, ns.value
+
+
+def rv_prefix_balanced_split(seq_lens, Hq, Hkv, n, d, num_cus=None):
+    """Split choice from the batch's host lengths (any int sequence or array)
+    -> (split_len, num_splits).  num_cus defaults to the current device's
+    compute-unit count."""
+    import numpy as np
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int64))
+    if lens.ndim != 1 or lens.size < 1:
+        raise ValueError("seq_lens must be a non-empty 1-D sequence")
+    if (lens < 0).any() or (lens > 0x7FFFFFFF).any():
+        raise ValueError("seq_lens must lie in [0, 2^31)")
+    lens = lens.astype(np.int32)
+    if num_cus is None:
+        import torch
+        num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    sl = ctypes.c_int64()
+    ns = ctypes.c_int()
+    _check(load_library().rv_prefix_balanced_split(
+        lens.ctypes.data_as(ctypes.c_void_p), int(lens.size), Hq, Hkv, n, d, int(num_cus),
+        ctypes.byref(sl), ctypes.byref(ns)), "rv_prefix_balanced_split")
     return sl.value, ns.value
 
 

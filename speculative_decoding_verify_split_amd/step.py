@@ -27,7 +27,9 @@ class VerifyStep:
     attn: a workloads.AttnInputs-like object (numpy uint16 bf16 bits), or
           None for the vocabulary pass only;
     vocab: a workloads.VocabInputs-like object, or None for attention only.
-    split: (split_len, num_splits) or None for the library's default.
+    split: (split_len, num_splits), or None to plan it from the batch's host
+           lengths (rv_prefix_balanced_split; for one sequence this is the
+           same as rv_prefix_default_split).
     """
 
     def __init__(self, attn, vocab=None, split=None, want_ratio=True, want_p_hat=False,
@@ -50,7 +52,7 @@ class VerifyStep:
             self.v_blk = bf16_to_device(attn.v_blk, device)
             self.seq_lens = to_device(attn.seq_lens.astype(np.int32), device)
             if split is None:
-                split = rv.rv_prefix_default_split(self.max_seq_len, B, Hq, Hkv, n, d)
+                split = rv.rv_prefix_balanced_split(attn.seq_lens, Hq, Hkv, n, d)
             self.split_len, self.num_splits = int(split[0]), int(split[1])
             S = self.num_splits
             self.o_part = torch.empty((B, Hq, n, S, d), dtype=f32, device=device)

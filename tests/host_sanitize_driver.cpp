@@ -57,6 +57,31 @@ int main() {
             ++calls;
           }
         }
+  // the balanced split, from host lengths
+  {
+    const int32_t lens_a[] = {48330, 92427, 125481, 53507, 127380, 42193, 70031, 103537};
+    const int32_t lens_b[] = {INT32_MAX, 0, 1, INT32_MAX, 128};
+    const int32_t lens_c[] = {0, 0, 0};
+    const int32_t lens_d[] = {5, -1, 7};
+    struct { const int32_t* p; int B; } sets[] = {{lens_a, 8}, {lens_b, 5}, {lens_c, 3},
+                                                  {lens_d, 3}, {nullptr, 2}};
+    for (auto set : sets)
+      for (int Hkv : {1, 4, 8, 0, INT_MAX})
+        for (int cus : {0, 1, 256, INT_MAX}) {
+          int64_t sl = 0;
+          int ns = 0;
+          const rv_status st =
+              rv_prefix_balanced_split(set.p, set.B, Hkv > INT_MAX / 4 ? Hkv : 4 * Hkv, Hkv, 11,
+                                       128, cus, &sl, &ns);
+          if (st == RV_OK) {
+            int64_t mx = 0;
+            for (int b = 0; b < set.B; ++b) mx = set.p[b] > mx ? set.p[b] : mx;
+            expect(sl > 0 && sl % kSplitQuantum == 0 && ns >= 1 && (mx + sl - 1) / sl <= ns,
+                   "balanced split covers");
+          }
+          ++calls;
+        }
+  }
   for (float sc : scales) {
     check_prefix(P, P, P, I, 4096, 1, 8, 2, 5, 64, 4096, sc, 1024, 4, F, F);
     ++calls;

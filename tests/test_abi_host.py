@@ -41,7 +41,7 @@ def test_header_declares_the_four_calls():
               "spec_attn_block_merge",
               "spec_attn_window", "spec_attn_window_workspace_size",
               "rapid_accept", "rapid_accept_ex", "rapid_accept_workspace_size",
-              "rv_status_string", "rv_prefix_default_split"):
+              "rv_status_string", "rv_prefix_default_split", "rv_prefix_balanced_split"):
         assert n in names
 
 
@@ -275,3 +275,63 @@ def test_default_split_covers_the_sequence(lib, L, B, Hq, Hkv, n, d):
         # one kv head (a GPU's share under 8-way head parallelism): splits of
         # 8 tiles per wave, 128 workgroups
         assert (split_len, S) == (1024, 128)
+
+
+def _balanced_c(lib, lens, Hq=28, Hkv=4, n=11, d=128, ncu=256):
+    arr = (ctypes.c_int32 * len(lens))(*lens)
+    sl, ns = ctypes.c_int64(), ctypes.c_int()
+    st = lib.rv_prefix_balanced_split(arr, len(lens), Hq, Hkv, n, d, ncu, ctypes.byref(sl),
+                                      ctypes.byref(ns))
+    return st, sl.value, ns.value
+
+
+def _busy(lens, Hkv, split_len):
+    return Hkv * sum((L + split_len - 1) // split_len for L in lens)
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv,n", [
+    ([48330, 92427, 125481, 53507, 127380, 42193, 70031, 103537], 28, 4, 11),
+    ([131072], 32, 8, 11), ([122880], 64, 8, 11), ([1048576], 32, 8, 32), ([4096], 8, 2, 5),
+    ([1, 31, 32, 33, 129], 4, 2, 3), ([0, 0], 4, 2, 5), ([131072] * 8, 28, 4, 11)])
+def test_balanced_split_fills_the_units_with_the_shortest_split(lib, lens, Hq, Hkv, n):
+    """The balanced split is the shortest multiple of 128 (>= 1024) whose
+    non-empty splits fit on 256 compute units, and S covers every sequence."""
+    st, split_len, S = _balanced_c(lib, lens, Hq, Hkv, n)
+    assert st == RV_OK
+    assert split_len % 128 == 0 and split_len >= 1024
+    assert S >= 1 and S * split_len >= max(lens)
+    assert (S - 1) * split_len < max(max(lens), 1)
+    assert _busy(lens, Hkv, split_len) <= 256
+    if split_len > 1024:
+        assert _busy(lens, Hkv, split_len - 128) > 256
+    # one sequence: the same choice as the default split
+    if len(lens) == 1:
+        assert (split_len, S) == rv.rv_prefix_default_split(lens[0], 1, Hq, Hkv, n, 128)
+    # the Python binding agrees with the C call
+    assert rv.rv_prefix_balanced_split(lens, Hq, Hkv, n, 128, num_cus=256) == (split_len, S)
+
+
+def test_balanced_split_ragged_batch_is_shorter_than_the_default(lib):
+    lens = [48330, 92427, 125481, 53507, 127380, 42193, 70031, 103537]
+    st, split_len, S = _balanced_c(lib, lens)
+    dl, dS = rv.rv_prefix_default_split(max(lens), len(lens), 28, 4, 11, 128)
+    assert st == RV_OK and split_len < dl
+    # the default leaves a quarter of the units without keys; the balanced split fills them
+    assert _busy(lens, 4, dl) < 200 <= _busy(lens, 4, split_len) <= 256
+
+
+def test_balanced_split_too_many_sequences_takes_one_split_each(lib):
+    lens = [5000] * 100  # 100 sequences x 4 kv heads > 256 units
+    st, split_len, S = _balanced_c(lib, lens)
+    assert st == RV_OK and S == 1 and split_len >= 5000
+
+
+def test_balanced_split_rejects_bad_arguments(lib):
+    assert _balanced_c(lib, [100, -1])[0] == RV_ERR_VALUE
+    assert _balanced_c(lib, [100], ncu=0)[0] == RV_ERR_SHAPE
+    assert _balanced_c(lib, [100], Hq=6, Hkv=4)[0] == RV_ERR_SHAPE
+    sl, ns = ctypes.c_int64(), ctypes.c_int()
+    assert lib.rv_prefix_balanced_split(None, 1, 4, 2, 5, 128, 256, ctypes.byref(sl),
+                                        ctypes.byref(ns)) == RV_ERR_NULL
+    with pytest.raises(ValueError):
+        rv.rv_prefix_balanced_split([100, -5], 4, 2, 5, 128, num_cus=256)
