@@ -100,11 +100,23 @@ def test_attention_small(case):
     assert np.abs(res[True][1] - res[False][1]).max() <= 1e-4
 
 
-def test_prefix_and_block_partials_match_split_oracle():
+# Batches of more than 64 sequences take the multi-chunk path of the history
+# kernels' workgroup-to-slot numbering; lengths include empty sequences.
+_B70_LENS = [int(x) for x in np.random.default_rng(41).integers(0, 700, 70)]
+_B70_LENS[5] = _B70_LENS[67] = 0
+PARTIAL_CASES = [
+    ATTN_CASES[0],
+    ("b70-narrow-d64", 42, 70, 4, 2, 64, 3, _B70_LENS, None, None, (128, 6)),
+    ("b70-wide-d64", 43, 70, 16, 2, 64, 11, _B70_LENS, None, None, (256, 3)),
+]
+
+
+@pytest.mark.parametrize("case", PARTIAL_CASES, ids=[c[0] for c in PARTIAL_CASES])
+def test_prefix_and_block_partials_match_split_oracle(case):
     """The history splits and the masked block part separately, against the
     oracle evaluated on exactly those key sets."""
-    ai, split = _make_case(ATTN_CASES[0])
-    announce("partials d128-g4-n11-ragged")
+    ai, split = _make_case(case)
+    announce("partials %s B=%d" % (case[0], ai.q.shape[0]))
     st = VerifyStep(ai, None, split=split)
     st.attention()
     torch.cuda.synchronize()
