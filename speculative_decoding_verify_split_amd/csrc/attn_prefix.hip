@@ -4,8 +4,11 @@
 // to a plain fast attention pass whose result is later merged by log-sum-exp).
 //
 // Work decomposition (gfx950, 64-wide waves):
-//   grid  = (split s, kv-head, sequence b).  A workgroup owns one split of
-//   one (b, kv-head).  The G = Hq/Hkv query heads of that kv-head share every
+//   grid  = S x Hkv x B workgroups, one per (split s, kv-head, sequence b)
+//   slot; for one sequence workgroup (s, kv-head) is its grid position, for
+//   a batch the slots that hold keys are numbered so that they spread evenly
+//   over the XCDs (split_item).  A workgroup owns one split of one
+//   (b, kv-head).  The G = Hq/Hkv query heads of that kv-head share every
 //   K/V byte, so their G*n rows are stacked into 16-row MFMA tiles, and one
 //   workgroup takes all of them, so every byte of the split is read once.
 //   Up to 4 row tiles (64 rows): attn_kernel below, 4 waves, wave w streams
