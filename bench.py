@@ -20,6 +20,7 @@ oracle timed on the host as a reported baseline.
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -67,8 +68,19 @@ class _HipEvents:
         self.ev = []
 
 
+def kernel_source_digest(path=PREFIX_SRC):
+    """sha256 of the history kernels' source with comments and whitespace
+    removed: a counter record stays valid across comment edits and is
+    dropped by any change to the code itself."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    text = re.sub(r"\s+", "", text)
+    return hashlib.sha256(text.encode()).hexdigest()
+
+
 def _src_sha():
-    return hashlib.sha256(open(PREFIX_SRC, "rb").read()).hexdigest()
+    return kernel_source_digest()
 
 
 def _traffic_per_launch(workload):
@@ -79,7 +91,7 @@ def _traffic_per_launch(workload):
         rec = json.load(open(TRAFFIC_FILE % workload))
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != _src_sha():
+    if rec.get("kernel_code_sha256") != _src_sha():
         return None
     return rec.get("hbm_bytes_per_launch")
 
