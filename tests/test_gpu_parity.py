@@ -362,6 +362,33 @@ def test_accept_bad_draft_id_sentinel():
     assert not res["errors"]
 
 
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+def test_accept_nonfinite_logits_stay_in_range(flags):
+    """Non-finite logits give unspecified tokens, never an out-of-range one:
+    every drawn id lies in [0, V), accepted prefixes are the drafts, the
+    rest is -1.  (Every address in the pass comes from loop indices and the
+    validated draft ids; no float value indexes memory.)"""
+    V, g = 5000, 4
+    vi = make_vocab(49, B=5, gamma=g, V=V, z_sigma=3.0, noise=1.0, T=1.0, eta=0.5)
+    vi.z[0] = np.nan                        # all-NaN target
+    vi.z[1, :, ::97] = np.inf               # +inf target entries
+    vi.y[1, :, ::89] = -np.inf              # -inf draft entries
+    vi.y[2] = np.nan                        # all-NaN draft
+    vi.z[3, :, 17] = np.inf                 # one +inf per target row
+    vi.y[3, :, 17] = np.inf
+    vi.z[4] = -np.inf                       # all -inf target
+    announce("rapid_accept non-finite logits, flags %d" % flags)
+    st = _run_accept(vi, p_hat=False, flags=flags)
+    n_g = st.n_accept.cpu().numpy()
+    tok = st.out_tokens.cpu().numpy()
+    for b in range(5):
+        n = int(n_g[b])
+        assert 0 <= n <= g, (b, n)
+        assert np.array_equal(tok[b, :n], vi.draft[b, :n])
+        assert 0 <= tok[b, n] < V, (b, tok[b])
+        assert np.all(tok[b, n + 1:] == -1)
+
+
 def test_step_is_bit_deterministic():
     ai = config_attention("tiny")
     vi = config_vocab("tiny")
