@@ -498,6 +498,25 @@ def main():
         graph = {"steps_per_s": K / g_el, "ms_per_step": g_el * 1e3 / K,
                  "note": "same K steps replayed from HIP graphs (one per rotated copy), "
                          "after the timed eager region"}
+        # The R rotated steps captured back to back in one graph: the graph
+        # launch is paid once per R steps, as in a serving loop that captures
+        # several steps (or a whole model) at once.
+        gm = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gm):
+            for i in range(R):
+                step(i)
+        reps = max(1, K // R)
+        for _ in range(max(1, args.warmup // R)):
+            gm.replay()
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        for _ in range(reps):
+            gm.replay()
+        torch.cuda.synchronize()
+        gm_el = time.perf_counter() - g0
+        graph["multi_step"] = {"steps_per_s": reps * R / gm_el,
+                               "ms_per_step": gm_el * 1e3 / (reps * R),
+                               "steps_per_graph": R, "replays": reps}
 
     prefix_ms = [hev.elapsed_ms(4 * i, 4 * i + 1) for i in range(K)]
     attn_ms = [hev.elapsed_ms(4 * i, 4 * i + 2) for i in range(K)]
