@@ -395,8 +395,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only (no multi-GPU path); "
-              "run with --gpus 1", file=sys.stderr)
+        print("bench.py: rapid_verify runs on one GPU; there is no multi-GPU path to "
+              "measure (how the step would shard is described, not built). "
+              "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
