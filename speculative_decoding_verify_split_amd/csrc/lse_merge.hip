@@ -7,10 +7,14 @@
 // merged alone, as for a drafter's cross-attention over the target cache.
 //
 // One 4-wave workgroup per output row; the row's S partials are contiguous
-// ([row][S][d]).  Wave w folds splits w, w + 4, ... (each step one 4*d-byte
-// line read by all 64 lanes, four steps in flight), the four wave sums are
+// ([row][S][d]).  Wave w folds splits w, w + 4, ... in ascending order (each
+// split one 4*d-byte line read by all 64 lanes), the four wave sums are
 // added in wave order and the block partial last, so the result is
-// bit-deterministic.
+// bit-deterministic.  A wave's partials are loaded in batches of FB with
+// every load of a batch in flight at once: the loads do not depend on the
+// row's maximum, so a row costs ceil(S / (4 FB)) memory round trips.  The
+// launch picks FB = 8, 16 or 32 from S (one round trip up to S = 128) and
+// so keeps the registers of short folds low.
 //
 // spec_attn_block_merge does the same with the block partial computed in
 // place: wave 0 of each row's workgroup also runs the row's masked block
@@ -24,7 +28,56 @@
 namespace rv {
 namespace {
 
-template <int D>
+// One wave's share of a row's history partials, s = wave, wave + NWV, ...,
+// batch b holding the FB of them from s = wave + b FB NWV.  op points at
+// this lane's PER columns of the row's first partial.
+template <int D, int NWV, int FB>
+struct PartialFold {
+  static constexpr int PER = D / 64;
+  float val[FB][PER];
+  float lse[FB];
+
+  // Issues every load of batch b; partials past S read as empty.
+  __device__ __forceinline__ void load(const float* __restrict__ op,
+                                       const float* __restrict__ lp, int S, int wave, int b) {
+#pragma unroll
+    for (int j = 0; j < FB; ++j) {
+      const int s = wave + (b * FB + j) * NWV;
+      lse[j] = s < S ? lp[s] : -INFINITY;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) val[j][e] = s < S ? op[(size_t)s * D + e] : 0.f;
+    }
+  }
+
+  // acc += a_s O_s and wsum += a_s over batch b in ascending s, with
+  // a_s = exp(LSE_s - M) (0 for an empty split, whose O_s is 0).
+  __device__ __forceinline__ void add(int S, int wave, int b, float M, float (&acc)[PER],
+                                      float& wsum) const {
+#pragma unroll
+    for (int j = 0; j < FB; ++j) {
+      const int s = wave + (b * FB + j) * NWV;
+      if (s < S) {
+        const float a = exp2_hw((lse[j] - M) * kLog2e);
+        wsum += a;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] = fmaf(a, val[j][e], acc[e]);
+      }
+    }
+  }
+
+  // Every batch of this wave, the first already loaded.
+  __device__ __forceinline__ void fold(const float* __restrict__ op,
+                                       const float* __restrict__ lp, int S, int wave, float M,
+                                       float (&acc)[PER], float& wsum) {
+    add(S, wave, 0, M, acc, wsum);
+    for (int b = 1; wave + b * FB * NWV < S; ++b) {
+      load(op, lp, S, wave, b);
+      add(S, wave, b, M, acc, wsum);
+    }
+  }
+};
+
+template <int D, int FB>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_part,
                                                     const float* __restrict__ lse_part, int S,
                                                     const float* __restrict__ o_blk,
@@ -41,15 +94,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
   const float* lp = lse_part + (size_t)row * S;
   const float* op = o_part + (size_t)row * S * D + lane * PER;
   // The first batch of this wave's partials is requested before the max is
-  // known (empty splits hold zeros), so the row costs one memory round trip.
-  constexpr int FIRST = 8;
-  float val0[FIRST][PER];
-#pragma unroll
-  for (int j = 0; j < FIRST; ++j) {
-    const int s = wave + j * NWV;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) val0[j][e] = (s < S) ? op[(size_t)s * D + e] : 0.f;
-  }
+  // known (empty splits hold zeros).
+  PartialFold<D, NWV, FB> pf;
+  pf.load(op, lp, S, wave, 0);
   float M = -INFINITY;
   for (int s = lane; s < S; s += 64) M = fmaxf(M, lp[s]);
   M = wave_max(M);
@@ -59,41 +106,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   float wsum = 0.f;
-  if (M != -INFINITY) {
-    // wave w folds splits w, w + 4, w + 8, ... in ascending order
-#pragma unroll
-    for (int j = 0; j < FIRST; ++j) {
-      const int s = wave + j * NWV;
-      if (s < S) {
-        const float a = exp2_hw((lp[s] - M) * kLog2e);
-        wsum += a;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(a, val0[j][e], acc[e]);
-      }
-    }
-    int s = wave + FIRST * NWV;
-    for (; s + 3 * NWV < S; s += 4 * NWV) {
-      float a[4], val[4][PER];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        a[j] = exp2_hw((lp[s + j * NWV] - M) * kLog2e);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) val[j][e] = op[(size_t)(s + j * NWV) * D + e];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        wsum += a[j];
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(a[j], val[j][e], acc[e]);
-      }
-    }
-    for (; s < S; s += NWV) {
-      const float a = exp2_hw((lp[s] - M) * kLog2e);
-      wsum += a;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = fmaf(a, op[(size_t)s * D + e], acc[e]);
-    }
-  }
+  if (M != -INFINITY) pf.fold(op, lp, S, wave, M, acc, wsum);
 #pragma unroll
   for (int e = 0; e < PER; ++e) part[wave][lane * PER + e] = acc[e];
   if (lane == 0) wpart[wave] = wsum;
@@ -126,7 +139,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
 // their own maximum Ms; the final combine rescales the history sums by
 // exp(Ms - M) and the block partial by exp(LSE_blk - M), M the larger of the
 // two, which is the same log-sum-exp merge.
-template <int D>
+template <int D, int FB>
 __global__ __launch_bounds__(256) void block_merge_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kb,
     const uint16_t* __restrict__ vb, BlockMask mask, int Hq, int G, int n, float scale_log2,
@@ -145,14 +158,8 @@ __global__ __launch_bounds__(256) void block_merge_kernel(
   const int h = bh - b * Hq;
   const float* lp = lse_part + (size_t)row * S;
   const float* op = o_part + (size_t)row * S * D + lane * PER;
-  constexpr int FIRST = 8;
-  float val0[FIRST][PER];
-#pragma unroll
-  for (int j = 0; j < FIRST; ++j) {
-    const int s = wave + j * NWV;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) val0[j][e] = (s < S) ? op[(size_t)s * D + e] : 0.f;
-  }
+  PartialFold<D, NWV, FB> pf;
+  pf.load(op, lp, S, wave, 0);
   float ob[PER], lb2 = 0.f;
   if (wave == 0) {
     const size_t kv0 = ((size_t)b * (Hq / G) + h / G) * n * D;
@@ -166,40 +173,7 @@ __global__ __launch_bounds__(256) void block_merge_kernel(
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
   float wsum = 0.f;
-  if (Ms != -INFINITY) {
-#pragma unroll
-    for (int j = 0; j < FIRST; ++j) {
-      const int s = wave + j * NWV;
-      if (s < S) {
-        const float a = exp2_hw((lp[s] - Ms) * kLog2e);
-        wsum += a;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(a, val0[j][e], acc[e]);
-      }
-    }
-    int s = wave + FIRST * NWV;
-    for (; s + 3 * NWV < S; s += 4 * NWV) {
-      float a[4], val[4][PER];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        a[j] = exp2_hw((lp[s + j * NWV] - Ms) * kLog2e);
-#pragma unroll
-        for (int e = 0; e < PER; ++e) val[j][e] = op[(size_t)(s + j * NWV) * D + e];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        wsum += a[j];
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(a[j], val[j][e], acc[e]);
-      }
-    }
-    for (; s < S; s += NWV) {
-      const float a = exp2_hw((lp[s] - Ms) * kLog2e);
-      wsum += a;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) acc[e] = fmaf(a, op[(size_t)s * D + e], acc[e]);
-    }
-  }
+  if (Ms != -INFINITY) pf.fold(op, lp, S, wave, Ms, acc, wsum);
 #pragma unroll
   for (int e = 0; e < PER; ++e) part[wave][lane * PER + e] = acc[e];
   if (lane == 0) wpart[wave] = wsum;
@@ -221,6 +195,25 @@ __global__ __launch_bounds__(256) void block_merge_kernel(
   if (lse_out != nullptr && lane == 0) lse_out[row] = M + log2_hw(tot) * kLn2;
 }
 
+// Partials per wave per batch of loads: 4 waves fold a row's S partials.
+int fold_batch(int S) { return S <= 4 * 8 ? 8 : (S <= 4 * 16 ? 16 : 32); }
+
+template <int D, int FB>
+void launch_block_merge(dim3 grid, hipStream_t s, const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const BlockMask& mask, int Hq, int G, int n,
+                        float scale_log2, const float* o_part, const float* lse_part, int S,
+                        uint16_t* out, float* lse_out) {
+  hipLaunchKernelGGL((block_merge_kernel<D, FB>), grid, dim3(256), 0, s, q, k, v, mask, Hq, G,
+                     n, scale_log2, o_part, lse_part, S, out, lse_out);
+}
+
+template <int D, int FB>
+void launch_merge(dim3 grid, hipStream_t s, const float* o_part, const float* lse_part, int S,
+                  const float* o_blk, const float* lse_blk, uint16_t* out, float* lse_out) {
+  hipLaunchKernelGGL((merge_kernel<D, FB>), grid, dim3(256), 0, s, o_part, lse_part, S, o_blk,
+                     lse_blk, out, lse_out);
+}
+
 }  // namespace
 }  // namespace rv
 
@@ -240,12 +233,19 @@ extern "C" rv_status spec_attn_block_merge(const void* q, const void* k_blk, con
   const uint16_t* kk = static_cast<const uint16_t*>(k_blk);
   const uint16_t* vv = static_cast<const uint16_t*>(v_blk);
   uint16_t* o16 = static_cast<uint16_t*>(out);
-  if (d == 64)
-    hipLaunchKernelGGL((rv::block_merge_kernel<64>), grid, dim3(256), 0, s, qq, kk, vv, mask, Hq,
-                       Hq / Hkv, n, scale_log2, o_part, lse_part, S, o16, lse_out);
-  else
-    hipLaunchKernelGGL((rv::block_merge_kernel<128>), grid, dim3(256), 0, s, qq, kk, vv, mask, Hq,
-                       Hq / Hkv, n, scale_log2, o_part, lse_part, S, o16, lse_out);
+  const int G = Hq / Hkv;
+  const int fb = rv::fold_batch(S);
+#define RV_BM_CASE(DD, FB)                                                                   \
+  if (d == DD && fb == FB)                                                                   \
+    rv::launch_block_merge<DD, FB>(grid, s, qq, kk, vv, mask, Hq, G, n, scale_log2, o_part, \
+                                   lse_part, S, o16, lse_out);
+  RV_BM_CASE(64, 8)
+  else RV_BM_CASE(64, 16)
+  else RV_BM_CASE(64, 32)
+  else RV_BM_CASE(128, 8)
+  else RV_BM_CASE(128, 16)
+  else RV_BM_CASE(128, 32)
+#undef RV_BM_CASE
   if (hipGetLastError() != hipSuccess) return RV_ERR_HIP;
   return RV_OK;
 }
@@ -259,12 +259,17 @@ extern "C" rv_status lse_merge(const float* o_part, const float* lse_part, int S
   hipStream_t s = static_cast<hipStream_t>(stream);
   dim3 grid((unsigned)rows);
   uint16_t* o16 = static_cast<uint16_t*>(out);
-  if (d == 64)
-    hipLaunchKernelGGL((rv::merge_kernel<64>), grid, dim3(256), 0, s, o_part, lse_part, S, o_blk,
-                       lse_blk, o16, lse_out);
-  else
-    hipLaunchKernelGGL((rv::merge_kernel<128>), grid, dim3(256), 0, s, o_part, lse_part, S, o_blk,
-                       lse_blk, o16, lse_out);
+  const int fb = rv::fold_batch(S);
+#define RV_M_CASE(DD, FB)                                                                   \
+  if (d == DD && fb == FB)                                                                   \
+    rv::launch_merge<DD, FB>(grid, s, o_part, lse_part, S, o_blk, lse_blk, o16, lse_out);
+  RV_M_CASE(64, 8)
+  else RV_M_CASE(64, 16)
+  else RV_M_CASE(64, 32)
+  else RV_M_CASE(128, 8)
+  else RV_M_CASE(128, 16)
+  else RV_M_CASE(128, 32)
+#undef RV_M_CASE
   if (hipGetLastError() != hipSuccess) return RV_ERR_HIP;
   return RV_OK;
 }
