@@ -103,7 +103,8 @@ int rv_version(void);
  * Choose the history split for spec_attn_prefix on this device class:
  * writes *split_len (tokens per split, a multiple of 128) and *num_splits
  * (S = ceil(max_seq_len / split_len), at least 1) so that the launch fills the
- * MI355X's 256 compute units.  Pure host arithmetic, no HIP call.
+ * MI355X's 256 compute units, with splits of at least 512 tokens.  Pure host
+ * arithmetic, no HIP call.
  */
 rv_status rv_prefix_default_split(int64_t max_seq_len, int B, int Hq, int Hkv, int n,
                                   int d, int64_t* split_len, int* num_splits);
@@ -113,7 +114,7 @@ rv_status rv_prefix_default_split(int64_t max_seq_len, int B, int Hq, int Hkv, i
  * on the host (a serving loop does: it manages the cache).  seq_lens_host is
  * HOST int32 [B], each >= 0 (else RV_ERR_VALUE); num_cus is the device's
  * compute-unit count.  Writes the shortest split_len (a multiple of 128, at
- * least 1024) for which the splits that hold keys, Hkv * sum_b
+ * least 512) for which the splits that hold keys, Hkv * sum_b
  * ceil(L_b / split_len), all fit on the compute units at once, and
  * S = ceil(max_b L_b / split_len); when even one split per sequence does not
  * fit, one split per sequence.  A ragged batch then keeps every compute unit

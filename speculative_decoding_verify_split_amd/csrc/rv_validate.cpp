@@ -224,7 +224,7 @@ rv_status rv_prefix_default_split(int64_t max_seq_len, int B, int Hq, int Hkv, i
                     ? max_seq_len
                     : (max_seq_len * groups + target_groups - 1) / target_groups;
   int64_t len = ((per + q - 1) / q) * q;
-  const int64_t min_len = 8 * q;  // at least 8 tiles per wave
+  const int64_t min_len = 4 * q;  // at least 4 tiles per wave
   if (len < min_len) len = min_len;
   int64_t S = (max_seq_len + len - 1) / len;
   if (S < 1) S = 1;
@@ -249,7 +249,7 @@ rv_status rv_prefix_balanced_split(const int32_t* seq_lens_host, int B, int Hq, 
     if (L > max_len) max_len = L;
   }
   const int64_t q = rv::kSplitQuantum;
-  const int64_t min_len = 8 * q;  // at least 8 tiles per wave
+  const int64_t min_len = 4 * q;  // at least 4 tiles per wave
   // Workgroups that get keys with splits of m quanta: Hkv * sum_b ceil(L_b / (m q)).
   auto busy = [&](int64_t m) {
     int64_t c = 0;

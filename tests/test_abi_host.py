@@ -272,9 +272,9 @@ def test_default_split_covers_the_sequence(lib, L, B, Hq, Hkv, n, d):
         # 8 kv heads x 32 splits: one 4-wave workgroup per compute unit
         assert (split_len, S) == (4096, 32)
     if L == 131072 and B == 1 and Hkv == 1:
-        # one kv head (a GPU's share under 8-way head parallelism): splits of
-        # 8 tiles per wave, 128 workgroups
-        assert (split_len, S) == (1024, 128)
+        # one kv head (a GPU's share under 8-way head parallelism): the
+        # shortest splits, 4 tiles per wave, one workgroup per compute unit
+        assert (split_len, S) == (512, 256)
 
 
 def _balanced_c(lib, lens, Hq=28, Hkv=4, n=11, d=128, ncu=256):
@@ -294,15 +294,15 @@ def _busy(lens, Hkv, split_len):
     ([131072], 32, 8, 11), ([122880], 64, 8, 11), ([1048576], 32, 8, 32), ([4096], 8, 2, 5),
     ([1, 31, 32, 33, 129], 4, 2, 3), ([0, 0], 4, 2, 5), ([131072] * 8, 28, 4, 11)])
 def test_balanced_split_fills_the_units_with_the_shortest_split(lib, lens, Hq, Hkv, n):
-    """The balanced split is the shortest multiple of 128 (>= 1024) whose
+    """The balanced split is the shortest multiple of 128 (>= 512) whose
     non-empty splits fit on 256 compute units, and S covers every sequence."""
     st, split_len, S = _balanced_c(lib, lens, Hq, Hkv, n)
     assert st == RV_OK
-    assert split_len % 128 == 0 and split_len >= 1024
+    assert split_len % 128 == 0 and split_len >= 512
     assert S >= 1 and S * split_len >= max(lens)
     assert (S - 1) * split_len < max(max(lens), 1)
     assert _busy(lens, Hkv, split_len) <= 256
-    if split_len > 1024:
+    if split_len > 512:
         assert _busy(lens, Hkv, split_len - 128) > 256
     # one sequence: the same choice as the default split
     if len(lens) == 1:
