@@ -12,8 +12,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (attn_keys_ref, attn_ref, bf16_bits_to_f64, block_visibility, rapid_accept_ref,
-                    retrieval_augmented_target)
+from oracle import (attn_keys_ref, attn_ref, bf16_bits_to_f64, block_visibility, lse_merge_ref,
+                    rapid_accept_ref, retrieval_augmented_target)
 from oracle.compare import ATTN_ROW_TOL, P_HAT_TOL, attn_row_errors, compare_accept
 from workloads import (CONFIGS, config_attention, config_vocab, make_attention, make_vocab,
                        tree_parents)
@@ -61,6 +61,8 @@ ATTN_CASES = [
     ("d128-g5-tree32-wide3", 35, 1, 10, 2, 128, 32, [1234], None, "tree", (256, 5)),
     ("d64-g16-n16-wide4", 36, 1, 16, 1, 64, 16, [777], None, "star", (384, 3)),
     ("wide-short-lengths", 37, 5, 16, 2, 128, 11, [1, 127, 128, 129, 0], None, None, (128, 2)),
+    # 300 partials per row: the merges fold them in three batches per wave
+    ("d128-g2-n3-300-splits", 38, 1, 4, 2, 128, 3, [38300], None, None, (128, 300)),
 ]
 
 
@@ -150,6 +152,73 @@ def test_prefix_and_block_partials_match_split_oracle(case):
             # splits, so it is held to the same attention tolerance
             assert attn_row_errors(o_blk[b, h], o).max() <= ATTN_ROW_TOL
             assert np.abs(lse_blk[b, h] - l).max() <= 1e-2
+
+
+# Split counts around the merges' fold batches (8, 16 or 32 partials per
+# wave, 4 waves) and several batches per wave.
+MERGE_S = [1, 7, 32, 33, 64, 65, 128, 129, 300]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("S", MERGE_S)
+def test_merges_fold_any_number_of_partials(S, d):
+    """lse_merge (with and without a block partial) and spec_attn_block_merge
+    on random fp32 partials, a quarter of the splits empty and one row with
+    every split empty, against the oracle's log-sum-exp merge."""
+    from speculative_decoding_verify_split_amd import rapid_verify as rv
+    from speculative_decoding_verify_split_amd.step import bf16_to_device
+    announce("merge fold S=%d d=%d" % (S, d))
+    rng = np.random.default_rng(5000 + 7 * S + d)
+    B, Hq, Hkv, n = 2, 4, 2, 5
+    o = rng.standard_normal((B, Hq, n, S, d)).astype(np.float32)
+    lse = (3.0 * rng.standard_normal((B, Hq, n, S))).astype(np.float32)
+    empty = rng.random((B, Hq, n, S)) < 0.25
+    empty[0, 0, 0, :] = True
+    lse[empty] = -np.inf
+    o[empty] = 0.0
+    o_blk = rng.standard_normal((B, Hq, n, d)).astype(np.float32)
+    lse_blk = (3.0 * rng.standard_normal((B, Hq, n))).astype(np.float32)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    o_t, lse_t, ob_t, lb_t = dev(o), dev(lse), dev(o_blk), dev(lse_blk)
+    out = torch.empty((B, Hq, n, d), dtype=torch.bfloat16, device="cuda")
+    lse_out = torch.empty((B, Hq, n), dtype=torch.float32, device="cuda")
+    hist = [(o[:, :, :, s].astype(np.float64), lse[:, :, :, s].astype(np.float64))
+            for s in range(S)]
+
+    def check(O_ref, L_ref, what):
+        torch.cuda.synchronize()
+        got = out.float().cpu().numpy()
+        got_l = lse_out.cpu().numpy()
+        err = attn_row_errors(got, O_ref).max()
+        both_inf = np.isneginf(got_l) & np.isneginf(L_ref)
+        with np.errstate(invalid="ignore"):  # -inf - -inf where both rows are empty
+            diff = np.abs(got_l - L_ref)
+        dl = np.where(both_inf, 0.0, diff).max()
+        announce("  %s: max row rel err %.3e, max |dLSE| %.3e" % (what, err, dl))
+        assert err <= 1e-2 and dl <= 1e-4
+
+    rv.lse_merge(o_t, lse_t, ob_t, lb_t, out, lse_out)
+    check(*lse_merge_ref(hist + [(o_blk.astype(np.float64), lse_blk.astype(np.float64))]),
+          "lse_merge")
+    rv.lse_merge(o_t, lse_t, None, None, out, lse_out)
+    O_ref, L_ref = lse_merge_ref(hist)
+    assert np.isneginf(L_ref[0, 0, 0]) and np.all(O_ref[0, 0, 0] == 0)
+    check(O_ref, L_ref, "lse_merge, history only")
+
+    # the fused call computes the causal block part itself
+    ai = make_attention(6000 + S + d, B, Hq, Hkv, d, n, [0] * B, L_max=128)
+    rv.spec_attn_block_merge(bf16_to_device(ai.q), bf16_to_device(ai.k_blk),
+                             bf16_to_device(ai.v_blk), None, o_t, lse_t, out, lse_out, 1.0)
+    vis = block_visibility(n, None)
+    O_b = np.zeros((B, Hq, n, d))
+    L_b = np.zeros((B, Hq, n))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            O_b[b, h], L_b[b, h] = attn_keys_ref(bf16_bits_to_f64(ai.q[b, h]),
+                                                 bf16_bits_to_f64(ai.k_blk[b, g]),
+                                                 bf16_bits_to_f64(ai.v_blk[b, g]), vis, 1.0)
+    check(*lse_merge_ref(hist + [(O_b, L_b)]), "spec_attn_block_merge")
 
 
 def test_prefix_ev_matches_prefix_and_records_the_kernel():
