@@ -6,15 +6,16 @@
 // Without a block partial (o_blk = lse_blk = NULL) the history partials are
 // merged alone, as for a drafter's cross-attention over the target cache.
 //
-// One 4-wave workgroup per output row; the row's S partials are contiguous
-// ([row][S][d]).  Wave w folds splits w, w + 4, ... in ascending order (each
-// split one 4*d-byte line read by all 64 lanes), the four wave sums are
-// added in wave order and the block partial last, so the result is
-// bit-deterministic.  A wave's partials are loaded in batches of FB with
-// every load of a batch in flight at once: the loads do not depend on the
-// row's maximum, so a row costs ceil(S / (4 FB)) memory round trips.  The
-// launch picks FB = 8, 16 or 32 from S (one round trip up to S = 128) and
-// so keeps the registers of short folds low.
+// One workgroup of NWV waves per output row; the row's S partials are
+// contiguous ([row][S][d]).  Wave w folds splits w, w + NWV, ... in
+// ascending order (each split one 4*d-byte line read by all 64 lanes), the
+// wave sums are added in wave order and the block partial last, so the
+// result is bit-deterministic for a given S.  A wave's partials are loaded
+// in batches of FB with every load of a batch in flight at once: the loads
+// do not depend on the row's maximum, so a row costs ceil(S / (NWV FB))
+// memory round trips.  The launch picks (FB, NWV) from S: (8, 4), (16, 4)
+// and (32, 4) up to S = 32, 64 and 128, then (32, 8), so that a row takes
+// one round trip up to S = 256 while short folds keep their registers low.
 //
 // spec_attn_block_merge does the same with the block partial computed in
 // place: wave 0 of each row's workgroup also runs the row's masked block
@@ -77,15 +78,23 @@ struct PartialFold {
   }
 };
 
-template <int D, int FB>
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_part,
+// Fixed-order (left to right) sum of the NWV wave values.
+template <int NWV>
+__device__ __forceinline__ float wave_order_sum(const float* v, int stride) {
+  float t = v[0];
+#pragma unroll
+  for (int w = 1; w < NWV; ++w) t += v[w * stride];
+  return t;
+}
+
+template <int D, int FB, int NWV>
+__global__ __launch_bounds__(NWV * 64) void merge_kernel(const float* __restrict__ o_part,
                                                     const float* __restrict__ lse_part, int S,
                                                     const float* __restrict__ o_blk,
                                                     const float* __restrict__ lse_blk,
                                                     uint16_t* __restrict__ out,
                                                     float* __restrict__ lse_out) {
   constexpr int PER = D / 64;
-  constexpr int NWV = 4;
   __shared__ float part[NWV][D];
   __shared__ float wpart[NWV];
   const int lane = threadIdx.x & 63;
@@ -112,13 +121,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
   if (lane == 0) wpart[wave] = wsum;
   __syncthreads();
   if (wave != 0) return;
-  float tot = ((wpart[0] + wpart[1]) + wpart[2]) + wpart[3];
+  float tot = wave_order_sum<NWV>(wpart, 1);
   float res[PER];
 #pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int c = lane * PER + e;
-    res[e] = ((part[0][c] + part[1][c]) + part[2][c]) + part[3][c];
-  }
+  for (int e = 0; e < PER; ++e) res[e] = wave_order_sum<NWV>(&part[0][lane * PER + e], D);
   if (M != -INFINITY && lse_blk != nullptr) {
     const float a = exp2_hw((lb - M) * kLog2e);
     tot += a;
@@ -139,14 +145,13 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
 // their own maximum Ms; the final combine rescales the history sums by
 // exp(Ms - M) and the block partial by exp(LSE_blk - M), M the larger of the
 // two, which is the same log-sum-exp merge.
-template <int D, int FB>
-__global__ __launch_bounds__(256) void block_merge_kernel(
+template <int D, int FB, int NWV>
+__global__ __launch_bounds__(NWV * 64) void block_merge_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kb,
     const uint16_t* __restrict__ vb, BlockMask mask, int Hq, int G, int n, float scale_log2,
     const float* __restrict__ o_part, const float* __restrict__ lse_part, int S,
     uint16_t* __restrict__ out, float* __restrict__ lse_out) {
   constexpr int PER = D / 64;
-  constexpr int NWV = 4;
   __shared__ float part[NWV][D];
   __shared__ float wpart[NWV];
   const int lane = threadIdx.x & 63;
@@ -183,35 +188,36 @@ __global__ __launch_bounds__(256) void block_merge_kernel(
   const float M = fmaxf(Ms, lb);
   const float fs = (Ms == -INFINITY) ? 0.f : exp2_hw((Ms - M) * kLog2e);
   const float fb = exp2_hw((lb - M) * kLog2e);
-  const float tot = fmaf(fs, ((wpart[0] + wpart[1]) + wpart[2]) + wpart[3], fb);
+  const float tot = fmaf(fs, wave_order_sum<NWV>(wpart, 1), fb);
   const float inv = 1.0f / tot;  // tot >= fb = 1 or fs * wsum >= 1
   uint16_t* dst = out + (size_t)row * D + lane * PER;
 #pragma unroll
   for (int e = 0; e < PER; ++e) {
     const int c = lane * PER + e;
-    const float hs = ((part[0][c] + part[1][c]) + part[2][c]) + part[3][c];
+    const float hs = wave_order_sum<NWV>(&part[0][c], D);
     dst[e] = f32_to_bf16_bits(fmaf(fs, hs, fb * ob[e]) * inv);
   }
   if (lse_out != nullptr && lane == 0) lse_out[row] = M + log2_hw(tot) * kLn2;
 }
 
-// Partials per wave per batch of loads: 4 waves fold a row's S partials.
-int fold_batch(int S) { return S <= 4 * 8 ? 8 : (S <= 4 * 16 ? 16 : 32); }
+// Fold shape for S partials per row: partials per wave per batch of loads
+// (FB) and waves per row (NWV); the index 0..3 selects one of the four.
+int fold_shape(int S) { return S <= 32 ? 0 : (S <= 64 ? 1 : (S <= 128 ? 2 : 3)); }
 
-template <int D, int FB>
+template <int D, int FB, int NWV>
 void launch_block_merge(dim3 grid, hipStream_t s, const uint16_t* q, const uint16_t* k,
                         const uint16_t* v, const BlockMask& mask, int Hq, int G, int n,
                         float scale_log2, const float* o_part, const float* lse_part, int S,
                         uint16_t* out, float* lse_out) {
-  hipLaunchKernelGGL((block_merge_kernel<D, FB>), grid, dim3(256), 0, s, q, k, v, mask, Hq, G,
-                     n, scale_log2, o_part, lse_part, S, out, lse_out);
+  hipLaunchKernelGGL((block_merge_kernel<D, FB, NWV>), grid, dim3(NWV * 64), 0, s, q, k, v,
+                     mask, Hq, G, n, scale_log2, o_part, lse_part, S, out, lse_out);
 }
 
-template <int D, int FB>
+template <int D, int FB, int NWV>
 void launch_merge(dim3 grid, hipStream_t s, const float* o_part, const float* lse_part, int S,
                   const float* o_blk, const float* lse_blk, uint16_t* out, float* lse_out) {
-  hipLaunchKernelGGL((merge_kernel<D, FB>), grid, dim3(256), 0, s, o_part, lse_part, S, o_blk,
-                     lse_blk, out, lse_out);
+  hipLaunchKernelGGL((merge_kernel<D, FB, NWV>), grid, dim3(NWV * 64), 0, s, o_part, lse_part,
+                     S, o_blk, lse_blk, out, lse_out);
 }
 
 }  // namespace
@@ -234,17 +240,19 @@ extern "C" rv_status spec_attn_block_merge(const void* q, const void* k_blk, con
   const uint16_t* vv = static_cast<const uint16_t*>(v_blk);
   uint16_t* o16 = static_cast<uint16_t*>(out);
   const int G = Hq / Hkv;
-  const int fb = rv::fold_batch(S);
-#define RV_BM_CASE(DD, FB)                                                                   \
-  if (d == DD && fb == FB)                                                                   \
-    rv::launch_block_merge<DD, FB>(grid, s, qq, kk, vv, mask, Hq, G, n, scale_log2, o_part, \
-                                   lse_part, S, o16, lse_out);
-  RV_BM_CASE(64, 8)
-  else RV_BM_CASE(64, 16)
-  else RV_BM_CASE(64, 32)
-  else RV_BM_CASE(128, 8)
-  else RV_BM_CASE(128, 16)
-  else RV_BM_CASE(128, 32)
+  const int fs = rv::fold_shape(S);
+#define RV_BM_CASE(DD, F, FB, NWV)                                                           \
+  if (d == DD && fs == F)                                                                    \
+    rv::launch_block_merge<DD, FB, NWV>(grid, s, qq, kk, vv, mask, Hq, G, n, scale_log2,     \
+                                        o_part, lse_part, S, o16, lse_out);
+  RV_BM_CASE(64, 0, 8, 4)
+  else RV_BM_CASE(64, 1, 16, 4)
+  else RV_BM_CASE(64, 2, 32, 4)
+  else RV_BM_CASE(64, 3, 32, 8)
+  else RV_BM_CASE(128, 0, 8, 4)
+  else RV_BM_CASE(128, 1, 16, 4)
+  else RV_BM_CASE(128, 2, 32, 4)
+  else RV_BM_CASE(128, 3, 32, 8)
 #undef RV_BM_CASE
   if (hipGetLastError() != hipSuccess) return RV_ERR_HIP;
   return RV_OK;
@@ -259,16 +267,18 @@ extern "C" rv_status lse_merge(const float* o_part, const float* lse_part, int S
   hipStream_t s = static_cast<hipStream_t>(stream);
   dim3 grid((unsigned)rows);
   uint16_t* o16 = static_cast<uint16_t*>(out);
-  const int fb = rv::fold_batch(S);
-#define RV_M_CASE(DD, FB)                                                                   \
-  if (d == DD && fb == FB)                                                                   \
-    rv::launch_merge<DD, FB>(grid, s, o_part, lse_part, S, o_blk, lse_blk, o16, lse_out);
-  RV_M_CASE(64, 8)
-  else RV_M_CASE(64, 16)
-  else RV_M_CASE(64, 32)
-  else RV_M_CASE(128, 8)
-  else RV_M_CASE(128, 16)
-  else RV_M_CASE(128, 32)
+  const int fs = rv::fold_shape(S);
+#define RV_M_CASE(DD, F, FB, NWV)                                                            \
+  if (d == DD && fs == F)                                                                    \
+    rv::launch_merge<DD, FB, NWV>(grid, s, o_part, lse_part, S, o_blk, lse_blk, o16, lse_out);
+  RV_M_CASE(64, 0, 8, 4)
+  else RV_M_CASE(64, 1, 16, 4)
+  else RV_M_CASE(64, 2, 32, 4)
+  else RV_M_CASE(64, 3, 32, 8)
+  else RV_M_CASE(128, 0, 8, 4)
+  else RV_M_CASE(128, 1, 16, 4)
+  else RV_M_CASE(128, 2, 32, 4)
+  else RV_M_CASE(128, 3, 32, 8)
 #undef RV_M_CASE
   if (hipGetLastError() != hipSuccess) return RV_ERR_HIP;
   return RV_OK;
