@@ -59,6 +59,9 @@
  *   which workgroup performs the draw, not what is drawn.
  * - Workspaces (rapid_accept, spec_attn_window) are caller-owned device
  *   scratch; they need no initial contents and hold nothing between calls.
+ *   A workspace counts as an output: calls that may run at the same time
+ *   (different streams) each need their own; calls on one stream may share
+ *   one.
  *
  * - Sizes beyond the launch grid's reach (B or Hq above 65535, a window or
  *   sink above 2^24) return RV_ERR_UNSUPPORTED.
