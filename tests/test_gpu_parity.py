@@ -154,6 +154,82 @@ def test_prefix_and_block_partials_match_split_oracle(case):
             assert np.abs(lse_blk[b, h] - l).max() <= 1e-2
 
 
+# ------------------------------------------------ seeded random shapes
+
+def _random_attention_cases(seed=77, count=24):
+    """Shapes drawn at random within the library's limits: both kernels
+    (up to and above 64 rows per kv head), both head dims, ragged and empty
+    histories, split lengths from 128 to 1408 keys, spare splits past every
+    history, causal chains and random trees."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(count):
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.integers(1, 4))
+        G = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 12, 16]))
+        n = int(rng.integers(1, min(64, 256 // G) + 1))
+        B = int(rng.integers(1, 5))
+        lens = [int(x) for x in rng.integers(0, 2600, B)]
+        if rng.random() < 0.3:
+            lens[int(rng.integers(0, B))] = 0
+        L_max = max(max(lens), 1) + int(rng.integers(0, 200))
+        parent = None
+        if n > 2 and rng.random() < 0.4:
+            parent = tree_parents(np.random.SeedSequence(seed * 1000 + k), n,
+                                  int(rng.integers(1, min(6, n - 1) + 1)))
+        split_len = 128 * int(rng.integers(1, 12))
+        S = max(1, -(-max(lens) // split_len)) + int(rng.integers(0, 3))
+        name = "r%02d-d%d-b%d-g%d-n%d%s" % (k, d, B, G, n, "-tree" if parent is not None else "")
+        cases.append((name, seed * 1000 + k, B, G * Hkv, Hkv, d, n, lens, L_max, parent,
+                      (split_len, S)))
+    return cases
+
+
+RANDOM_ATTN_CASES = _random_attention_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM_ATTN_CASES, ids=[c[0] for c in RANDOM_ATTN_CASES])
+def test_attention_random_shapes(case):
+    name, seed, B, Hq, Hkv, d, n, lens, L_max, parent, split = case
+    ai = make_attention(seed, B, Hq, Hkv, d, n, lens, L_max=L_max, parent=parent,
+                        pad_bits=0x7FC0)
+    announce("random attention %s lens=%s split=%s" % (name, lens, split))
+    st = VerifyStep(ai, None, split=split)
+    O_ref, L_ref = attn_ref(ai.q, ai.k_cache, ai.v_cache, ai.k_blk, ai.v_blk, ai.seq_lens,
+                            ai.parent, ai.sm_scale)
+    for fused in (False, True):
+        st.attention(fused=fused)
+        out, lse = _attn_outputs(st)
+        err = attn_row_errors(out, O_ref).max()
+        dl = np.abs(lse - L_ref).max()
+        announce("  %s: max row rel err %.3e, max |dLSE| %.3e"
+                 % ("block_merge" if fused else "block+merge", err, dl))
+        assert err <= ATTN_ROW_TOL and dl <= 1e-2
+
+
+def _random_vocab_cases(seed=78, count=16):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(count):
+        kw = dict(seed=seed * 1000 + k, B=int(rng.integers(1, 7)), gamma=int(rng.integers(1, 13)),
+                  V=int(rng.choice([2, 3, 5]) if rng.random() < 0.15 else rng.integers(6, 60000)),
+                  z_sigma=float(rng.uniform(0.5, 4.0)), noise=float(rng.uniform(0.2, 2.0)),
+                  T=float(rng.uniform(0.5, 1.5)), eta=float(rng.choice([0.0, rng.uniform(0.1, 2.5)])))
+        cases.append(("r%02d-b%d-g%d-V%d" % (k, kw["B"], kw["gamma"], kw["V"]), kw))
+    return cases
+
+
+RANDOM_VOCAB_CASES = _random_vocab_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM_VOCAB_CASES, ids=[c[0] for c in RANDOM_VOCAB_CASES])
+def test_accept_random_shapes(case):
+    name, kw = case
+    vi = make_vocab(**kw)
+    announce("random rapid_accept %s T=%.2f eta=%.2f" % (name, kw["T"], kw["eta"]))
+    _check_accept(vi, _run_accept(vi), name)
+
+
 # Split counts around the merges' fold batches (8, 16 or 32 partials per
 # wave, 4 waves) and several batches per wave.
 MERGE_S = [1, 7, 32, 33, 64, 65, 128, 129, 300]
