@@ -45,7 +45,29 @@ WINDOW_CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", WINDOW_CASES, ids=[c[0] for c in WINDOW_CASES])
+def _random_window_cases(seed=79, count=16):
+    """Window shapes drawn at random: windows of 1 to 700 keys, 0 to 8
+    anchors, rings from the tightest capacity to 40 slots more, query
+    positions before and after the ring wraps."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(count):
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.integers(1, 4))
+        G = int(rng.choice([1, 2, 4, 7, 8]))
+        n = int(rng.integers(1, 17))
+        sink = int(rng.choice([0, 1, 4, 8]))
+        window = int(rng.integers(1, 701))
+        cap = sink + window + n - 1 + int(rng.integers(0, 41))
+        B = int(rng.integers(1, 4))
+        pos = [int(rng.integers(0, 3 * cap)) for _ in range(B)]
+        cases.append(("r%02d-d%d-g%d-n%d-s%d-w%d-c%d" % (k, d, G, n, sink, window, cap),
+                      seed * 1000 + k, B, G * Hkv, Hkv, d, n, pos, cap, sink, window))
+    return cases
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES + _random_window_cases(),
+                         ids=[c[0] for c in WINDOW_CASES + _random_window_cases()])
 def test_window_small(case):
     name, seed, B, Hq, Hkv, d, n, pos, cap, sink, window = case
     wi = make_window(seed, B, Hq, Hkv, d, n, pos=pos, cap=cap, sink=sink, window=window)
