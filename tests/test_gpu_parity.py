@@ -230,6 +230,19 @@ def test_accept_random_shapes(case):
     _check_accept(vi, _run_accept(vi), name)
 
 
+@pytest.mark.parametrize("flags", [RV_ACCEPT_TAIL_PRESERVE, RV_ACCEPT_PRINTED_RESIDUAL,
+                                   RV_ACCEPT_TAIL_PRESERVE | RV_ACCEPT_PRINTED_RESIDUAL])
+@pytest.mark.parametrize("case", RANDOM_VOCAB_CASES[:8], ids=[c[0] for c in RANDOM_VOCAB_CASES[:8]])
+def test_accept_rules_random_shapes(case, flags):
+    name, kw = case
+    vi = make_vocab(**kw)
+    if flags & RV_ACCEPT_TAIL_PRESERVE and _tail_margin(vi) <= 1e-5:
+        pytest.skip("a p_hat entry lies within 1e-5 of the tail threshold, which fp32 and "
+                    "fp64 may place on different sides")
+    announce("random rapid_accept_ex %s flags=%d" % (name, flags))
+    _check_accept(vi, _run_accept(vi, flags=flags), "%s flags=%d" % (name, flags), flags)
+
+
 # Split counts around the merges' fold batches (8, 16 or 32 partials per
 # wave, 4 waves) and several batches per wave.
 MERGE_S = [1, 7, 32, 33, 64, 65, 128, 129, 300]
