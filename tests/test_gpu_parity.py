@@ -395,8 +395,8 @@ def _check_accept(vi, st, tag, flags=0):
     ref = rapid_accept_ref(vi.z, vi.y, vi.draft, vi.r, vi.u, vi.T, vi.eta, tail_preserve=tail,
                            residual="printed" if flags & RV_ACCEPT_PRINTED_RESIDUAL else "p_hat")
     if tail and _tail_margin(vi) <= 1e-5:
-        announce("  %s: an entry lies within 1e-5 of the tail threshold; not compared" % tag)
-        return ref, None
+        pytest.skip("%s: a p_hat entry lies within 1e-5 of the tail threshold, which fp32 and "
+                    "fp64 may place on different sides" % tag)
     n_g = st.n_accept.cpu().numpy()
     tok = st.out_tokens.cpu().numpy()
     res = compare_accept(ref, n_g, tok, vi.r, vi.u)
