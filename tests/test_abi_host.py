@@ -277,6 +277,27 @@ def test_default_split_covers_the_sequence(lib, L, B, Hq, Hkv, n, d):
         assert (split_len, S) == (512, 256)
 
 
+def test_default_split_properties_on_random_shapes(lib):
+    """Seeded random shapes: a multiple of 128 of at least 512 tokens that
+    covers the sequence in S <= 65535 splits, and with fewer (b, kv head)
+    groups than compute units, no split shorter than the units need."""
+    from hypothesis import given, settings, strategies as st
+
+    @settings(max_examples=300, derandomize=True, deadline=None)
+    @given(L=st.integers(0, 1 << 26), B=st.integers(1, 300), Hkv=st.integers(1, 16),
+           G=st.sampled_from([1, 4, 8]))
+    def check(L, B, Hkv, G):
+        split_len, S = rv.rv_prefix_default_split(L, B, G * Hkv, Hkv, 11, 128)
+        assert split_len % 128 == 0 and split_len >= 512
+        assert 1 <= S <= 65535 and S * split_len >= L
+        assert (S - 1) * split_len < max(L, 1)
+        if B * Hkv < 256 and split_len > 512:
+            # one split of 128 fewer tokens would need more workgroups than units
+            assert B * Hkv * -(-L // (split_len - 128)) > 256
+
+    check()
+
+
 def _balanced_c(lib, lens, Hq=28, Hkv=4, n=11, d=128, ncu=256):
     arr = (ctypes.c_int32 * len(lens))(*lens)
     sl, ns = ctypes.c_int64(), ctypes.c_int()
@@ -309,6 +330,35 @@ def test_balanced_split_fills_the_units_with_the_shortest_split(lib, lens, Hq, H
         assert (split_len, S) == rv.rv_prefix_default_split(lens[0], 1, Hq, Hkv, n, 128)
     # the Python binding agrees with the C call
     assert rv.rv_prefix_balanced_split(lens, Hq, Hkv, n, 128, num_cus=256) == (split_len, S)
+
+
+def test_balanced_split_properties_on_random_batches(lib):
+    """Seeded random batches (1-80 sequences of 0..2^20 tokens, 1-16 kv
+    heads, 64-304 compute units): the split is a multiple of 128 of at least
+    512 tokens, the splits cover the longest sequence, the busy workgroups
+    fit on the units (unless even one split per sequence does not), and no
+    shorter split would fit."""
+    from hypothesis import given, settings, strategies as st
+
+    @settings(max_examples=300, derandomize=True, deadline=None)
+    @given(lens=st.lists(st.integers(0, 1 << 20), min_size=1, max_size=80),
+           Hkv=st.integers(1, 16), G=st.sampled_from([1, 4, 7, 8]),
+           ncu=st.sampled_from([64, 256, 304]))
+    def check(lens, Hkv, G, ncu):
+        status, split_len, S = _balanced_c(lib, lens, Hq=G * Hkv, Hkv=Hkv, n=11, ncu=ncu)
+        assert status == RV_OK
+        assert split_len % 128 == 0 and split_len >= 512
+        assert S >= 1 and S * split_len >= max(lens)
+        assert (S - 1) * split_len < max(max(lens), 1)
+        one_each = max(max(lens), 1)
+        if _busy(lens, Hkv, ((one_each + 127) // 128) * 128) <= ncu:
+            assert _busy(lens, Hkv, split_len) <= ncu
+            if split_len > 512:
+                assert _busy(lens, Hkv, split_len - 128) > ncu
+        else:
+            assert S == 1  # one split per sequence
+
+    check()
 
 
 def test_balanced_split_ragged_batch_is_shorter_than_the_default(lib):
