@@ -5,7 +5,8 @@ One step is the whole hot path on one batch of synthetic inputs:
 spec_attn_prefix (history pass over the KV cache), the masked draft block and
 the log-sum-exp merge (one spec_attn_block_merge call; --unfused runs
 spec_attn_block and lse_merge separately), and rapid_accept (RAPID's
-vocabulary pass), back to back on one stream.  Default workload: the LLaMA-3.1-8B-shaped verify layer
+vocabulary pass), back to back on one stream.  Default workload: the
+LLaMA-3.1-8B-shaped verify layer
 (32 query / 8 kv heads, d=128, 131072-token bf16 KV cache, gamma=10, vocab
 128256, T=1, eta=0.5), inputs resident in HBM.  Three copies of the KV cache
 and of the logits rotate from step to step so that no step reads what the
@@ -181,11 +182,11 @@ def _calibrate_copy(n_bytes, reps):
     print(json.dumps({"calibration_copy_bytes": n_bytes, "reps": reps}))
 
 
-def _timed_loop(step, K, warmup):
+def _timed_loop(step, K, warmup, n_events=3):
     import torch
     for i in range(warmup):
         step(i)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_events)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -330,7 +331,6 @@ def run_model(args):
         ms.vocab.accept()
         if ev is not None:
             ev[2].record()
-            ev[3].record()
 
     K = args.steps
     evs, elapsed = _timed_loop(step, K, args.warmup)
