@@ -313,14 +313,15 @@ def run_model(args):
     import numpy as np
     import torch
     from speculative_decoding_verify_split_amd.step import ModelStep
-    from workloads import CONFIGS, MODEL_CONFIGS, config_vocab
+    from workloads import CONFIGS, MODEL_CONFIGS, config_vocab, make_layer_device
 
     mc = MODEL_CONFIGS[args.workload]
     c = CONFIGS[mc["layer_config"]]
     eta = c["etas"][min(1, len(c["etas"]) - 1)] if args.eta is None else args.eta
     vi = config_vocab(mc["layer_config"], eta=eta)
-    ms = ModelStep(mc["layers"], c["B"], c["Hq"], c["Hkv"], c["d"], c["gamma"] + 1, c["L"],
-                   mc["seed"], vocab=vi)
+    layers = [make_layer_device(mc["seed"], l, c["B"], c["Hq"], c["Hkv"], c["d"], c["gamma"] + 1,
+                                c["L"]) for l in range(mc["layers"])]
+    ms = ModelStep(layers, c["L"], vocab=vi)
 
     def step(i, ev=None):
         if ev is not None:

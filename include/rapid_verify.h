@@ -50,8 +50,11 @@
  *   HIP call.  On a failed check the call returns a nonzero rv_status and
  *   writes nothing.  A failed kernel launch returns RV_ERR_HIP (the HIP error
  *   is cleared).  No C++ exception crosses this interface.
- * - Device data are the caller's responsibility: seq_lens values are clamped
- *   to [0, L_max]; a draft id outside [0, V) makes rapid_accept report
+ * - Device data are the caller's responsibility: spec_attn_prefix reads
+ *   min(max(seq_lens[b], 0), L_max, num_splits * split_len) history tokens of
+ *   sequence b (the partials hold num_splits splits, so a device length
+ *   above the host's max_seq_len is cut at num_splits * split_len, never
+ *   read past); a draft id outside [0, V) makes rapid_accept report
  *   n_accept = -1 for that sequence; non-finite logits give unspecified
  *   tokens but never an out-of-bounds access.
  * - Results are bit-deterministic: every reduction has a fixed order; the
@@ -146,7 +149,9 @@ rv_status rv_prefix_balanced_split(const int32_t* seq_lens_host, int B, int Hq, 
  *                                    split; -inf (and o_part = 0) for a split
  *                                    that holds no history token
  * Split s of sequence b covers tokens [s*split_len, min((s+1)*split_len,
- * seq_lens[b])).  Supports d in {64, 128}, n <= 64, (Hq/Hkv)*n <= 256.
+ * L_b)), L_b = min(max(seq_lens[b], 0), L_max): the call attends over the
+ * first min(L_b, S*split_len) tokens.  Supports d in {64, 128}, n <= 64,
+ * (Hq/Hkv)*n <= 256.
  */
 rv_status spec_attn_prefix(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* seq_lens, int64_t max_seq_len, int B, int Hq,

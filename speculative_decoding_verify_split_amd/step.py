@@ -145,20 +145,22 @@ class WindowStep:
 
 class ModelStep:
     """Every attention layer of a model's verify step, then one acceptance
-    pass.  Layer inputs are generated on the device by workloads'
-    make_layer_device; the split partials are reused from layer to layer
-    (stream order keeps each merge ahead of the next layer's history pass);
-    each layer keeps its own output."""
+    pass.  layer_inputs: one (q, k_cache, v_cache, k_blk, v_blk) tuple of
+    device bf16 tensors per layer, shaped as spec_attn_prefix and
+    spec_attn_block take them, every layer's cache holding L history tokens
+    per sequence.  The split partials are reused from layer to layer (stream
+    order keeps each merge ahead of the next layer's history pass); each
+    layer keeps its own output."""
 
-    def __init__(self, layers, B, Hq, Hkv, d, n, L, seed, vocab=None, device="cuda"):
+    def __init__(self, layer_inputs, L, vocab=None, device="cuda"):
         import torch
-        from workloads import make_layer_device
-        self.B, self.Hq, self.Hkv, self.d, self.n, self.L = B, Hq, Hkv, d, n, L
-        self.seed = seed
-        self.layer_inputs = [make_layer_device(seed, l, B, Hq, Hkv, d, n, L, device)
-                             for l in range(layers)]
-        self.seq_lens = torch.full((B,), L, dtype=torch.int32, device=device)
-        self.split_len, self.num_splits = rv.rv_prefix_default_split(L, B, Hq, Hkv, n, d)
+        self.layer_inputs = list(layer_inputs)
+        B, Hq, n, d = self.layer_inputs[0][0].shape
+        Hkv = self.layer_inputs[0][1].shape[1]
+        layers = len(self.layer_inputs)
+        self.B, self.Hq, self.Hkv, self.d, self.n, self.L = B, Hq, Hkv, d, n, int(L)
+        self.seq_lens = torch.full((B,), self.L, dtype=torch.int32, device=device)
+        self.split_len, self.num_splits = rv.rv_prefix_default_split(self.L, B, Hq, Hkv, n, d)
         S = self.num_splits
         f32 = torch.float32
         self.o_part = torch.empty((B, Hq, n, S, d), dtype=f32, device=device)

@@ -13,7 +13,7 @@ import torch
 
 from oracle import attn_ref, rapid_accept_ref
 from oracle.compare import ATTN_ROW_TOL, attn_row_errors, compare_accept
-from workloads import CONFIGS, MODEL_CONFIGS, config_vocab
+from workloads import CONFIGS, MODEL_CONFIGS, config_vocab, make_layer_device
 from speculative_decoding_verify_split_amd.step import ModelStep
 
 pytestmark = pytest.mark.gpu
@@ -34,8 +34,9 @@ def test_model_step_graph_replay_and_oracle():
     c = CONFIGS[mc["layer_config"]]
     announce("generating %d layers on the device" % mc["layers"])
     vi = config_vocab(mc["layer_config"], eta=0.5)
-    ms = ModelStep(mc["layers"], c["B"], c["Hq"], c["Hkv"], c["d"], c["gamma"] + 1, c["L"],
-                   mc["seed"], vocab=vi)
+    layers = [make_layer_device(mc["seed"], l, c["B"], c["Hq"], c["Hkv"], c["d"], c["gamma"] + 1,
+                                c["L"]) for l in range(mc["layers"])]
+    ms = ModelStep(layers, c["L"], vocab=vi)
     announce("eager model step")
     ms.run()
     torch.cuda.synchronize()
@@ -66,7 +67,7 @@ def test_model_step_graph_replay_and_oracle():
 
     res = compare_accept(rapid_accept_ref(vi.z, vi.y, vi.draft, vi.r, vi.u, vi.T, vi.eta),
                          ms.vocab.n_accept.cpu().numpy(), ms.vocab.out_tokens.cpu().numpy(),
-                         vi.r, vi.u)
+                         vi.r, vi.u, draft=vi.draft)
     assert not res["errors"], res["errors"]
 
     out = ms.out.float().cpu().numpy()

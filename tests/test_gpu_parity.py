@@ -399,7 +399,7 @@ def _check_accept(vi, st, tag, flags=0):
                     "fp64 may place on different sides" % tag)
     n_g = st.n_accept.cpu().numpy()
     tok = st.out_tokens.cpu().numpy()
-    res = compare_accept(ref, n_g, tok, vi.r, vi.u)
+    res = compare_accept(ref, n_g, tok, vi.r, vi.u, draft=vi.draft)
     ratio = st.ratio.cpu().numpy()
     dr = np.abs(ratio - ref["ratio"]).max()
     dp = None
@@ -516,7 +516,7 @@ def test_accept_bad_draft_id_sentinel():
     assert np.all(tok[1] == -1) and np.all(tok[2] == -1)
     good = make_vocab(48, B=3, gamma=4, V=5000, z_sigma=3.0, noise=1.0, T=1.0, eta=0.5)
     ref = rapid_accept_ref(good.z[:1], good.y[:1], good.draft[:1], good.r[:1], good.u[:1], 1.0, 0.5)
-    res = compare_accept(ref, n_g[:1], tok[:1], good.r[:1], good.u[:1])
+    res = compare_accept(ref, n_g[:1], tok[:1], good.r[:1], good.u[:1], draft=good.draft[:1])
     assert not res["errors"]
 
 

@@ -1,0 +1,236 @@
+"""Pins for the GPU-vs-oracle comparison rules (CPU only).
+
+Every token and n_accept verdict of the GPU tests goes through
+oracle.compare.compare_accept, so it is checked here on outputs built by
+hand around an oracle result: the rules it must apply are those of the
+acceptance procedure (RAPID blog post, section 2.1 "Background: speculative
+decoding": the first rejection cuts the chain and one token is drawn there;
+section 2.4: p_hat in place of p), with the boundary flagging at 1e-4.
+"""
+
+import numpy as np
+
+from oracle import rapid_accept_ref
+from oracle.compare import BOUNDARY_TOL, attn_row_errors, compare_accept
+
+TOL = BOUNDARY_TOL
+
+
+def _case(r=None, u=None):
+    """One sequence, gamma = 3, V = 6, hand-picked logits whose residual at
+    every row has both positive and zero entries."""
+    z = np.array([[[2.0, 0.5, -1.0, 1.0, 0.0, -0.5],
+                   [0.3, 1.5, 0.2, -0.7, 1.1, 0.0],
+                   [1.2, -0.3, 0.8, 0.8, -1.5, 0.4],
+                   [0.0, 0.9, -0.2, 1.7, 0.3, -1.0]]])
+    y = np.array([[[1.0, 1.5, -1.0, 0.2, 0.0, -0.5],
+                   [0.9, 0.4, 0.2, -0.1, 1.6, -0.8],
+                   [0.2, 0.1, 1.8, 0.3, -1.0, 0.4]]])
+    draft = np.array([[1, 4, 2]])
+    T, eta = 1.0, 0.5
+    r0 = np.array([[0.5, 0.5, 0.5]]) if r is None else np.array([r], dtype=np.float64)
+    u0 = np.array([[0.37, 0.37, 0.37, 0.37]]) if u is None else np.array([u], dtype=np.float64)
+    ref = rapid_accept_ref(z, y, draft, r0, u0, T, eta)
+    return z, y, draft, r0, u0, T, eta, ref
+
+
+def _ratios():
+    return _case()[-1]["ratio"][0]
+
+
+def _reject_at(t_star, flag_t=None):
+    """Uniforms that accept rows < t_star and reject row t_star, each at
+    least 0.05 from its ratio unless it is flag_t, which sits at ratio +
+    tol/2 (a flagged rejection)."""
+    ratio = _ratios()
+    r = []
+    for t in range(3):
+        if t == flag_t:
+            r.append(ratio[t] + 0.5 * TOL)
+        elif t < t_star:
+            r.append(max(0.0, ratio[t] - 0.05))
+        else:
+            r.append(min(0.999, ratio[t] + 0.05))
+    return r
+
+
+def test_case_has_rejections_and_zero_weights():
+    ratio = _ratios()
+    assert np.all(ratio < 0.9) and np.all(ratio > 0.1)
+    ref = _case(r=_reject_at(1))[-1]
+    assert ref["n_accept"][0] == 1
+    w = ref["draw"][0]["w"]
+    assert np.any(w == 0) and np.any(w > 0)
+
+
+def test_identical_outputs_pass():
+    for t_star in range(4):
+        z, y, draft, r, u, T, eta, ref = _case(r=_reject_at(t_star))
+        assert ref["n_accept"][0] == t_star
+        res = compare_accept(ref, ref["n_accept"], ref["out_tokens"], r, u, draft=draft)
+        assert res["errors"] == [] and res["diverged"] == 0
+        assert res["flagged_accept"] == 0 and res["flagged_draw"] == 0
+
+
+def test_wrong_unflagged_n_accept_is_an_error():
+    z, y, draft, r, u, T, eta, ref = _case(r=_reject_at(1))
+    for n_bad in (0, 2, 3):
+        tok = np.full((1, 4), -1)
+        tok[0, :n_bad] = draft[0, :n_bad]
+        tok[0, n_bad] = 0
+        res = compare_accept(ref, [n_bad], tok, r, u, draft=draft)
+        assert res["errors"] and res["diverged"] == 0, n_bad
+
+
+def test_n_accept_outside_range_is_an_error_whatever_the_flags():
+    # The last draft's uniform sits on its ratio: a negative index must not
+    # read that flag and call the sequence "diverged".
+    ratio = _ratios()
+    r = [ratio[0] + 0.05, ratio[1] - 0.05, ratio[2]]
+    z, y, draft, r, u, T, eta, ref = _case(r=r)
+    for n_bad in (-1, -2, 4, 7):
+        tok = np.full((1, 4), -1)
+        res = compare_accept(ref, [n_bad], tok, r, u, draft=draft)
+        assert res["errors"], n_bad
+        assert res["diverged"] == 0
+
+
+def test_wrong_unflagged_token_is_an_error():
+    z, y, draft, r, u, T, eta, ref = _case(r=_reject_at(2))
+    tok = ref["out_tokens"].copy()
+    k = tok[0, 2]
+    w = ref["draw"][0]["w"]
+    other = [j for j in range(6) if j != k and w[j] > 0][0]
+    tok[0, 2] = other
+    res = compare_accept(ref, ref["n_accept"], tok, r, u, draft=draft)
+    assert res["errors"] and res["flagged_draw"] == 0
+    tok[0, 2] = 6  # out of the vocabulary
+    assert compare_accept(ref, ref["n_accept"], tok, r, u, draft=draft)["errors"]
+
+
+def test_wrong_accepted_prefix_is_an_error():
+    z, y, draft, r, u, T, eta, ref = _case(r=_reject_at(2))
+    tok = ref["out_tokens"].copy()
+    tok[0, 1] = (tok[0, 1] + 1) % 6
+    assert compare_accept(ref, ref["n_accept"], tok, r, u, draft=draft)["errors"]
+    assert compare_accept(ref, ref["n_accept"], tok, r, u)["errors"]
+
+
+def test_tokens_past_the_draw_must_be_minus_one():
+    z, y, draft, r, u, T, eta, ref = _case(r=_reject_at(1))
+    for j in (2, 3):
+        tok = ref["out_tokens"].copy()
+        tok[0, j] = 0
+        assert compare_accept(ref, ref["n_accept"], tok, r, u, draft=draft)["errors"], j
+
+
+def _edge_uniform(row, k_edge, r):
+    """A uniform whose target u*W lies tol/2 below C[k_edge] at draw row
+    `row` (the oracle then picks the first positive id at or below k_edge
+    whose interval holds the target)."""
+    ref = _case(r=r)[-1]
+    d = ref["draw"][0]
+    assert d["row"] == row
+    C, W = d["C"], d["W"]
+    u = (C[k_edge] - 0.5 * TOL * W) / W
+    uu = [0.37] * 4
+    uu[row] = u
+    return uu
+
+
+def test_flagged_draw_inside_the_widened_interval_passes():
+    r = _reject_at(1)
+    ref0 = _case(r=r)[-1]
+    w = ref0["draw"][0]["w"]
+    pos = [j for j in range(6) if w[j] > 0]
+    k = pos[0]
+    nxt = pos[1]  # next id of positive weight
+    u = _edge_uniform(1, k, r)
+    z, y, draft, r, u, T, eta, ref = _case(r=r, u=u)
+    assert ref["out_tokens"][0, 1] == k
+    tok = ref["out_tokens"].copy()
+    res = compare_accept(ref, ref["n_accept"], tok, r, u, draft=draft)
+    assert res["errors"] == [] and res["flagged_draw"] == 1
+    tok[0, 1] = nxt  # across the edge, within tol*W of it
+    res = compare_accept(ref, ref["n_accept"], tok, r, u, draft=draft)
+    assert res["errors"] == [] and res["flagged_draw"] == 1
+
+
+def test_flagged_draw_outside_the_interval_or_on_zero_weight_fails():
+    r = _reject_at(1)
+    ref0 = _case(r=r)[-1]
+    w = ref0["draw"][0]["w"]
+    pos = [j for j in range(6) if w[j] > 0]
+    zero = [j for j in range(6) if w[j] == 0]
+    k = pos[0]
+    u = _edge_uniform(1, k, r)
+    z, y, draft, r, u, T, eta, ref = _case(r=r, u=u)
+    tok = ref["out_tokens"].copy()
+    tok[0, 1] = pos[-1]  # far from the target
+    if pos[-1] != pos[1]:
+        res = compare_accept(ref, ref["n_accept"], tok, r, u, draft=draft)
+        assert res["errors"] and res["flagged_draw"] == 1
+    for j in zero:  # zero-weight ids are never a valid draw, widened or not
+        tok[0, 1] = j
+        res = compare_accept(ref, ref["n_accept"], tok, r, u, draft=draft)
+        assert res["errors"], j
+
+
+def test_disagreement_at_a_flagged_accept_counts_as_diverged():
+    # Oracle: accept row 0, reject row 1 (r_1 = ratio_1 + tol/2, flagged);
+    # row 2's uniform is well below its ratio.  A GPU that accepted row 1
+    # and row 2 and drew the bonus is consistent with the flag.
+    ratio = _ratios()
+    r = [ratio[0] - 0.05, ratio[1] + 0.5 * TOL, ratio[2] - 0.05]
+    z, y, draft, r, u, T, eta, ref = _case(r=r)
+    assert ref["n_accept"][0] == 1
+    tok = np.array([[draft[0, 0], draft[0, 1], draft[0, 2], 3]])
+    res = compare_accept(ref, [3], tok, r, u, draft=draft)
+    assert res["errors"] == [] and res["diverged"] == 1 and res["flagged_accept"] == 1
+    # The GPU's continuation past the flag must still agree with the
+    # oracle's unflagged decisions: rejecting row 2 there is an error.
+    tok = np.array([[draft[0, 0], draft[0, 1], 0, -1]])
+    res = compare_accept(ref, [2], tok, r, u, draft=draft)
+    assert res["errors"] and res["diverged"] == 0
+    # ... and its accepted prefix and tail are checked too.
+    tok = np.array([[draft[0, 0], (draft[0, 1] + 1) % 6, draft[0, 2], 3]])
+    assert compare_accept(ref, [3], tok, r, u, draft=draft)["errors"]
+    tok = np.array([[draft[0, 0], draft[0, 1], 5, 3]])  # n=2: slot 3 must be -1
+    assert compare_accept(ref, [2], tok, r, u, draft=draft)["errors"]
+
+
+def test_disagreement_at_an_unflagged_accept_is_an_error():
+    ratio = _ratios()
+    r = [ratio[0] - 0.05, ratio[1] + 0.05, ratio[2] - 0.05]
+    z, y, draft, r, u, T, eta, ref = _case(r=r)
+    tok = np.array([[draft[0, 0], draft[0, 1], draft[0, 2], 3]])
+    res = compare_accept(ref, [3], tok, r, u, draft=draft)
+    assert res["errors"] and res["diverged"] == 0
+
+
+def test_batch_counts_are_per_sequence():
+    ratio = _ratios()
+    cases = [_case(r=_reject_at(1)), _case(r=[ratio[0] + 0.5 * TOL, 0.5, 0.5])]
+    z = np.concatenate([c[0] for c in cases])
+    y = np.concatenate([c[1] for c in cases])
+    draft = np.concatenate([c[2] for c in cases])
+    r = np.concatenate([c[3] for c in cases])
+    u = np.concatenate([c[4] for c in cases])
+    ref = rapid_accept_ref(z, y, draft, r, u, 1.0, 0.5)
+    res = compare_accept(ref, ref["n_accept"], ref["out_tokens"], r, u, draft=draft)
+    assert res["errors"] == [] and res["flagged_accept"] == 1
+    n = ref["n_accept"].copy()
+    n[0] = -1
+    res = compare_accept(ref, n, ref["out_tokens"], r, u, draft=draft)
+    assert len(res["errors"]) == 1 and res["errors"][0].startswith("b=0")
+
+
+def test_attn_row_errors_hand_values():
+    o_ref = np.array([[1.0, -2.0, 0.5], [0.1, 0.0, -0.1]])
+    o_gpu = np.array([[1.01, -2.0, 0.5], [0.1, 0.02, -0.1]])
+    e = attn_row_errors(o_gpu, o_ref)
+    assert e.shape == (2,)
+    np.testing.assert_allclose(e, [0.01 / 2.0, 0.02 / 0.1], rtol=1e-12)
+    # the error is per row: a bad row does not hide behind a good one
+    assert e[0] < 2e-2 < e[1]
+    np.testing.assert_array_equal(attn_row_errors(o_ref, o_ref), [0.0, 0.0])
