@@ -28,6 +28,17 @@ import numpy as np
 ATTN_ROW_TOL = 2e-2
 P_HAT_TOL = 1e-5
 BOUNDARY_TOL = 1e-4
+# Log-sum-exp of attention rows.  Where the row sum adds the same bf16-rounded
+# probabilities that multiply V (matrix-core row sums), each term carries a
+# relative rounding error of at most 2^-8 (bf16 has 8 significant bits), so
+# the sum does too and |dLSE| <= -ln(1 - 2^-8) = 3.9e-3.  With fp32 sums the
+# error is a few fp32 ulps of the scores; 1e-4 leaves room for the hardware
+# exp2/log2 approximations.
+LSE_TOL_BF16_SUMS = 4e-3
+LSE_TOL_FP32 = 1e-4
+# Block partial computed in fp32 on the vector ALU: absolute bound on its
+# outputs (entries are O(1)).
+BLOCK_FP32_TOL = 1e-4
 
 
 def attn_row_errors(o_gpu, o_ref):
@@ -63,6 +74,7 @@ def compare_accept(ref, n_gpu, tok_gpu, r, u, tol=BOUNDARY_TOL, draft=None):
     diverged = 0
     flagged_accept = 0
     flagged_draw = 0
+    exact_draws = 0
     tok_gpu = np.asarray(tok_gpu)
     B, g1 = tok_gpu.shape
     gamma = g1 - 1
@@ -117,5 +129,26 @@ def compare_accept(ref, n_gpu, tok_gpu, r, u, tol=BOUNDARY_TOL, draft=None):
         elif kg != k:
             errors.append("b=%d: drawn token %d != oracle %d (u*W=%r, [%r, %r))"
                           % (b, kg, k, tgt, lo, hi))
+        else:
+            exact_draws += 1
     return {"errors": errors, "diverged": diverged, "flagged_accept": flagged_accept,
-            "flagged_draw": flagged_draw}
+            "flagged_draw": flagged_draw, "exact_draws": exact_draws}
+
+
+def flag_counts(ref, r, tol):
+    """Flagged positions of an oracle result at boundary distance `tol`,
+    without any GPU output: accept steps the oracle evaluated with
+    |r_t - ratio_t| <= tol, and draws whose target u*W lies within tol*W of
+    an edge of the chosen interval.  Returns (flagged_accept, flagged_draw,
+    draws)."""
+    fa = fd = 0
+    B, gamma = np.asarray(ref["ratio"]).shape
+    for b in range(B):
+        n_ref = int(ref["n_accept"][b])
+        fa += sum(abs(float(r[b, t]) - float(ref["ratio"][b, t])) <= tol
+                  for t in range(min(n_ref + 1, gamma)))
+        dr = ref["draw"][b]
+        C, W, tgt, k = dr["C"], dr["W"], dr["target"], dr["k"]
+        lo = C[k - 1] if k > 0 else 0.0
+        fd += min(abs(tgt - lo), abs(tgt - C[k])) <= tol * W
+    return fa, fd, B

@@ -1,9 +1,11 @@
 """GPU parity: librapid_verify.so (through its C ABI) against the fp64 oracle.
 
 Small cases compare every output element; the five workloads at full size run
-in the launch configuration the benchmark times and are compared on sampled
-heads (attention) and in full (vocabulary pass), plus properties that hold at
-any size.  Tolerances and boundary flagging follow oracle/compare.py.
+in the launch configuration the benchmark times and are compared on every
+query head (attention) and in full (vocabulary pass), plus properties that
+hold at any size; many-sequence sweeps at the workloads' vocabulary sizes
+compare hundreds of draws.  Tolerances and boundary flagging follow
+oracle/compare.py.
 """
 
 import sys
@@ -14,7 +16,9 @@ import torch
 
 from oracle import (attn_keys_ref, attn_ref, bf16_bits_to_f64, block_visibility, lse_merge_ref,
                     rapid_accept_ref, retrieval_augmented_target)
-from oracle.compare import ATTN_ROW_TOL, P_HAT_TOL, attn_row_errors, compare_accept
+from oracle.compare import (ATTN_ROW_TOL, BLOCK_FP32_TOL, BOUNDARY_TOL, LSE_TOL_BF16_SUMS,
+                            LSE_TOL_FP32, P_HAT_TOL, attn_row_errors, compare_accept,
+                            flag_counts)
 from workloads import (CONFIGS, config_attention, config_vocab, make_attention, make_vocab,
                        tree_parents)
 from speculative_decoding_verify_split_amd.rapid_verify import (RV_ACCEPT_PRINTED_RESIDUAL,
@@ -31,6 +35,13 @@ def announce(msg):
 
 def _tree(seed, n, depth):
     return tree_parents(np.random.SeedSequence(seed), n, depth)
+
+
+def _lse_tol(Hq, Hkv, n):
+    """Bound on |dLSE| of a history pass: groups of more than 64 rows per kv
+    head go to the shared-stage kernel, whose row sums add the bf16-rounded
+    probabilities on the matrix cores; narrower groups sum them in fp32."""
+    return LSE_TOL_BF16_SUMS if (Hq // Hkv) * n > 64 else LSE_TOL_FP32
 
 
 def _attn_outputs(st):
@@ -95,9 +106,11 @@ def test_attention_small(case):
         announce("  %s: max row rel err %.3e, max |dLSE| %.3e"
                  % ("block_merge" if fused else "block+merge", err.max(), dl))
         assert err.max() <= ATTN_ROW_TOL
-        assert dl <= 1e-2
+        assert dl <= _lse_tol(ai.q.shape[1], ai.k_cache.shape[1], ai.q.shape[2])
         res[fused] = (out, lse)
-    # the fused call differs from the two calls only in fp32 rounding order
+    # the fused call differs from the two calls only in fp32 rounding order,
+    # so their bf16 outputs differ by at most one bf16 step (2^-7 of an
+    # entry's binade): 7.8e-3 of the row's largest entry
     assert attn_row_errors(res[True][0], res[False][0]).max() <= 1e-2
     assert np.abs(res[True][1] - res[False][1]).max() <= 1e-4
 
@@ -127,7 +140,8 @@ def test_prefix_and_block_partials_match_split_oracle(case):
     o_blk = st.o_blk.cpu().numpy()
     lse_blk = st.lse_blk.cpu().numpy()
     B, Hq, n, d = ai.q.shape
-    G = Hq // ai.k_cache.shape[1]
+    Hkv = ai.k_cache.shape[1]
+    G = Hq // Hkv
     split_len, S = split
     vis = block_visibility(n, ai.parent)
     for b in range(B):
@@ -145,13 +159,13 @@ def test_prefix_and_block_partials_match_split_oracle(case):
                                      bf16_bits_to_f64(ai.v_cache[b, g, lo:hi]),
                                      np.ones((n, hi - lo), bool), 1.0)
                 assert attn_row_errors(o_part[b, h, :, s], o).max() <= ATTN_ROW_TOL
-                assert np.abs(lse_part[b, h, :, s] - l).max() <= 1e-2
+                assert np.abs(lse_part[b, h, :, s] - l).max() <= _lse_tol(Hq, Hkv, n)
             o, l = attn_keys_ref(q, bf16_bits_to_f64(ai.k_blk[b, g]), bf16_bits_to_f64(ai.v_blk[b, g]),
                                  vis, 1.0)
-            # the block part runs on the same bf16 MFMA path as the history
-            # splits, so it is held to the same attention tolerance
-            assert attn_row_errors(o_blk[b, h], o).max() <= ATTN_ROW_TOL
-            assert np.abs(lse_blk[b, h] - l).max() <= 1e-2
+            # the block part is fp32 on the vector ALU (bf16 inputs widened
+            # exactly), so it is held to an fp32 bound
+            assert np.abs(o_blk[b, h] - o).max() <= BLOCK_FP32_TOL
+            assert np.abs(lse_blk[b, h] - l).max() <= BLOCK_FP32_TOL
 
 
 # ------------------------------------------------ seeded random shapes
@@ -204,7 +218,7 @@ def test_attention_random_shapes(case):
         dl = np.abs(lse - L_ref).max()
         announce("  %s: max row rel err %.3e, max |dLSE| %.3e"
                  % ("block_merge" if fused else "block+merge", err, dl))
-        assert err <= ATTN_ROW_TOL and dl <= 1e-2
+        assert err <= ATTN_ROW_TOL and dl <= _lse_tol(Hq, Hkv, n)
 
 
 def _random_vocab_cases(seed=78, count=16):
@@ -352,7 +366,24 @@ def test_seq_lens_are_clamped_on_the_device():
     eff = np.array([640, 0, 300])
     O_ref, L_ref = attn_ref(ai.q, ai.k_cache, ai.v_cache, ai.k_blk, ai.v_blk, eff)
     assert attn_row_errors(out, O_ref).max() <= ATTN_ROW_TOL
-    assert np.abs(lse - L_ref).max() <= 1e-2
+    assert np.abs(lse - L_ref).max() <= _lse_tol(4, 2, 4)
+
+
+@pytest.mark.parametrize("G", [2, 8])
+def test_seq_lens_beyond_the_splits_are_cut_at_their_capacity(G):
+    """A device length in (S*split_len, L_max] attends over the first
+    S*split_len tokens only (the partials hold S splits); both kernels."""
+    ai = make_attention(35, 2, 2 * G, 2, 128, 11, [500, 200], L_max=1000)
+    announce("seq_lens past the splits, G=%d" % G)
+    st = VerifyStep(ai, None, split=(256, 2))
+    st.seq_lens.copy_(torch.tensor([900, 513], dtype=torch.int32))
+    for fused in (False, True):
+        st.attention(fused=fused)
+        out, lse = _attn_outputs(st)
+        O_ref, L_ref = attn_ref(ai.q, ai.k_cache, ai.v_cache, ai.k_blk, ai.v_blk,
+                                np.array([512, 512]))
+        assert attn_row_errors(out, O_ref).max() <= ATTN_ROW_TOL
+        assert np.abs(lse - L_ref).max() <= _lse_tol(2 * G, 2, 11)
 
 
 def test_sm_scale_is_applied():
@@ -365,7 +396,7 @@ def test_sm_scale_is_applied():
     O_ref, L_ref = attn_ref(ai.q, ai.k_cache, ai.v_cache, ai.k_blk, ai.v_blk, ai.seq_lens,
                             sm_scale=0.37)
     assert attn_row_errors(out, O_ref).max() <= ATTN_ROW_TOL
-    assert np.abs(lse - L_ref).max() <= 1e-2
+    assert np.abs(lse - L_ref).max() <= _lse_tol(4, 2, 5)
 
 
 # ------------------------------------------------------ vocabulary, small
@@ -568,17 +599,11 @@ def test_step_is_bit_deterministic():
 
 # ------------------------------------------- the five workloads, full size
 
-def _sample_pairs(ai, name):
-    B, Hq = ai.q.shape[:2]
-    if B == 1:
-        return list(dict.fromkeys([(0, 0), (0, Hq // 2 + 1), (0, Hq - 1)]))
-    lens = ai.seq_lens
-    return [(int(np.argmin(lens)), 1), (int(np.argmax(lens)), Hq - 2), (3 % B, Hq // 2)]
-
-
 def _config_attention_check(name):
     announce("generating %s attention inputs" % name)
     ai = config_attention(name)
+    B, Hq, n, d = ai.q.shape
+    Hkv = ai.k_cache.shape[1]
     announce("attention %s shape=%s" % (name, ai.shape))
     st = VerifyStep(ai, None)  # default split: the benchmark's launch configuration
     st.attention()
@@ -591,20 +616,31 @@ def _config_attention_check(name):
     for o, l in ((out, lse), (out_f, lse_f)):
         assert np.isfinite(o).all() and np.isfinite(l).all()
         assert np.all(l >= np.maximum(lse_part.max(axis=-1), lse_blk) - 1e-4)
-    assert attn_row_errors(out_f, out).max() <= 1e-2
+    assert attn_row_errors(out_f, out).max() <= 1e-2  # one bf16 step, as above
     assert np.abs(lse_f - lse).max() <= 1e-4
-    pairs = _sample_pairs(ai, name)
-    announce("  oracle on sampled heads %s" % pairs)
-    O_ref, L_ref = attn_ref(ai.q, ai.k_cache, ai.v_cache, ai.k_blk, ai.v_blk, ai.seq_lens,
-                            ai.parent, ai.sm_scale, pairs=pairs)
-    for i, (b, h) in enumerate(pairs):
-        for tag, o, l in (("block+merge", out, lse), ("block_merge", out_f, lse_f)):
-            err = attn_row_errors(o[b, h], O_ref[i])
-            dl = np.abs(l[b, h] - L_ref[i]).max()
-            announce("  %s (b=%d,h=%d) max row rel err %.3e |dLSE| %.3e"
-                     % (tag, b, h, err.max(), dl))
-            assert err.max() <= ATTN_ROW_TOL
-            assert dl <= 1e-2
+    # every (sequence, query head, row) against the oracle, one kv head at a
+    # time (the oracle's scores for a kv head are G*n rows by the history)
+    tol = _lse_tol(Hq, Hkv, n)
+    worst = {False: (0.0, 0.0), True: (0.0, 0.0)}
+    G = Hq // Hkv
+    for b in range(B):
+        for g in range(Hkv):
+            heads = list(range(g * G, (g + 1) * G))
+            O_ref, L_ref = attn_ref(ai.q[b:b + 1, g * G:(g + 1) * G], ai.k_cache[b:b + 1, g:g + 1],
+                                    ai.v_cache[b:b + 1, g:g + 1], ai.k_blk[b:b + 1, g:g + 1],
+                                    ai.v_blk[b:b + 1, g:g + 1], ai.seq_lens[b:b + 1], ai.parent,
+                                    ai.sm_scale)
+            for fused, o, l in ((False, out, lse), (True, out_f, lse_f)):
+                err = attn_row_errors(o[b, heads], O_ref[0]).max()
+                dl = np.abs(l[b, heads] - L_ref[0]).max()
+                worst[fused] = (max(worst[fused][0], err), max(worst[fused][1], dl))
+                assert err <= ATTN_ROW_TOL, (b, g, fused, err)
+                assert dl <= tol, (b, g, fused, dl)
+        announce("  b=%d: %d query heads x %d rows checked" % (b, Hq, n))
+    for fused in (False, True):
+        announce("  %s: max row rel err %.3e, max |dLSE| %.3e over all %d rows"
+                 % ("block_merge" if fused else "block+merge", worst[fused][0], worst[fused][1],
+                    B * Hq * n))
 
 
 # (llama8b_tp8: one GPU's share under 8-way head parallelism; its default
@@ -662,3 +698,61 @@ def test_config_vocab(name, eta):
     vi = config_vocab(name, eta=eta)
     announce("rapid_accept %s eta=%s B=%d gamma=%d V=%d" % (name, vi.eta, *vi.y.shape))
     _check_accept(vi, _run_accept(vi), "%s eta=%s" % (name, vi.eta))
+
+
+# Many sequences at the workloads' vocabulary sizes: every setting's draws
+# compared one by one (bit-exact outside flagged positions).  About 40% of
+# the draws at V ~ 1.3e5 fall within 1e-4 of an interval edge (the residual
+# mass spreads over ~10^3 ids), so 384 sequences leave well over 150
+# unflagged draws per setting.
+SWEEP = [("llama8b", 0.0), ("llama8b", 0.5), ("llama8b", 2.0), ("llama70b", 1.0),
+         ("qwen7b_ragged", 0.5)]
+
+
+@pytest.mark.parametrize("name,eta", SWEEP, ids=["%s-eta%g" % c for c in SWEEP])
+@pytest.mark.timeout(900)
+def test_config_vocab_many_sequences(name, eta):
+    B = 384
+    vi = config_vocab(name, eta=eta, B_override=B)
+    announce("rapid_accept sweep %s eta=%g T=%g B=%d gamma=%d V=%d"
+             % (name, eta, vi.T, B, vi.y.shape[1], vi.y.shape[2]))
+    st = _run_accept(vi, p_hat=False)
+    ref, res = _check_accept(vi, st, "%s eta=%g sweep" % (name, eta))
+    fa6, fd6, _ = flag_counts(ref, vi.r, 1e-6)
+    fa4, fd4, _ = flag_counts(ref, vi.r, BOUNDARY_TOL)
+    alpha = float(np.mean([np.sum(np.minimum(ref["p_hat"][b, t], _q_row(vi, b, t)))
+                           for b in range(4) for t in range(vi.y.shape[1])]))
+    announce("  exact draws %d of %d; flagged accepts %d (1e-4) / %d (1e-6); flagged draws "
+             "%d (1e-4) / %d (1e-6); diverged %d; mean n_accept %.3f; alpha (4 seqs) %.3f"
+             % (res["exact_draws"], B, fa4, fa6, fd4, fd6, res["diverged"],
+                float(np.mean(ref["n_accept"])), alpha))
+    assert res["exact_draws"] >= 150
+    assert res["diverged"] <= 3
+
+
+def _q_row(vi, b, t):
+    from oracle import draft_probs
+    return draft_probs(vi.y[b, t], vi.T)
+
+
+# Chunking edges of the vocabulary pass: a vocabulary of exactly one decide
+# chunk, an odd one (scalar loads), gamma = 16 and 20, and V = 300000, whose
+# draw scans more than one block of 256 decide chunks.
+ACCEPT_EDGE_CASES = [
+    ("V100000-g16-b2", dict(seed=51, B=2, gamma=16, V=100000, z_sigma=3.0, noise=1.0, T=1.0, eta=0.5)),
+    ("V5001-g20-b3", dict(seed=52, B=3, gamma=20, V=5001, z_sigma=3.0, noise=1.0, T=0.8, eta=1.5)),
+    ("V300000-g4-b2", dict(seed=53, B=2, gamma=4, V=300000, z_sigma=3.0, noise=1.0, T=1.0, eta=0.5)),
+    ("V1024-g10-b3", dict(seed=54, B=3, gamma=10, V=1024, z_sigma=3.0, noise=1.0, T=1.0, eta=0.5)),
+]
+
+
+@pytest.mark.parametrize("flags", [0, RV_ACCEPT_TAIL_PRESERVE | RV_ACCEPT_PRINTED_RESIDUAL])
+@pytest.mark.parametrize("case", ACCEPT_EDGE_CASES, ids=[c[0] for c in ACCEPT_EDGE_CASES])
+def test_accept_chunking_edges(case, flags):
+    name, kw = case
+    vi = make_vocab(**kw)
+    if flags & RV_ACCEPT_TAIL_PRESERVE and _tail_margin(vi) <= 1e-5:
+        pytest.skip("a p_hat entry lies within 1e-5 of the tail threshold, which fp32 and "
+                    "fp64 may place on different sides")
+    announce("rapid_accept %s flags=%d" % (name, flags))
+    _check_accept(vi, _run_accept(vi, flags=flags), "%s flags=%d" % (name, flags), flags)

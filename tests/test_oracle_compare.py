@@ -11,7 +11,7 @@ section 2.4: p_hat in place of p), with the boundary flagging at 1e-4.
 import numpy as np
 
 from oracle import rapid_accept_ref
-from oracle.compare import BOUNDARY_TOL, attn_row_errors, compare_accept
+from oracle.compare import BOUNDARY_TOL, attn_row_errors, compare_accept, flag_counts
 
 TOL = BOUNDARY_TOL
 
@@ -234,3 +234,23 @@ def test_attn_row_errors_hand_values():
     # the error is per row: a bad row does not hide behind a good one
     assert e[0] < 2e-2 < e[1]
     np.testing.assert_array_equal(attn_row_errors(o_ref, o_ref), [0.0, 0.0])
+
+
+def test_flag_counts_and_exact_draws():
+    ratio = _ratios()
+    r = [ratio[0] - 0.05, ratio[1] + 0.5 * TOL, 0.5]
+    z, y, draft, r, u, T, eta, ref = _case(r=r)
+    # rows 0 and 1 evaluated; row 1 flagged at 1e-4, not at 1e-6
+    assert flag_counts(ref, r, TOL)[0] == 1
+    assert flag_counts(ref, r, 1e-6)[0] == 0
+    res = compare_accept(ref, ref["n_accept"], ref["out_tokens"], r, u, draft=draft)
+    assert res["exact_draws"] == 1 - flag_counts(ref, r, TOL)[1]
+    # a draw placed tol/2 below an edge is flagged at 1e-4 only
+    rr = _reject_at(1)
+    k = [j for j in range(6) if _case(r=rr)[-1]["draw"][0]["w"][j] > 0][0]
+    uu = _edge_uniform(1, k, rr)
+    z, y, draft, r, u, T, eta, ref = _case(r=rr, u=uu)
+    assert flag_counts(ref, r, TOL)[1:] == (1, 1)
+    assert flag_counts(ref, r, 1e-6)[1:] == (0, 1)
+    res = compare_accept(ref, ref["n_accept"], ref["out_tokens"], r, u, draft=draft)
+    assert res["exact_draws"] == 0 and res["flagged_draw"] == 1
