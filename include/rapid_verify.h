@@ -332,6 +332,28 @@ rv_status rapid_accept_ex(const float* z, const float* y, const int32_t* draft, 
                           float* ratio_out, float* p_hat_out, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/*
+ * rapid_accept_noalloc -- rapid_accept_ex with no workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Its workspace is
+ * a static device array of RV_NOALLOC_SCRATCH_BYTES (4 MiB; one copy on each
+ * device the library runs on, held until the process ends); the call itself
+ * allocates and frees nothing.  Shapes whose workspace
+ * (rapid_accept_workspace_size) exceeds it return RV_ERR_WORKSPACE before
+ * any HIP call; the other arguments and their checks are those of
+ * rapid_accept_ex.  The first call on a device looks up that device's copy
+ * (hipGetSymbolAddress) and keeps the address; a failure there is
+ * RV_ERR_HIP.  Every call on one device shares that device's array, so calls
+ * that may overlap on one device (different streams) race and must not be
+ * made; calls in one stream are safe, each one clearing what it needs.
+ */
+#define RV_NOALLOC_SCRATCH_BYTES (4u << 20)
+rv_status rapid_accept_noalloc(const float* z, const float* y, const int32_t* draft,
+                               const float* r, const float* u, int B, int gamma, int V,
+                               float T, float eta, unsigned flags, int32_t* n_accept,
+                               int32_t* out_tokens, float* ratio_out, float* p_hat_out,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

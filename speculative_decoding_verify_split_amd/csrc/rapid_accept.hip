@@ -35,6 +35,8 @@
 // which workgroup runs the draw, so results are bit-exact run to run; no
 // workgroup ever waits for another.
 
+#include <mutex>
+
 #include "rv_device.h"
 #include "rv_internal.h"
 
@@ -722,4 +724,58 @@ extern "C" rv_status rapid_accept(const float* z, const float* y, const int32_t*
                                   size_t workspace_bytes, void* stream) {
   return rapid_accept_ex(z, y, draft, r, u, B, gamma, V, T, eta, 0u, n_accept, out_tokens,
                          ratio_out, p_hat_out, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// rapid_accept_noalloc: the same pass with its workspace in a static device
+// array, for callers that cannot allocate.  The array has one copy per device
+// (held until the process ends).  On the host its name stands for no device
+// address, so it is never passed to a kernel: each device's address comes
+// from hipGetSymbolAddress, taken once with that device current and kept.
+// The pass clears what must start at zero (its arrival counters) itself.
+
+static_assert(RV_NOALLOC_SCRATCH_BYTES == rv::kNoAllocScratchBytes, "scratch size");
+static __device__ __align__(256) unsigned char scratch[rv::kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices];
+
+rv_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return RV_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) return RV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return RV_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RV_OK;
+}
+}  // namespace
+
+extern "C" rv_status rapid_accept_noalloc(const float* z, const float* y, const int32_t* draft,
+                                          const float* r, const float* u, int B, int gamma,
+                                          int V, float T, float eta, unsigned flags,
+                                          int32_t* n_accept, int32_t* out_tokens,
+                                          float* ratio_out, float* p_hat_out, void* stream) {
+  rv_status st = rv::check_accept_args(z, y, draft, r, u, B, gamma, V, T, eta, flags, n_accept,
+                                       out_tokens);
+  if (st != RV_OK) return st;
+  if (rv::accept_layout(B, gamma, V).words * 4 > rv::kNoAllocScratchBytes)
+    return RV_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != RV_OK) return st;
+  return rapid_accept_ex(z, y, draft, r, u, B, gamma, V, T, eta, flags, n_accept, out_tokens,
+                         ratio_out, p_hat_out, ws, rv::kNoAllocScratchBytes, stream);
 }

@@ -113,6 +113,15 @@ AcceptLayout accept_layout(int B, int gamma, int V);
 
 constexpr unsigned kAcceptFlags = RV_ACCEPT_TAIL_PRESERVE | RV_ACCEPT_PRINTED_RESIDUAL;
 
+// Every argument check of rapid_accept except those of the workspace.
+rv_status check_accept_args(const float* z, const float* y, const int32_t* draft,
+                            const float* r, const float* u, int B, int gamma, int V, float T,
+                            float eta, unsigned flags, const int32_t* n_accept,
+                            const int32_t* out_tokens);
+
+// Largest workspace rapid_accept_noalloc's static scratch holds.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+
 rv_status check_accept(const float* z, const float* y, const int32_t* draft, const float* r,
                        const float* u, int B, int gamma, int V, float T, float eta, unsigned flags,
                        const int32_t* n_accept, const int32_t* out_tokens, const void* workspace,

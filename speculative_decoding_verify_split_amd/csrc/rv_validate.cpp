@@ -171,17 +171,28 @@ AcceptLayout accept_layout(int B, int gamma, int V) {
   return L;
 }
 
-rv_status check_accept(const float* z, const float* y, const int32_t* draft, const float* r,
-                       const float* u, int B, int gamma, int V, float T, float eta, unsigned flags,
-                       const int32_t* n_accept, const int32_t* out_tokens, const void* workspace,
-                       size_t workspace_bytes) {
-  if (!z || !y || !draft || !r || !u || !n_accept || !out_tokens || !workspace)
-    return RV_ERR_NULL;
+rv_status check_accept_args(const float* z, const float* y, const int32_t* draft,
+                            const float* r, const float* u, int B, int gamma, int V, float T,
+                            float eta, unsigned flags, const int32_t* n_accept,
+                            const int32_t* out_tokens) {
+  if (!z || !y || !draft || !r || !u || !n_accept || !out_tokens) return RV_ERR_NULL;
   if (B < 1 || gamma < 1 || V < 2) return RV_ERR_SHAPE;
   if (gamma > kMaxGamma || V > kMaxVocab || B > 65535) return RV_ERR_UNSUPPORTED;
   if (!(T > 0.0f) || !isfinite(T) || !isfinite(eta)) return RV_ERR_VALUE;
   if (flags & ~kAcceptFlags) return RV_ERR_VALUE;
-  if (!aligned16(z) || !aligned16(y) || !aligned16(workspace)) return RV_ERR_ALIGNMENT;
+  if (!aligned16(z) || !aligned16(y)) return RV_ERR_ALIGNMENT;
+  return RV_OK;
+}
+
+rv_status check_accept(const float* z, const float* y, const int32_t* draft, const float* r,
+                       const float* u, int B, int gamma, int V, float T, float eta, unsigned flags,
+                       const int32_t* n_accept, const int32_t* out_tokens, const void* workspace,
+                       size_t workspace_bytes) {
+  if (!workspace) return RV_ERR_NULL;
+  const rv_status st =
+      check_accept_args(z, y, draft, r, u, B, gamma, V, T, eta, flags, n_accept, out_tokens);
+  if (st != RV_OK) return st;
+  if (!aligned16(workspace)) return RV_ERR_ALIGNMENT;
   if (workspace_bytes < accept_layout(B, gamma, V).words * 4) return RV_ERR_WORKSPACE;
   return RV_OK;
 }

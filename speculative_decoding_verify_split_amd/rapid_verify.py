@@ -72,6 +72,9 @@ def load_library():
     lib.rapid_accept_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, ctypes.c_uint,
                                     vp, vp, vp, vp, vp, sz, vp]
     lib.rapid_accept_ex.restype = i32
+    lib.rapid_accept_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, f32,
+                                         ctypes.c_uint, vp, vp, vp, vp, vp]
+    lib.rapid_accept_noalloc.restype = i32
     _lib = lib
     return lib
 
@@ -292,7 +295,8 @@ def rapid_accept_workspace_size(B, gamma, V):
     return int(load_library().rapid_accept_workspace_size(B, gamma, V))
 
 
-def _accept_args(z, y, draft, r, u, n_accept, out_tokens, workspace, ratio_out, p_hat_out):
+def _accept_args(z, y, draft, r, u, n_accept, out_tokens, workspace, ratio_out, p_hat_out,
+                 need_workspace=True):
     import torch
     _need(z, "z", torch.float32)
     B, g1, V = z.shape
@@ -303,7 +307,8 @@ def _accept_args(z, y, draft, r, u, n_accept, out_tokens, workspace, ratio_out, 
     _need(u, "u", torch.float32, (B, g + 1))
     _need(n_accept, "n_accept", torch.int32, (B,))
     _need(out_tokens, "out_tokens", torch.int32, (B, g + 1))
-    _need(workspace, "workspace", torch.uint8)
+    if need_workspace:
+        _need(workspace, "workspace", torch.uint8)
     if ratio_out is not None:
         _need(ratio_out, "ratio_out", torch.float32, (B, g))
     if p_hat_out is not None:
@@ -334,3 +339,16 @@ def rapid_accept_ex(z, y, draft, r, u, T, eta, flags, n_accept, out_tokens, work
         _ptr(z), _ptr(y), _ptr(draft), _ptr(r), _ptr(u), B, g, V, float(T), float(eta),
         int(flags), _ptr(n_accept), _ptr(out_tokens), _ptr(ratio_out), _ptr(p_hat_out),
         _ptr(workspace), workspace.numel(), _stream(stream)), "rapid_accept_ex")
+
+
+def rapid_accept_noalloc(z, y, draft, r, u, T, eta, flags, n_accept, out_tokens, ratio_out=None,
+                         p_hat_out=None, stream=None):
+    """rapid_accept_ex with the library's static per-device scratch as its
+    workspace (no allocation by the call); calls that may overlap on one
+    device must not be made."""
+    B, g, V = _accept_args(z, y, draft, r, u, n_accept, out_tokens, None, ratio_out, p_hat_out,
+                           need_workspace=False)
+    _check(load_library().rapid_accept_noalloc(
+        _ptr(z), _ptr(y), _ptr(draft), _ptr(r), _ptr(u), B, g, V, float(T), float(eta),
+        int(flags), _ptr(n_accept), _ptr(out_tokens), _ptr(ratio_out), _ptr(p_hat_out),
+        _stream(stream)), "rapid_accept_noalloc")
