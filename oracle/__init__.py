@@ -35,6 +35,10 @@ patterns and are widened exactly; fp32 inputs are widened exactly.
   sink anchors over its constant-size ring cache (LongSpec summary, sections
   2.1 and 2.2), written as the definition over the visible positions.
 
+* ``tree`` -- acceptance over a draft tree: a rule from outside the pages
+  (they verify trees only as attention), recursive rejection among sibling
+  candidates with p_hat as the target, which reduces to ``rapid`` on a chain.
+
 Blog section 2.4 also prints a tail-preserving adjustment of p_hat and a
 different residual; both are available as options of ``rapid_accept_ref``
 (off by default) with the readings stated in ``rapid``.
@@ -65,4 +69,9 @@ from .rapid import (  # noqa: F401
     inverse_cdf_ref,
     rapid_accept_ref,
     tail_preserve_ref,
+)
+from .tree import (  # noqa: F401
+    rapid_tree_accept_ref,
+    residual_sequence,
+    tree_children,
 )
