@@ -34,7 +34,9 @@
  *                           caller's uniform; if every draft is kept, a bonus
  *                           token is drawn from the last row's p;
  *      rapid_accept_ex   -- the same with section 2.4's tail-preserving rule
- *                           and/or its printed residual as options.
+ *                           and/or its printed residual as options;
+ *      rapid_tree_accept -- the same over a draft tree, with a rule among
+ *                           sibling candidates taken from outside the pages.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -331,6 +333,54 @@ rv_status rapid_accept_ex(const float* z, const float* y, const int32_t* draft, 
                           unsigned flags, int32_t* n_accept, int32_t* out_tokens,
                           float* ratio_out, float* p_hat_out, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace rapid_tree_accept needs for (B, n, V), for any
+ * tree of n nodes. */
+size_t rapid_tree_accept_workspace_size(int B, int n, int V);
+
+/*
+ * rapid_tree_accept -- acceptance over a draft tree for B sequences that share
+ * one tree.  The pages verify trees only as attention (LongSpec summary,
+ * section 1 challenge 3 and section 2.3); the rule among siblings is taken
+ * from outside them (recursive rejection, with RAPID's p_hat as the target,
+ * RAPID blog post section 2.4): at node v the children are tested in
+ * ascending node id, child c with its uniform r[c] against a residual R that
+ * starts at p_hat_v and becomes norm(max(R - q_v, 0)) after each rejection,
+ * where q_v = softmax(y_v/T) and p_hat_v = softmax(z_v/T + eta (q_v - p_v));
+ * the first child accepted continues the walk; if every child is rejected a
+ * token is drawn from the last residual with u[v]; at a leaf a bonus token is
+ * drawn from p_v = softmax(z_v/T) with u[v].  On a chain (parent[i] = i - 1)
+ * this is rapid_accept.  Given the path, the token emitted at a node follows
+ * p_hat of the node when its children were drawn independently from its q.
+ *
+ *   z, y         fp32 [B, n, V]  target and drafter logits after each node
+ *                                (node 0 is the root, the last committed
+ *                                token; leaves' y rows are not read)
+ *   tokens       int32 [B, n]    draft token of each node (tokens[b][0] is
+ *                                not read)
+ *   parent_host  HOST int32 [n]  parent[0] == -1, 0 <= parent[i] < i (else
+ *                                RV_ERR_VALUE); 1 <= n <= 64
+ *   r, u         fp32 [B, n]     acceptance uniform of each node, sampling
+ *                                uniform used if the walk stops at the node
+ *   T > 0, eta finite
+ *   n_accept     int32 [B]       out: nodes accepted on the path (-1 if a
+ *                                token of a non-root node is outside [0, V))
+ *   path         int32 [B, n]    out: the accepted node ids in order, then -1
+ *   out_tokens   int32 [B, n]    out: their tokens, then the drawn token,
+ *                                then -1
+ *   ratio_out    fp32 [B, n] or NULL  out: the ratio min(1, R[x_c]/q[x_c]) of
+ *                                every child tested on the path, NaN elsewhere
+ *   workspace    device scratch of rapid_tree_accept_workspace_size bytes (no
+ *                initial contents needed)
+ * The draw is rapid_accept's inverse CDF (smallest id whose cumulative weight
+ * exceeds u * W).  Launches 3 + (largest child count - 1) kernels on stream.
+ * Supports V in [2, 2^22].
+ */
+rv_status rapid_tree_accept(const float* z, const float* y, const int32_t* tokens,
+                            const int32_t* parent_host, const float* r, const float* u, int B,
+                            int n, int V, float T, float eta, int32_t* n_accept, int32_t* path,
+                            int32_t* out_tokens, float* ratio_out, void* workspace,
+                            size_t workspace_bytes, void* stream);
 
 /*
  * rapid_accept_noalloc -- rapid_accept_ex with no workspace argument, for

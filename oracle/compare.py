@@ -152,3 +152,110 @@ def flag_counts(ref, r, tol):
         lo = C[k - 1] if k > 0 else 0.0
         fd += min(abs(tgt - lo), abs(tgt - C[k])) <= tol * W
     return fa, fd, B
+
+
+def _draw_check(dr, kg, tol):
+    """(flagged, error message or None) for a GPU draw kg against the oracle's
+    draw record, by the rules above."""
+    C, W, tgt, k = dr["C"], dr["W"], dr["target"], dr["k"]
+    lo = C[k - 1] if k > 0 else 0.0
+    hi = C[k]
+    flagged = min(abs(tgt - lo), abs(tgt - hi)) <= tol * W
+    if flagged:
+        ok = dr["w"][kg] > 0
+        if ok:
+            lo_g = C[kg - 1] if kg > 0 else 0.0
+            ok = lo_g - tol * W <= tgt <= C[kg] + tol * W
+        return True, None if ok else "flagged draw token %d outside the widened interval" % kg
+    if kg != k:
+        return False, "drawn token %d != oracle %d (u*W=%r, [%r, %r))" % (kg, k, tgt, lo, hi)
+    return False, None
+
+
+def compare_tree_accept(ref, parent, tokens, n_gpu, path_gpu, tok_gpu, r, tol=BOUNDARY_TOL):
+    """Compare rapid_tree_accept outputs with the tree oracle's.
+
+    Per sequence b, with the GPU's path of n = n_gpu[b] nodes:
+    * n outside [0, number of nodes - 1] is an error;
+    * the path must run down the tree from the root (each node a child of the
+      one before), be padded with -1, and carry the nodes' draft tokens, then
+      one id in [0, V), then -1;
+    * every decision the path implies (at each node on it, the children
+      before the accepted one rejected, the accepted one accepted; at the
+      stop node every child rejected) must equal the oracle's
+      r_c <= ratio_c wherever the oracle tested c and |r_c - ratio_c| > tol;
+    * if the path differs from the oracle's (possible only through flagged
+      decisions) the sequence is counted as diverged and its draw is
+      range-checked only; otherwise the draw is checked as for a chain.
+    Returns a dict like compare_accept's."""
+    from .tree import tree_children
+    ch = tree_children(parent)
+    tok_gpu = np.asarray(tok_gpu)
+    path_gpu = np.asarray(path_gpu)
+    B, nn = tok_gpu.shape
+    errors = []
+    diverged = flagged_accept = flagged_draw = exact_draws = 0
+    for b in range(B):
+        ratio = ref["ratio"][b]
+        tested = ~np.isnan(ratio)
+        flagged_accept += int(np.sum(np.abs(np.asarray(r[b], dtype=np.float64)[tested]
+                                            - ratio[tested]) <= tol))
+        m = int(n_gpu[b])
+        if not 0 <= m <= nn - 1:
+            errors.append("b=%d: n_accept %d outside [0, %d]" % (b, m, nn - 1))
+            continue
+        gp = [int(x) for x in path_gpu[b, :m]]
+        prev, ok = 0, True
+        for c in gp:
+            if not (0 < c < nn and c in ch[prev]):
+                ok = False
+                break
+            prev = c
+        if not ok:
+            errors.append("b=%d: path %s does not run down the tree" % (b, gp))
+            continue
+        if any(int(x) != -1 for x in path_gpu[b, m:]):
+            errors.append("b=%d: path entries past n_accept are not -1" % b)
+        toks = [int(x) for x in tok_gpu[b]]
+        want = [int(tokens[b, c]) for c in gp]
+        if toks[:m] != want:
+            errors.append("b=%d: accepted tokens %s != the path's %s" % (b, toks[:m], want))
+        if any(x != -1 for x in toks[m + 1:]):
+            errors.append("b=%d: tokens past the draw are not -1" % b)
+        kg = toks[m]
+        V = len(ref["draw"][b]["C"])
+        if not 0 <= kg < V:
+            errors.append("b=%d: drawn token %d outside [0, %d)" % (b, kg, V))
+            continue
+        bad = None
+        v = 0
+        for i in range(m + 1):
+            acc = gp[i] if i < m else None
+            for c in ch[v]:
+                if acc is not None and c > acc:
+                    break
+                if not tested[c]:
+                    continue  # past a flagged divergence: the oracle never tested c
+                decided = c == acc
+                if decided != (float(r[b, c]) <= ratio[c]) and abs(float(r[b, c]) - ratio[c]) > tol:
+                    bad = "b=%d: node %d %s unflagged (r=%r ratio=%r)" % (
+                        b, c, "accepted" if decided else "rejected", float(r[b, c]), ratio[c])
+                    break
+            if bad or acc is None:
+                break
+            v = acc
+        if bad:
+            errors.append(bad)
+            continue
+        ref_path = [int(x) for x in ref["path"][b, :int(ref["n_accept"][b])]]
+        if gp != ref_path:
+            diverged += 1
+            continue
+        flagged, msg = _draw_check(ref["draw"][b], kg, tol)
+        flagged_draw += flagged
+        if msg:
+            errors.append("b=%d: %s" % (b, msg))
+        elif not flagged:
+            exact_draws += 1
+    return {"errors": errors, "diverged": diverged, "flagged_accept": flagged_accept,
+            "flagged_draw": flagged_draw, "exact_draws": exact_draws}

@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "librapid_verify.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["rv_validate.cpp", "attn_prefix.hip", "attn_block.hip", "lse_merge.hip",
-           "attn_window.hip", "rapid_accept.hip"]
+           "attn_window.hip", "rapid_accept.hip", "rapid_tree.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

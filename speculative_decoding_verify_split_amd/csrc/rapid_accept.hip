@@ -37,178 +37,10 @@
 
 #include <mutex>
 
-#include "rv_device.h"
-#include "rv_internal.h"
+#include "vocab_common.h"
 
 namespace rv {
 namespace {
-
-constexpr int TPB = kVocabThreads;
-
-// x[e] = row[start + e] for e < N (zero at or past V).
-template <bool VEC, int N>
-__device__ __forceinline__ void load_run(const float* __restrict__ row, int V, int start,
-                                         float (&x)[N]) {
-  static_assert(N % 4 == 0, "runs are whole float4s");
-  if (VEC && start + N <= V) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(row + start);
-#pragma unroll
-    for (int j = 0; j < N / 4; ++j) {
-      const f32x4 v = p[j];
-      x[4 * j + 0] = v[0];
-      x[4 * j + 1] = v[1];
-      x[4 * j + 2] = v[2];
-      x[4 * j + 3] = v[3];
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < N; ++e) x[e] = (start + e < V) ? row[start + e] : 0.f;
-  }
-}
-
-__device__ float block_max(float v) {
-  __shared__ float sh[TPB / 64];
-  v = wave_max(v);
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-  __syncthreads();
-  const float r = fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3]));
-  __syncthreads();
-  return r;
-}
-
-__device__ float block_sum(float v) {
-  __shared__ float sh[TPB / 64];
-  v = wave_sum(v);
-  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
-  __syncthreads();
-  const float r = (sh[0] + sh[1]) + (sh[2] + sh[3]);
-  __syncthreads();
-  return r;
-}
-
-// Two workgroup sums with one pair of barriers.
-__device__ float2 block_sum2(float a, float b) {
-  __shared__ float sh[2][TPB / 64];
-  a = wave_sum(a);
-  b = wave_sum(b);
-  if ((threadIdx.x & 63) == 0) {
-    sh[0][threadIdx.x >> 6] = a;
-    sh[1][threadIdx.x >> 6] = b;
-  }
-  __syncthreads();
-  const float2 r = make_float2((sh[0][0] + sh[0][1]) + (sh[0][2] + sh[0][3]),
-                               (sh[1][0] + sh[1][1]) + (sh[1][2] + sh[1][3]));
-  __syncthreads();
-  return r;
-}
-
-// Inclusive prefix sums of (v.x, v.y) over the workgroup in thread order:
-// a scan inside each wave, then the wave totals added in wave order.  *total
-// receives the workgroup sums, which equal the last thread's inclusive
-// values exactly (the same additions in the same order).
-__device__ float2 block_incl_scan2(float2 v, float2* total) {
-  __shared__ float2 sh[TPB / 64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float2 in = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float a = __shfl_up(in.x, o, 64);
-    const float b = __shfl_up(in.y, o, 64);
-    if (lane >= o) {
-      in.x += a;
-      in.y += b;
-    }
-  }
-  if (lane == 63) sh[wave] = in;
-  __syncthreads();
-  float2 run = make_float2(0.f, 0.f), off = run;
-#pragma unroll
-  for (int w = 0; w < TPB / 64; ++w) {
-    if (w == wave) off = run;
-    run.x += sh[w].x;
-    run.y += sh[w].y;
-  }
-  __syncthreads();
-  *total = run;
-  return make_float2(off.x + in.x, off.y + in.y);
-}
-
-// Index of the first thread with `hit` and of the last thread with `pos`
-// (-1 if none); every thread gets the same pair.
-__device__ int2 block_first_last(bool hit, bool pos) {
-  __shared__ int sf[TPB / 64], sl[TPB / 64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint64_t h = __ballot(hit), p = __ballot(pos);
-  if (lane == 0) {
-    sf[wave] = h ? wave * 64 + (int)__ffsll((long long)h) - 1 : -1;
-    sl[wave] = p ? wave * 64 + 63 - (int)__builtin_clzll(p) : -1;
-  }
-  __syncthreads();
-  int f = -1, l = -1;
-#pragma unroll
-  for (int w = 0; w < TPB / 64; ++w) {
-    if (f < 0) f = sf[w];
-    if (sl[w] >= 0) l = sl[w];
-  }
-  __syncthreads();
-  return make_int2(f, l);
-}
-
-// Merge two (max, sum-of-2^(x - max)) pairs.  Symmetric in its arguments, so
-// both lanes of a butterfly step obtain bit-identical results.
-__device__ __forceinline__ void lse_pair_merge(float& m, float& l, float mo, float lo) {
-  const float mn = fmaxf(m, mo);
-  const float a = (m == -INFINITY) ? 0.f : l * exp2_hw(m - mn);
-  const float c = (mo == -INFINITY) ? 0.f : lo * exp2_hw(mo - mn);
-  l = a + c;
-  m = mn;
-}
-
-// Base-2 log-sum-exp of a row from its per-chunk (max, sum) pairs, reduced by
-// a group of `width` lanes (16 or 64, aligned) in one pass: lane j of the
-// group folds chunks j, j + width, ... in order, then the group merges with
-// symmetric lane pairings (DPP quad permutes and mirrors, then the row-swap
-// permutes).  Every lane of the group returns the same value.
-template <int width>
-__device__ __forceinline__ float group_combine(const float* __restrict__ st, int C, int j,
-                                               float* max_out = nullptr) {
-  static_assert(width == 16 || width == 64, "group width");
-  float m = -INFINITY, l = 0.f;
-  for (int c = j; c < C; c += width) lse_pair_merge(m, l, st[2 * c], st[2 * c + 1]);
-  lse_pair_merge(m, l, dpp_f<kDppXor1>(m), dpp_f<kDppXor1>(l));
-  lse_pair_merge(m, l, dpp_f<kDppXor2>(m), dpp_f<kDppXor2>(l));
-  lse_pair_merge(m, l, dpp_f<kDppHalfMirror>(m), dpp_f<kDppHalfMirror>(l));
-  lse_pair_merge(m, l, dpp_f<kDppMirror>(m), dpp_f<kDppMirror>(l));
-  if constexpr (width == 64) {
-    float2 a = swap16(m), c = swap16(l);
-    m = a.x; l = c.x;
-    lse_pair_merge(m, l, a.y, c.y);
-    a = swap32(m);
-    c = swap32(l);
-    m = a.x; l = c.x;
-    lse_pair_merge(m, l, a.y, c.y);
-  }
-  if (max_out) *max_out = m;
-  return m + log2_hw(l);
-}
-
-// Sum of st[c], c < C, by a 16-lane group: lane j adds c = j, j + 16, ... in
-// order, then the group adds by symmetric pairings; all 16 lanes agree.
-__device__ __forceinline__ float group16_sum(const float* __restrict__ st, int C, int j) {
-  float v = 0.f;
-  for (int c = j; c < C; c += 16) v += st[c];
-  return row16_sum(v);
-}
-
-// p, q and s/ln2 of one vocabulary entry.  x2 = z/T/ln2, lz = log2 sum 2^x2,
-// likewise for y; s2 = (z/T + eta (q - p)) / ln2.
-__device__ __forceinline__ void pq_s(float zv, float yv, float invT2, float eta2, float lz,
-                                     float ly, float& p, float& q, float& s2) {
-  const float x2 = zv * invT2;
-  p = exp2_hw(x2 - lz);
-  q = exp2_hw(yv * invT2 - ly);
-  s2 = fmaf(eta2, q - p, x2);
-}
 
 // Row-table offsets, per sequence, in words: [4][gamma+1].
 __device__ __forceinline__ int rt_lz(int, int t) { return t; }
@@ -417,108 +249,6 @@ __global__ __launch_bounds__(TPB) void tail_kernel(const float* __restrict__ z,
   if (threadIdx.x == 0) tstat[((size_t)b * gamma + t) * cp + c] = csum;
 }
 
-// Inverse CDF of the draw row ts of sequence b with the caller's uniform,
-// run by one whole workgroup.  Chunk level: a scan of the cd chunk weights
-// (both kinds; kind 1, p_hat itself, only if a rejected row has no residual
-// mass, which exact arithmetic rules out) picks the first chunk of positive
-// weight whose running total exceeds u * W; thread level: the same over the
-// chunk's thread totals; element level: the same inside the thread.  Where
-// rounding leaves no such unit, the last unit of positive weight is taken
-// (and every lower level then takes its last positive unit, i.e. the largest
-// id of positive weight).
-template <bool VEC>
-__device__ void draw_row(const float* __restrict__ z, const float* __restrict__ y,
-                         const float* __restrict__ u, int b, int ts, int gamma, int V,
-                         float invT2, float eta2, int cd, const RowLse& rc,
-                         float* __restrict__ wsum, int32_t* __restrict__ out_tokens) {
-  __shared__ float sh_base;
-  // The chunk weights were published by the other workgroups with
-  // device-scope atomic stores before their arrival was counted; read them
-  // with device-scope atomic loads, which do not return a stale copy from
-  // this workgroup's L2.
-  float* ws = wsum + (size_t)b * cd * 2;
-  const float u_ts = u[(size_t)b * (gamma + 1) + ts];
-  auto chunk_w = [&](int i) {
-    return i < cd ? make_float2(
-                        __hip_atomic_load(ws + 2 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                        __hip_atomic_load(ws + 2 * i + 1, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT))
-                  : make_float2(0.f, 0.f);
-  };
-
-  // Totals of both kinds, block of TPB chunks by block.  The last block's
-  // values stay in registers (with cd <= TPB the only block).
-  float2 wv = make_float2(0.f, 0.f), incl = wv, tot = wv, carry = wv;
-  for (int c0 = 0; c0 < cd; c0 += TPB) {
-    carry.x += tot.x;
-    carry.y += tot.y;
-    wv = chunk_w(c0 + threadIdx.x);
-    incl = block_incl_scan2(wv, &tot);
-  }
-  const float2 W2 = make_float2(carry.x + tot.x, carry.y + tot.y);
-  const int kind = W2.x > 0.f ? 0 : 1;
-  const float tau = u_ts * (kind ? W2.y : W2.x);
-
-  int pick = -1, last = -1;
-  float tau_c = INFINITY;
-  float run = 0.f;
-  for (int c0 = 0; c0 < cd; c0 += TPB) {
-    if (cd > TPB) {
-      wv = chunk_w(c0 + threadIdx.x);
-      incl = block_incl_scan2(wv, &tot);
-    }
-    const float wk = kind ? wv.y : wv.x;
-    const float ik = run + (kind ? incl.y : incl.x);
-    const int2 fl = block_first_last(wk > 0.f && ik > tau, wk > 0.f);
-    if (fl.x >= 0) {
-      if ((int)threadIdx.x == fl.x) sh_base = ik - wk;
-      __syncthreads();
-      pick = c0 + fl.x;
-      tau_c = tau - sh_base;
-      break;
-    }
-    if (fl.y >= 0) last = c0 + fl.y;
-    run += kind ? tot.y : tot.x;
-  }
-  if (pick < 0) pick = last < 0 ? 0 : last;  // tau_c stays infinite
-
-  constexpr int PER = kDrawPer;
-  const int start = pick * kDrawChunk + threadIdx.x * PER;
-  float zx[PER], yx[PER], w[PER];
-  load_run<VEC>(z + ((size_t)b * (gamma + 1) + ts) * V, V, start, zx);
-  if (ts < gamma)
-    load_run<VEC>(y + ((size_t)b * gamma + ts) * V, V, start, yx);
-  else
-#pragma unroll
-    for (int e = 0; e < PER; ++e) yx[e] = 0.f;
-  float tsum = 0.f;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    w[e] = (start + e < V) ? draw_weight(zx[e], yx[e], ts, gamma, kind, invT2, eta2, rc) : 0.f;
-    tsum += w[e];
-  }
-  float2 ttot;
-  const float tincl = block_incl_scan2(make_float2(tsum, 0.f), &ttot).x;
-  const int2 fl = block_first_last(tsum > 0.f && tincl > tau_c, tsum > 0.f);
-  const int sel = fl.x >= 0 ? fl.x : (fl.y >= 0 ? fl.y : 0);
-  if ((int)threadIdx.x != sel) return;
-  const float tau_l = fl.x >= 0 ? tau_c - (tincl - tsum) : INFINITY;
-  float acc = 0.f;
-  int k = -1, klast = -1;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    if (w[e] > 0.f) {
-      if (k < 0 && acc + w[e] > tau_l) k = e;
-      klast = e;
-    }
-    acc += w[e];
-  }
-  if (k < 0) k = klast < 0 ? 0 : klast;
-  int tok = start + k;
-  if (tok >= V) tok = V - 1;
-  out_tokens[(size_t)b * (gamma + 1) + ts] = tok;
-}
-
 // grid (cd, B).  Every chunk recomputes the row LSEs of s (16 lanes per row,
 // all rows at once), the ratios and the first-reject cut, then writes its
 // share of the draw weights; chunk 0 writes the per-sequence outputs.
@@ -652,7 +382,13 @@ __global__ __launch_bounds__(TPB) void decide_kernel(
   }
   __syncthreads();
   if (sh_arrived != (uint32_t)(cd - 1)) return;  // uniform
-  draw_row<VEC>(z, y, u, b, ts, gamma, V, invT2, eta2, cd, rc, wsum, out_tokens);
+  draw_from_chunks<VEC, kDrawPer>(
+      z + ((size_t)b * (gamma + 1) + ts) * V,
+      ts < gamma ? y + ((size_t)b * gamma + ts) * V : nullptr, u[(size_t)b * (gamma + 1) + ts], V,
+      cd, wsum + (size_t)b * cd * 2, out_tokens + (size_t)b * (gamma + 1) + ts,
+      [&](float zv, float yv, int kind) {
+        return draw_weight(zv, yv, ts, gamma, kind, invT2, eta2, rc);
+      });
 }
 
 template <bool VEC>

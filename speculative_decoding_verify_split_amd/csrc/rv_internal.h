@@ -113,6 +113,49 @@ AcceptLayout accept_layout(int B, int gamma, int V);
 
 constexpr unsigned kAcceptFlags = RV_ACCEPT_TAIL_PRESERVE | RV_ACCEPT_PRINTED_RESIDUAL;
 
+// --- acceptance over a draft tree ---------------------------------------------
+
+constexpr int kMaxTreeNodes = RV_MAX_BLOCK_ROWS;
+
+// The tree as the kernels see it, built on the host from the caller's parent
+// array and passed to them by value.  Internal nodes (those with children)
+// are numbered by slot in node order.
+struct TreePlan {
+  int n;                         // nodes
+  int ni;                        // internal nodes
+  int npass;                     // residual passes: largest child count - 1
+  int8_t parent[kMaxTreeNodes];
+  int8_t rank[kMaxTreeNodes];    // position of node c among its siblings (by id)
+  int8_t nchild[kMaxTreeNodes];
+  int8_t slot[kMaxTreeNodes];    // internal slot of node v, -1 for a leaf
+  int8_t inode[kMaxTreeNodes];   // node of internal slot a
+  uint64_t kids[kMaxTreeNodes];  // children of node v, bit c for node c
+};
+// Builds the plan; RV_ERR_VALUE unless parent[0] == -1 and
+// 0 <= parent[i] < i for every other node.
+rv_status tree_plan(const int32_t* parent_host, int n, TreePlan* plan);
+
+// Workspace layout of rapid_tree_accept, in 4-byte words (independent of the
+// tree's shape: sized for any tree of n nodes).
+struct TreeLayout {
+  int cs, cp, cd;      // chunk counts as in AcceptLayout
+  size_t zstat;        // [B][n][cs][2]  (max, sum) of z/T per node
+  size_t ystat;        // [B][n][cs][2]  of y/T per internal slot
+  size_t sstat;        // [B][n][cp][2]  of s per internal slot
+  size_t rowtab;       // [B][2][n]      base-2 LSE of z/T per node, of y/T per slot
+  size_t rstat;        // [B][n][n][cp]  chunk sums of residual pass j per slot
+  size_t wsum;         // [B][cd][2]     draw weights per chunk
+  size_t arrivals;     // [B][kArrivalStride]
+  size_t words;
+};
+TreeLayout tree_layout(int B, int n, int V);
+
+rv_status check_tree_accept(const float* z, const float* y, const int32_t* tokens,
+                            const int32_t* parent_host, const float* r, const float* u, int B,
+                            int n, int V, float T, float eta, const int32_t* n_accept,
+                            const int32_t* path, const int32_t* out_tokens,
+                            const void* workspace, size_t workspace_bytes, TreePlan* plan);
+
 // Every argument check of rapid_accept except those of the workspace.
 rv_status check_accept_args(const float* z, const float* y, const int32_t* draft,
                             const float* r, const float* u, int B, int gamma, int V, float T,

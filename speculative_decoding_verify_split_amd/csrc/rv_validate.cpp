@@ -197,6 +197,79 @@ rv_status check_accept(const float* z, const float* y, const int32_t* draft, con
   return RV_OK;
 }
 
+rv_status tree_plan(const int32_t* parent, int n, TreePlan* P) {
+  if (!parent) return RV_ERR_NULL;
+  if (n < 1 || n > kMaxTreeNodes) return RV_ERR_SHAPE;
+  if (parent[0] != -1) return RV_ERR_VALUE;
+  for (int i = 1; i < n; ++i)
+    if (parent[i] < 0 || parent[i] >= i) return RV_ERR_VALUE;
+  *P = TreePlan{};
+  P->n = n;
+  for (int v = 0; v < n; ++v) {
+    P->parent[v] = (int8_t)parent[v];
+    P->slot[v] = -1;
+    P->inode[v] = -1;
+  }
+  for (int c = 1; c < n; ++c) {
+    const int v = parent[c];
+    P->rank[c] = P->nchild[v]++;
+    P->kids[v] |= 1ull << c;
+  }
+  int maxk = 0;
+  for (int v = 0; v < n; ++v) {
+    if (P->nchild[v] > 0) {
+      P->slot[v] = (int8_t)P->ni;
+      P->inode[P->ni++] = (int8_t)v;
+    }
+    if (P->nchild[v] > maxk) maxk = P->nchild[v];
+  }
+  P->npass = maxk > 0 ? maxk - 1 : 0;
+  return RV_OK;
+}
+
+TreeLayout tree_layout(int B, int n, int V) {
+  TreeLayout L;
+  L.cs = ceil_div(V, kStatChunk);
+  L.cp = ceil_div(V, kPhatChunk);
+  L.cd = ceil_div(V, kDrawChunk);
+  const size_t Bz = (size_t)B, N = (size_t)n;
+  size_t off = 0;
+  L.zstat = off;
+  off += round_words(Bz * N * L.cs * 2);
+  L.ystat = off;
+  off += round_words(Bz * N * L.cs * 2);
+  L.sstat = off;
+  off += round_words(Bz * N * L.cp * 2);
+  L.rowtab = off;
+  off += round_words(Bz * 2 * N);
+  L.rstat = off;
+  off += round_words(Bz * N * N * L.cp);
+  L.wsum = off;
+  off += round_words(Bz * L.cd * 2);
+  L.arrivals = off;
+  off += round_words(Bz * kArrivalStride);
+  L.words = off;
+  return L;
+}
+
+rv_status check_tree_accept(const float* z, const float* y, const int32_t* tokens,
+                            const int32_t* parent_host, const float* r, const float* u, int B,
+                            int n, int V, float T, float eta, const int32_t* n_accept,
+                            const int32_t* path, const int32_t* out_tokens,
+                            const void* workspace, size_t workspace_bytes, TreePlan* plan) {
+  if (!z || !y || !tokens || !parent_host || !r || !u || !n_accept || !path || !out_tokens ||
+      !workspace)
+    return RV_ERR_NULL;
+  if (B < 1 || n < 1 || V < 2) return RV_ERR_SHAPE;
+  if (n > kMaxTreeNodes || V > kMaxVocab || B > 65535) return RV_ERR_UNSUPPORTED;
+  if (!(T > 0.0f) || !isfinite(T) || !isfinite(eta)) return RV_ERR_VALUE;
+  const rv_status st = tree_plan(parent_host, n, plan);
+  if (st != RV_OK) return st;
+  if (!aligned16(z) || !aligned16(y) || !aligned16(workspace)) return RV_ERR_ALIGNMENT;
+  if (workspace_bytes < tree_layout(B, n, V).words * 4) return RV_ERR_WORKSPACE;
+  return RV_OK;
+}
+
 }  // namespace rv
 
 extern "C" {

@@ -72,6 +72,11 @@ def load_library():
     lib.rapid_accept_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, ctypes.c_uint,
                                     vp, vp, vp, vp, vp, sz, vp]
     lib.rapid_accept_ex.restype = i32
+    lib.rapid_tree_accept_workspace_size.argtypes = [i32, i32, i32]
+    lib.rapid_tree_accept_workspace_size.restype = sz
+    lib.rapid_tree_accept.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp, vp,
+                                      vp, vp, sz, vp]
+    lib.rapid_tree_accept.restype = i32
     lib.rapid_accept_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, f32, f32,
                                          ctypes.c_uint, vp, vp, vp, vp, vp]
     lib.rapid_accept_noalloc.restype = i32
@@ -352,3 +357,35 @@ def rapid_accept_noalloc(z, y, draft, r, u, T, eta, flags, n_accept, out_tokens,
         _ptr(z), _ptr(y), _ptr(draft), _ptr(r), _ptr(u), B, g, V, float(T), float(eta),
         int(flags), _ptr(n_accept), _ptr(out_tokens), _ptr(ratio_out), _ptr(p_hat_out),
         _stream(stream)), "rapid_accept_noalloc")
+
+
+def rapid_tree_accept_workspace_size(B, n, V):
+    return load_library().rapid_tree_accept_workspace_size(int(B), int(n), int(V))
+
+
+def rapid_tree_accept(z, y, tokens, parent, r, u, T, eta, n_accept, path, out_tokens, workspace,
+                      ratio_out=None, stream=None):
+    """Acceptance over a draft tree.  z, y fp32 [B,n,V]; tokens int32 [B,n];
+    parent: host sequence of n ints (parent[0] = -1); r, u fp32 [B,n];
+    n_accept int32 [B]; path, out_tokens int32 [B,n]; ratio_out fp32 [B,n] or
+    None; workspace uint8 of rapid_tree_accept_workspace_size bytes."""
+    import torch
+    _need(z, "z", torch.float32)
+    B, n, V = z.shape
+    _need(y, "y", torch.float32, (B, n, V))
+    _need(tokens, "tokens", torch.int32, (B, n))
+    _need(r, "r", torch.float32, (B, n))
+    _need(u, "u", torch.float32, (B, n))
+    _need(n_accept, "n_accept", torch.int32, (B,))
+    _need(path, "path", torch.int32, (B, n))
+    _need(out_tokens, "out_tokens", torch.int32, (B, n))
+    _need(workspace, "workspace", torch.uint8)
+    if ratio_out is not None:
+        _need(ratio_out, "ratio_out", torch.float32, (B, n))
+    if len(parent) != n:
+        raise ValueError("parent must have n = %d entries" % n)
+    par = (ctypes.c_int32 * n)(*[int(p) for p in parent])
+    _check(load_library().rapid_tree_accept(
+        _ptr(z), _ptr(y), _ptr(tokens), par, _ptr(r), _ptr(u), B, n, V, float(T), float(eta),
+        _ptr(n_accept), _ptr(path), _ptr(out_tokens), _ptr(ratio_out), _ptr(workspace),
+        workspace.numel(), _stream(stream)), "rapid_tree_accept")

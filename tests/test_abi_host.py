@@ -385,3 +385,40 @@ def test_balanced_split_rejects_bad_arguments(lib):
                                         ctypes.byref(ns)) == RV_ERR_NULL
     with pytest.raises(ValueError):
         rv.rv_prefix_balanced_split([100, -5], 4, 2, 5, 128, num_cus=256)
+
+
+def _tree(lib, parent=(-1, 0, 0, 1), **kw):
+    n = 4 if parent is None else len(parent)
+    a = dict(z=P, y=P, tok=P, r=P, u=P, B=1, n=n, V=1000, T=1.0, eta=0.5, na=P, path=P, out=P,
+             ratio=None, ws=P, wsb=1 << 22)
+    a.update(kw)
+    par = None if parent is None else (ctypes.c_int32 * len(parent))(*parent)
+    return lib.rapid_tree_accept(a["z"], a["y"], a["tok"], par, a["r"], a["u"], a["B"], a["n"],
+                                 a["V"], a["T"], a["eta"], a["na"], a["path"], a["out"],
+                                 a["ratio"], a["ws"], a["wsb"], None)
+
+
+def test_tree_accept_validation(lib):
+    assert _tree(lib, parent=None) == RV_ERR_NULL
+    assert _tree(lib, z=None) == RV_ERR_NULL
+    assert _tree(lib, path=None) == RV_ERR_NULL
+    assert _tree(lib, ws=None) == RV_ERR_NULL
+    assert _tree(lib, parent=(0, 0, 0, 1)) == RV_ERR_VALUE      # root must be -1
+    assert _tree(lib, parent=(-1, 0, 2, 1)) == RV_ERR_VALUE     # parent not earlier
+    assert _tree(lib, parent=(-1, 0, -1, 1)) == RV_ERR_VALUE
+    assert _tree(lib, n=0) == RV_ERR_SHAPE
+    assert _tree(lib, B=0) == RV_ERR_SHAPE
+    assert _tree(lib, V=1) == RV_ERR_SHAPE
+    assert _tree(lib, parent=tuple([-1] + list(range(64))), n=65) == RV_ERR_UNSUPPORTED
+    assert _tree(lib, V=(1 << 22) + 1) == RV_ERR_UNSUPPORTED
+    assert _tree(lib, T=0.0) == RV_ERR_VALUE
+    assert _tree(lib, eta=float("nan")) == RV_ERR_VALUE
+    assert _tree(lib, z=MIS) == RV_ERR_ALIGNMENT
+    assert _tree(lib, ws=MIS) == RV_ERR_ALIGNMENT
+    need = rv.rapid_tree_accept_workspace_size(1, 4, 1000)
+    assert need > 0 and need % 256 == 0
+    assert _tree(lib, wsb=need - 1) == RV_ERR_WORKSPACE
+    assert rv.rapid_tree_accept_workspace_size(1, 65, 1000) == 0
+    assert rv.rapid_tree_accept_workspace_size(1, 0, 1000) == 0
+    # the size does not depend on the tree's shape, only on (B, n, V)
+    assert rv.rapid_tree_accept_workspace_size(8, 32, 128256) > need

@@ -254,3 +254,81 @@ def test_flag_counts_and_exact_draws():
     assert flag_counts(ref, r, 1e-6)[1:] == (0, 1)
     res = compare_accept(ref, ref["n_accept"], ref["out_tokens"], r, u, draft=draft)
     assert res["exact_draws"] == 0 and res["flagged_draw"] == 1
+
+
+# ------------------------------------------------------ tree comparison rule
+
+from oracle import rapid_tree_accept_ref  # noqa: E402
+from oracle.compare import compare_tree_accept  # noqa: E402
+
+_TREE = [-1, 0, 0, 1, 1]
+
+
+def _tree_case(r, u=None):
+    rng = np.random.default_rng(21)
+    z = rng.standard_normal((1, 5, 6)) * 2
+    y = z + rng.standard_normal((1, 5, 6))
+    from oracle import retrieval_augmented_target
+    _, q1, ph1 = retrieval_augmented_target(z[0, 1], y[0, 1], 1.0, 0.5)
+    # node 3's token is where p_hat_1 falls shortest of q_1: its ratio is below 1
+    tok = np.array([[0, 1, 4, int(np.argmax(q1 - ph1)), 5]])
+    r = np.array([r], dtype=np.float64)
+    u = np.full((1, 5), 0.37) if u is None else np.array([u], dtype=np.float64)
+    ref = rapid_tree_accept_ref(z, y, _TREE, tok, r, u, 1.0, 0.5)
+    return tok, r, u, ref
+
+
+def _tree_out(ref):
+    return ref["n_accept"].copy(), ref["path"].copy(), ref["out_tokens"].copy()
+
+
+def test_tree_compare_identical_and_broken_outputs():
+    # accept node 1, reject node 3, accept node 4 (a leaf: bonus)
+    r0 = _tree_case([0.5] * 5)[-1]["ratio"][0]
+    base = [0.5, 0.0, 0.5, 0.999999, 0.0]
+    tok, r, u, ref = _tree_case(base)
+    assert list(ref["path"][0, :2]) == [1, 4], ref["path"]
+    n, p, t = _tree_out(ref)
+    res = compare_tree_accept(ref, _TREE, tok, n, p, t, r)
+    assert res["errors"] == [] and res["exact_draws"] == 1 and res["diverged"] == 0
+    for bad_n in (-1, 5, 9):
+        assert compare_tree_accept(ref, _TREE, tok, [bad_n], p, t, r)["errors"]
+    p2 = p.copy()
+    p2[0, 1] = 3  # node 3 was rejected (r ~ 1): an unflagged wrong decision
+    t2 = t.copy()
+    t2[0, 1] = tok[0, 3]
+    assert compare_tree_accept(ref, _TREE, tok, n, p2, t2, r)["errors"]
+    p3 = p.copy()
+    p3[0, 1] = 2  # node 2 is not a child of node 1
+    assert compare_tree_accept(ref, _TREE, tok, n, p3, t, r)["errors"]
+    t3 = t.copy()
+    t3[0, 0] = 3  # not node 1's token
+    assert compare_tree_accept(ref, _TREE, tok, n, p, t3, r)["errors"]
+    t4 = t.copy()
+    t4[0, 3] = 0  # past the draw
+    assert compare_tree_accept(ref, _TREE, tok, n, p, t4, r)["errors"]
+    t5 = t.copy()
+    w = ref["draw"][0]["w"]
+    t5[0, 2] = [j for j in range(6) if j != t[0, 2] and w[j] > 0][0]
+    assert compare_tree_accept(ref, _TREE, tok, n, p, t5, r)["errors"]
+    p6 = p.copy()
+    p6[0, 3] = 1  # path padding not -1
+    assert compare_tree_accept(ref, _TREE, tok, n, p6, t, r)["errors"]
+    del r0
+
+
+def test_tree_compare_flagged_divergence():
+    r0 = _tree_case([0.5] * 5)[-1]["ratio"][0]
+    # node 1's uniform sits just above its ratio: the oracle rejects node 1;
+    # a GPU that accepted it took a flagged decision and diverges
+    base = [0.5, r0[1] + 0.5 * BOUNDARY_TOL, 0.999999, 0.0, 0.0]
+    tok, r, u, ref = _tree_case(base)
+    assert ref["path"][0, 0] != 1
+    n = np.array([1])
+    p = np.full((1, 5), -1)
+    p[0, 0] = 1
+    t = np.full((1, 5), -1)
+    t[0, 0] = tok[0, 1]
+    t[0, 1] = 0
+    res = compare_tree_accept(ref, _TREE, tok, n, p, t, r)
+    assert res["errors"] == [] and res["diverged"] == 1 and res["flagged_accept"] >= 1

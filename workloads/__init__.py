@@ -289,6 +289,56 @@ def make_vocab(seed, B, gamma, V, z_sigma, noise, T, eta):
     return VocabInputs(z=z, y=y, draft=draft, r=r, u=u, T=float(T), eta=float(eta))
 
 
+@dataclass
+class TreeVocabInputs:
+    z: np.ndarray          # fp32 [B, n, V] target logits after each node
+    y: np.ndarray          # fp32 [B, n, V] drafter logits after each node
+    parent: np.ndarray     # int32 [n]
+    tokens: np.ndarray     # int32 [B, n] draft token of each node (0 at the root)
+    r: np.ndarray          # fp32 [B, n] acceptance uniforms
+    u: np.ndarray          # fp32 [B, n] sampling uniforms
+    T: float
+    eta: float
+
+
+def make_tree_vocab(seed, B, parent, V, z_sigma, noise, T, eta):
+    """Inputs of an acceptance over a draft tree: per node, z ~ N(0, z_sigma^2)
+    and y = z + N(0, noise^2); the token of node c is drawn from the drafter
+    distribution of its parent, softmax(y_parent / T), by the Gumbel-max
+    trick, so siblings are independent draws."""
+    parent = np.asarray(parent, dtype=np.int32)
+    n = len(parent)
+    ss = np.random.SeedSequence(seed).spawn(_N_SLOTS)
+    gz = np.random.Generator(np.random.PCG64(ss[_S_Z]))
+    gy = np.random.Generator(np.random.PCG64(ss[_S_Y]))
+    gg = np.random.Generator(np.random.PCG64(ss[_S_G]))
+    z = gz.standard_normal((B, n, V), dtype=np.float32)
+    z *= np.float32(z_sigma)
+    y = gy.standard_normal((B, n, V), dtype=np.float32)
+    y *= np.float32(noise)
+    y += z
+    tokens = np.zeros((B, n), dtype=np.int32)
+    for b in range(B):
+        for c in range(1, n):
+            gum = gg.gumbel(size=V)
+            tokens[b, c] = int(np.argmax(y[b, parent[c]].astype(np.float64) / T + gum))
+    r = _uniform_f32(ss[_S_R], (B, n))
+    u = _uniform_f32(ss[_S_U], (B, n))
+    return TreeVocabInputs(z=z, y=y, parent=parent, tokens=tokens, r=r, u=u, T=float(T),
+                           eta=float(eta))
+
+
+def config_tree_vocab(name, B_override=None, V_override=None, eta=None):
+    """Tree acceptance inputs on a tree workload's own tree (the tree1m
+    workload's 32-node tree and vocabulary)."""
+    c = CONFIGS[name]
+    ss = np.random.SeedSequence(c["seed"]).spawn(_N_SLOTS)
+    parent = tree_parents(ss[_S_TREE], c["n_nodes"], c["tree_depth"])
+    return make_tree_vocab(c["seed"] + 1, B_override or c["B"], parent, V_override or c["V"],
+                           c["z_sigma"], c["noise"], c["T"],
+                           c["etas"][0] if eta is None else eta)
+
+
 def config_attention(name, L_override=None, B_override=None, pad_bits=0, threads=None):
     """Attention inputs of a named workload (optionally with a shorter history)."""
     c = CONFIGS[name]
