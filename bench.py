@@ -17,7 +17,9 @@ stream), per-kernel device times from HIP events recorded on the library's
 stream during a second, untimed pass over the same K steps (the history
 kernel's pair rides on its own dispatch), the KV-stream bandwidth, the
 roofline of the history kernel, and the fp64 CPU oracle timed on the host as
-a reported baseline.
+a reported baseline, which also checks one step of the library's outputs on
+the same inputs and reports their acceptance statistics.  A plain 2 GiB
+device copy is measured before the warm-up (context for the peak).
 """
 
 import argparse
@@ -86,17 +88,23 @@ def _src_sha():
     return kernel_source_digest()
 
 
-def _traffic_per_launch(workload):
-    """HBM bytes per history-kernel launch from the committed counter
-    summary of this workload, or None if it is missing or was taken on
-    other kernel source."""
+def _counter_record(workload):
+    """The committed counter summary of this workload's history kernel, or
+    None if it is missing or was taken on other kernel source."""
     try:
         rec = json.load(open(TRAFFIC_FILE % workload))
     except (OSError, ValueError):
         return None
     if rec.get("kernel_code_sha256") != _src_sha():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def _traffic_per_launch(workload):
+    """HBM bytes per history-kernel launch (FETCH_SIZE + WRITE_SIZE passes,
+    scaled by a plain copy), or None."""
+    rec = _counter_record(workload)
+    return None if rec is None else rec.get("hbm_bytes_per_launch")
 
 
 def _host_info():
@@ -120,9 +128,12 @@ def _host_info():
             "affinity": len(os.sched_getaffinity(0)), "blas": blas}
 
 
-def _cpu_baseline(ai, vi, budget_s):
+def _cpu_baseline(ai, vi, budget_s, gpu=None):
     """Time the fp64 oracle on the host: full unsplit attention over every
-    head plus the step-by-step acceptance, repeated within the budget."""
+    head plus the step-by-step acceptance, repeated within the budget.  With
+    gpu (the library's outputs for the same inputs) the oracle's last result
+    is also compared with them, and the acceptance statistics of the inputs
+    are reported (check)."""
     from oracle import attn_ref, rapid_accept_ref
     threads = None
     try:
@@ -134,39 +145,132 @@ def _cpu_baseline(ai, vi, budget_s):
         threads = len(os.sched_getaffinity(0))
     reps, t0 = 0, time.perf_counter()
     while True:
-        attn_ref(ai.q, ai.k_cache, ai.v_cache, ai.k_blk, ai.v_blk, ai.seq_lens, ai.parent,
-                 ai.sm_scale)
-        rapid_accept_ref(vi.z, vi.y, vi.draft, vi.r, vi.u, vi.T, vi.eta)
+        O_ref, L_ref = attn_ref(ai.q, ai.k_cache, ai.v_cache, ai.k_blk, ai.v_blk, ai.seq_lens,
+                                ai.parent, ai.sm_scale)
+        ref = rapid_accept_ref(vi.z, vi.y, vi.draft, vi.r, vi.u, vi.T, vi.eta)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s or reps >= 20:
             break
-    return {"value": reps / el, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": "%d full verify step(s) of the same workload (all %d query heads over "
-                      "%d history tokens + vocabulary pass), %.1f s" %
-                      (reps, ai.q.shape[1], int(ai.seq_lens.max()), el),
-            "host": _host_info()}
+    out = {"value": reps / el, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+           "sample": "%d full verify step(s) of the same workload (all %d query heads over "
+                     "%d history tokens + vocabulary pass), %.1f s" %
+                     (reps, ai.q.shape[1], int(ai.seq_lens.max()), el),
+           "host": _host_info()}
+    if gpu is not None:
+        out["check"] = _check_against_oracle(O_ref, L_ref, ref, vi, gpu)
+    return out
 
 
-def _copy_context(n_bytes=1 << 31, reps=5):
+def _check_against_oracle(O_ref, L_ref, ref, vi, gpu):
+    """The benchmark step's own outputs against the oracle's on the same
+    inputs (rules of oracle/compare.py), and the acceptance statistics of
+    those inputs: alpha_t = sum_v min(q_t(v), p_hat_t(v)) per draft row and
+    the expected accepted length sum_k prod_{t<k} alpha_t (RAPID blog
+    section 2.1's test with p_hat, on independent rows)."""
+    import numpy as np
+    from oracle import draft_probs
+    from oracle.compare import attn_row_errors, compare_accept, flag_counts
+    res = compare_accept(ref, gpu["n_accept"], gpu["out_tokens"], vi.r, vi.u, draft=vi.draft)
+    B, g = vi.draft.shape
+    alpha = np.array([[np.sum(np.minimum(draft_probs(vi.y[b, t], vi.T), ref["p_hat"][b, t]))
+                       for t in range(g)] for b in range(B)])
+    exp_len = np.mean([sum(np.prod(alpha[b, :k]) for k in range(1, g + 1)) for b in range(B)])
+    fa6, fd6, _ = flag_counts(ref, vi.r, 1e-6)
+    return {
+        "attn_max_row_rel_err": float(attn_row_errors(gpu["out"], O_ref).max()),
+        "attn_max_abs_dlse": float(np.abs(gpu["lse"] - L_ref).max()),
+        "p_hat_max_abs_err": float(np.abs(gpu["p_hat"] - ref["p_hat"]).max()),
+        "ratio_max_abs_err": float(np.abs(gpu["ratio"] - ref["ratio"]).max()),
+        "n_accept": {"gpu": [int(x) for x in gpu["n_accept"]],
+                     "oracle": [int(x) for x in ref["n_accept"]]},
+        "tokens_errors": res["errors"],
+        "exact_draws": res["exact_draws"], "diverged": res["diverged"],
+        "flagged_1e-4": {"accept": res["flagged_accept"], "draw": res["flagged_draw"]},
+        "flagged_1e-6": {"accept": int(fa6), "draw": int(fd6)},
+        "alpha_per_row": [float(a) for a in alpha.mean(axis=0)],
+        "expected_accepted_length": float(exp_len),
+        "note": "one step on the benchmark's resident inputs (first rotated copy), outputs "
+                "read back after the timed region",
+    }
+
+
+def _tree_accept_time(workload, K, warmup):
+    """rapid_tree_accept on the workload's own draft tree (all nodes, B = 1,
+    the workload's vocabulary): K calls timed with events after the warm-up;
+    the inputs and outputs of one call are kept (_io) for the oracle leg."""
+    import numpy as np
+    import torch
+    from speculative_decoding_verify_split_amd import rapid_verify as rv
+    from speculative_decoding_verify_split_amd.step import to_device
+    from workloads import config_tree_vocab
+    vt = config_tree_vocab(workload, B_override=1)
+    B, n, V = vt.z.shape
+    d = {k: to_device(getattr(vt, k)) for k in ("z", "y", "tokens", "r", "u")}
+    n_acc = torch.empty((B,), dtype=torch.int32, device="cuda")
+    path = torch.empty((B, n), dtype=torch.int32, device="cuda")
+    tok = torch.empty((B, n), dtype=torch.int32, device="cuda")
+    ws = torch.empty((rv.rapid_tree_accept_workspace_size(B, n, V),), dtype=torch.uint8,
+                     device="cuda")
+    par = [int(p) for p in vt.parent]
+
+    def call():
+        rv.rapid_tree_accept(d["z"], d["y"], d["tokens"], par, d["r"], d["u"], vt.T, vt.eta,
+                             n_acc, path, tok, ws)
+
+    for _ in range(max(1, warmup)):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(K):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    kids = np.bincount(np.asarray(vt.parent[1:]), minlength=n)
+    return {"us_per_call": e0.elapsed_time(e1) * 1e3 / K, "calls": K, "nodes": n, "vocab": V,
+            "launches": 3 + max(0, int(kids.max()) - 1),
+            "note": "rapid_tree_accept over the workload's whole draft tree (the step above "
+                    "accepts along its chain 0..depth)",
+            "_io": (vt, (n_acc.cpu().numpy(), path.cpu().numpy(), tok.cpu().numpy()))}
+
+
+def _tree_check(vt, outs):
+    """The timed tree acceptance's outputs against the tree oracle."""
+    from oracle import rapid_tree_accept_ref
+    from oracle.compare import compare_tree_accept
+    n_g, path_g, tok_g = outs
+    ref = rapid_tree_accept_ref(vt.z, vt.y, vt.parent, vt.tokens, vt.r, vt.u, vt.T, vt.eta)
+    res = compare_tree_accept(ref, vt.parent, vt.tokens, n_g, path_g, tok_g, vt.r)
+    return {"errors": res["errors"], "n_accept": {"gpu": [int(x) for x in n_g],
+                                                  "oracle": [int(x) for x in ref["n_accept"]]},
+            "exact_draws": res["exact_draws"], "flagged_draw": res["flagged_draw"]}
+
+
+def _copy_context(n_bytes=1 << 31, min_ms=0.0, reps=5):
     """A plain 2 GiB device-to-device copy_ on the same box, as context for
-    the 8 TB/s peak: (read + write bytes) / time."""
+    the 8 TB/s peak: (read + write bytes) / time, over at least `reps`
+    copies and at least min_ms of device time."""
     import torch
     src = torch.empty(n_bytes, dtype=torch.uint8, device="cuda")
     src.fill_(1)
     dst = torch.empty_like(src)
     dst.copy_(src)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(reps):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    s = e0.elapsed_time(e1) / 1e3 / reps
+    total_ms, done = 0.0, 0
+    while done < reps or total_ms < min_ms:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        total_ms += e0.elapsed_time(e1)
+        done += reps
+    s = total_ms / 1e3 / done
     del src, dst
     torch.cuda.empty_cache()
-    return {"bytes_copied": n_bytes, "GBps_read_plus_write": 2 * n_bytes / s / 1e9}
+    return {"bytes_copied": n_bytes, "copies": done, "GBps_read_plus_write": 2 * n_bytes / s / 1e9}
 
 
 def _calibrate_copy(n_bytes, reps):
@@ -402,6 +506,8 @@ def main():
                     help="skip the HIP-graph replay measurement reported beside the eager one")
     ap.add_argument("--unfused", action="store_true",
                     help="run spec_attn_block and lse_merge as two calls")
+    ap.add_argument("--settle-ms", type=float, default=0.0,
+                    help="device time of the copy-bandwidth measurement before the warm-up")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -443,6 +549,10 @@ def main():
     kvs = [(st.k_cache, st.v_cache)] + [(st.k_cache.clone(), st.v_cache.clone())
                                         for _ in range(R - 1)]
     logits = [(st.z, st.y)] + [(st.z.clone(), st.y.clone()) for _ in range(R - 1)]
+
+    # A plain device copy, measured before the warm-up (context for the 8 TB/s
+    # peak; it also takes the device out of the idle clocks of the setup).
+    copy_ctx = _copy_context(min_ms=args.settle_ms)
 
     K = args.steps
     # four raw HIP events per timed step: the history kernel's own dispatch
@@ -538,6 +648,26 @@ def main():
                                "ms_per_step": gm_el * 1e3 / (reps * R),
                                "steps_per_graph": R, "replays": reps}
 
+    # One more step on the resident inputs (first rotated copy), with the
+    # ratios and p_hat requested, whose outputs the oracle leg checks.
+    ratio_t = torch.empty((st.B, st.gamma), dtype=torch.float32, device="cuda")
+    p_hat_t = torch.empty((st.B, st.gamma, st.V), dtype=torch.float32, device="cuda")
+    rv.spec_attn_prefix(st.q, st.k_cache, st.v_cache, st.seq_lens, st.max_seq_len, st.split_len,
+                        st.num_splits, st.o_part, st.lse_part, st.sm_scale)
+    rv.spec_attn_block_merge(st.q, st.k_blk, st.v_blk, st.parent, st.o_part, st.lse_part, st.out,
+                             st.lse_out, st.sm_scale)
+    rv.rapid_accept(st.z, st.y, st.draft, st.r, st.u, st.T, st.eta, st.n_accept, st.out_tokens,
+                    st.workspace, ratio_t, p_hat_t)
+    torch.cuda.synchronize()
+    gpu_out = {"out": st.out.float().cpu().numpy(), "lse": st.lse_out.cpu().numpy(),
+               "n_accept": st.n_accept.cpu().numpy(), "out_tokens": st.out_tokens.cpu().numpy(),
+               "ratio": ratio_t.cpu().numpy(), "p_hat": p_hat_t.cpu().numpy()}
+    del ratio_t, p_hat_t
+
+    tree = None
+    if "n_nodes" in cfg:
+        tree = _tree_accept_time(args.workload, K, args.warmup)
+
     prefix_ms = [hev.elapsed_ms(4 * i, 4 * i + 1) for i in range(K)]
     attn_ms = [hev.elapsed_ms(4 * i, 4 * i + 2) for i in range(K)]
     acc_ms = [hev.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(K)]
@@ -594,17 +724,22 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": _traffic_per_launch(args.workload),
                      "kernel": "spec_attn_prefix (history pass)",
-                     "algorithmic_bytes_per_launch": kv_bytes},
+                     "algorithmic_bytes_per_launch": kv_bytes,
+                     "mfma_busy_frac": (_counter_record(args.workload) or {}).get(
+                         "mfma_busy_frac")},
         "mean_n_accept": float(np.mean(n_acc)),
         "graph_replay": graph,
-        "copy_context": None,
+        "copy_context": copy_ctx,
+        "tree_accept": tree,
         "cpu_baseline": None,
     }
     del kvs, logits
     torch.cuda.empty_cache()
-    line["copy_context"] = _copy_context()
+    tree_io = tree.pop("_io") if tree is not None else None
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = _cpu_baseline(ai, vi, args.cpu_budget)
+        line["cpu_baseline"] = _cpu_baseline(ai, vi, args.cpu_budget, gpu=gpu_out)
+        if tree is not None:
+            tree["check"] = _tree_check(*tree_io)
     print(json.dumps(line), flush=True)
 
 
