@@ -1,11 +1,13 @@
 #!/usr/bin/env python3
 """Verify-step benchmark on one MI355X.
 
-One step is the whole hot path on one batch of synthetic inputs:
-spec_attn_prefix (history pass over the KV cache), the masked draft block and
-the log-sum-exp merge (one spec_attn_block_merge call; --unfused runs
-spec_attn_block and lse_merge separately), and rapid_accept (RAPID's
-vocabulary pass), back to back on one stream.  Default workload: the
+One step is the whole hot path on one batch of synthetic inputs: the verify
+attention -- history pass over the KV cache, masked draft block and
+log-sum-exp merge -- as one spec_attn_verify call (a single launch at the
+default workload; --attention block_merge runs spec_attn_prefix then
+spec_attn_block_merge, --attention unfused spec_attn_prefix, spec_attn_block
+and lse_merge), and rapid_accept (RAPID's vocabulary pass), back to back on
+one stream.  Default workload: the
 LLaMA-3.1-8B-shaped verify layer
 (32 query / 8 kv heads, d=128, 131072-token bf16 KV cache, gamma=10, vocab
 128256, T=1, eta=0.5), inputs resident in HBM.  Three copies of the KV cache
@@ -14,9 +16,9 @@ previous one left in the 256 MB last-level cache.
 
 Prints one JSON line: steps/s (value: K steps timed with nothing else on the
 stream), per-kernel device times from HIP events recorded on the library's
-stream during a second, untimed pass over the same K steps (the history
-kernel's pair rides on its own dispatch), the KV-stream bandwidth, the
-roofline of the history kernel, and the fp64 CPU oracle timed on the host as
+stream during a second, untimed pass over the same K steps (the attention's
+pair rides on its own dispatches), the KV-stream bandwidth, the roofline of
+the attention kernel, and the fp64 CPU oracle timed on the host as
 a reported baseline, which also checks one step of the library's outputs on
 the same inputs and reports their acceptance statistics.  A plain 2 GiB
 device copy is measured before the warm-up (context for the peak).
@@ -36,9 +38,11 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "verify steps/s + KV-stream HBM GB/s, 8B-shaped layer, 128K ctx, gamma=10"
-# HBM bytes per history-kernel launch, from rocprofv3 FETCH_SIZE/WRITE_SIZE
-# passes on this workload (one file per workload).
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "spec_attn_prefix_%s_traffic.json")
+# HBM bytes per launch of the attention's dominant kernel (the single-launch
+# spec_attn_verify, else the history pass of spec_attn_prefix), from rocprofv3
+# FETCH_SIZE/WRITE_SIZE passes on this workload (one file per kernel and
+# workload).
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "%s_%s_traffic.json")
 PREFIX_SRC = os.path.join(ROOT, "speculative_decoding_verify_split_amd", "csrc", "attn_prefix.hip")
 
 
@@ -88,11 +92,11 @@ def _src_sha():
     return kernel_source_digest()
 
 
-def _counter_record(workload):
-    """The committed counter summary of this workload's history kernel, or
-    None if it is missing or was taken on other kernel source."""
+def _counter_record(workload, kernel="spec_attn_prefix"):
+    """The committed counter summary of this workload's kernel, or None if
+    it is missing or was taken on other kernel source."""
     try:
-        rec = json.load(open(TRAFFIC_FILE % workload))
+        rec = json.load(open(TRAFFIC_FILE % (kernel, workload)))
     except (OSError, ValueError):
         return None
     if rec.get("kernel_code_sha256") != _src_sha():
@@ -100,10 +104,10 @@ def _counter_record(workload):
     return rec
 
 
-def _traffic_per_launch(workload):
-    """HBM bytes per history-kernel launch (FETCH_SIZE + WRITE_SIZE passes,
-    scaled by a plain copy), or None."""
-    rec = _counter_record(workload)
+def _traffic_per_launch(workload, kernel="spec_attn_prefix"):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE passes, scaled by a
+    plain copy), or None."""
+    rec = _counter_record(workload, kernel)
     return None if rec is None else rec.get("hbm_bytes_per_launch")
 
 
@@ -504,8 +508,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay measurement reported beside the eager one")
-    ap.add_argument("--unfused", action="store_true",
-                    help="run spec_attn_block and lse_merge as two calls")
+    ap.add_argument("--attention", choices=("verify", "block_merge", "unfused"),
+                    default="verify",
+                    help="verify: one spec_attn_verify call (default); block_merge: "
+                         "spec_attn_prefix + spec_attn_block_merge; unfused: spec_attn_prefix + "
+                         "spec_attn_block + lse_merge")
     ap.add_argument("--settle-ms", type=float, default=0.0,
                     help="device time of the copy-bandwidth measurement before the warm-up")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -555,29 +562,33 @@ def main():
     copy_ctx = _copy_context(min_ms=args.settle_ms)
 
     K = args.steps
-    # four raw HIP events per timed step: the history kernel's own dispatch
-    # start and end (spec_attn_prefix_ev), then after the block + merge and
-    # after the acceptance pass
+    mode = args.attention
+    single = mode == "verify" and rv.rv_verify_single_launch(st.B, st.Hq, st.Hkv, st.n, st.d,
+                                                             st.num_splits)
+    # four raw HIP events per timed step: the attention's start and end on
+    # its own dispatches (spec_attn_verify's events; with the separate calls,
+    # the history kernel's, spec_attn_prefix_ev), then after the block + merge
+    # and after the acceptance pass
     hev = _HipEvents(4 * K)
     sid = torch.cuda.current_stream().cuda_stream
 
     def step(i, timed=False):
         kc, vc = kvs[i % R]
         z, y = logits[i % R]
-        if timed:
+        evs = (hev.ev[4 * i], hev.ev[4 * i + 1]) if timed else (None, None)
+        if mode == "verify":
+            st.attention(kc, vc, single=True, events=evs)
+        else:
             rv.spec_attn_prefix_ev(st.q, kc, vc, st.seq_lens, st.max_seq_len, st.split_len,
-                                   st.num_splits, st.o_part, st.lse_part, hev.ev[4 * i],
-                                   hev.ev[4 * i + 1], st.sm_scale)
-        else:
-            rv.spec_attn_prefix(st.q, kc, vc, st.seq_lens, st.max_seq_len, st.split_len,
-                                st.num_splits, st.o_part, st.lse_part, st.sm_scale)
-        if args.unfused:
-            rv.spec_attn_block(st.q, st.k_blk, st.v_blk, st.parent, st.o_blk, st.lse_blk,
-                               st.sm_scale)
-            rv.lse_merge(st.o_part, st.lse_part, st.o_blk, st.lse_blk, st.out, st.lse_out)
-        else:
-            rv.spec_attn_block_merge(st.q, st.k_blk, st.v_blk, st.parent, st.o_part, st.lse_part,
-                                     st.out, st.lse_out, st.sm_scale)
+                                   st.num_splits, st.o_part, st.lse_part, evs[0], evs[1],
+                                   st.sm_scale)
+            if mode == "unfused":
+                rv.spec_attn_block(st.q, st.k_blk, st.v_blk, st.parent, st.o_blk, st.lse_blk,
+                                   st.sm_scale)
+                rv.lse_merge(st.o_part, st.lse_part, st.o_blk, st.lse_blk, st.out, st.lse_out)
+            else:
+                rv.spec_attn_block_merge(st.q, st.k_blk, st.v_blk, st.parent, st.o_part,
+                                         st.lse_part, st.out, st.lse_out, st.sm_scale)
         if timed:
             hev.record(4 * i + 2, sid)
         rv.rapid_accept(z, y, st.draft, st.r, st.u, st.T, st.eta, st.n_accept, st.out_tokens,
@@ -652,10 +663,12 @@ def main():
     # ratios and p_hat requested, whose outputs the oracle leg checks.
     ratio_t = torch.empty((st.B, st.gamma), dtype=torch.float32, device="cuda")
     p_hat_t = torch.empty((st.B, st.gamma, st.V), dtype=torch.float32, device="cuda")
-    rv.spec_attn_prefix(st.q, st.k_cache, st.v_cache, st.seq_lens, st.max_seq_len, st.split_len,
-                        st.num_splits, st.o_part, st.lse_part, st.sm_scale)
-    rv.spec_attn_block_merge(st.q, st.k_blk, st.v_blk, st.parent, st.o_part, st.lse_part, st.out,
-                             st.lse_out, st.sm_scale)
+    st.out.zero_()
+    st.lse_out.zero_()
+    if mode == "verify":
+        st.attention(single=True)
+    else:
+        st.attention(fused=mode == "block_merge")
     rv.rapid_accept(st.z, st.y, st.draft, st.r, st.u, st.T, st.eta, st.n_accept, st.out_tokens,
                     st.workspace, ratio_t, p_hat_t)
     torch.cuda.synchronize()
@@ -668,8 +681,12 @@ def main():
     if "n_nodes" in cfg:
         tree = _tree_accept_time(args.workload, K, args.warmup)
 
+    # verify: the kernel's own start and end (one launch, or the history
+    # kernel's start and the merge kernel's end); otherwise the history
+    # kernel alone, and the attention up to the marker after the merge
     prefix_ms = [hev.elapsed_ms(4 * i, 4 * i + 1) for i in range(K)]
-    attn_ms = [hev.elapsed_ms(4 * i, 4 * i + 2) for i in range(K)]
+    attn_ms = prefix_ms if mode == "verify" else [hev.elapsed_ms(4 * i, 4 * i + 2)
+                                                  for i in range(K)]
     acc_ms = [hev.elapsed_ms(4 * i + 2, 4 * i + 3) for i in range(K)]
     step_dev_ms = [hev.elapsed_ms(4 * i, 4 * i + 3) for i in range(K)]
     hev.close()
@@ -681,6 +698,7 @@ def main():
     logits_bytes = int(B * (2 * st.gamma + 1) * st.V * 4)
     acc_s = float(np.mean(acc_ms)) / 1e3
     n_acc = st.n_accept.cpu().numpy()
+    roof_kernel = "spec_attn_verify" if single else "spec_attn_prefix"
 
     line = {
         "metric": METRIC,
@@ -701,8 +719,12 @@ def main():
                    "head_dim": d, "kv_tokens": int(np.max(ai.seq_lens)), "block_rows": st.n,
                    "gamma": st.gamma, "vocab": st.V, "T": st.T, "eta": st.eta,
                    "split_len": st.split_len, "num_splits": st.num_splits,
-                   "rotated_copies": R, "block_and_merge": "two calls" if args.unfused else
-                   "spec_attn_block_merge", "parallelism": "single GPU"},
+                   "rotated_copies": R,
+                   "attention": {"verify": "spec_attn_verify (%s)" % (
+                       "one launch" if single else "two launches"),
+                                 "block_merge": "spec_attn_prefix + spec_attn_block_merge",
+                                 "unfused": "spec_attn_prefix + spec_attn_block + lse_merge"}[mode],
+                   "parallelism": "single GPU"},
         "kv_stream_GBps": kv_bytes / attn_s / 1e9,
         "kv_stream_frac_of_peak": kv_bytes / attn_s / 1e9 / HBM_PEAK_GBPS,
         # one read of z [B, gamma+1, V] and y [B, gamma, V] (fp32) over the
@@ -710,22 +732,27 @@ def main():
         "logits_bytes": logits_bytes,
         "logits_stream_GBps": logits_bytes / acc_s / 1e9,
         "logits_stream_frac_of_peak": logits_bytes / acc_s / 1e9 / HBM_PEAK_GBPS,
-        "kernels_us": {"spec_attn_prefix": prefix_s * 1e6,
-                       ("spec_attn_block+lse_merge" if args.unfused else
-                        "spec_attn_block_merge"): (attn_s - prefix_s) * 1e6,
-                       "rapid_accept": float(np.mean(acc_ms)) * 1e3,
-                       "device_step": float(np.mean(step_dev_ms)) * 1e3},
+        "kernels_us": dict(
+            ({"spec_attn_verify": attn_s * 1e6} if mode == "verify" else
+             {"spec_attn_prefix": prefix_s * 1e6,
+              ("spec_attn_block+lse_merge" if mode == "unfused" else
+               "spec_attn_block_merge"): (attn_s - prefix_s) * 1e6}),
+            rapid_accept=float(np.mean(acc_ms)) * 1e3,
+            device_step=float(np.mean(step_dev_ms)) * 1e3),
         "device_step_us": {"median": float(np.median(step_dev_ms)) * 1e3,
                            "p10": float(np.percentile(step_dev_ms, 10)) * 1e3,
                            "p90": float(np.percentile(step_dev_ms, 90)) * 1e3},
-        "spec_attn_prefix_us": {"median": float(np.median(prefix_ms)) * 1e3,
-                                "p10": float(np.percentile(prefix_ms, 10)) * 1e3,
-                                "p90": float(np.percentile(prefix_ms, 90)) * 1e3},
+        ("spec_attn_verify_us" if mode == "verify" else "spec_attn_prefix_us"): {
+            "median": float(np.median(prefix_ms)) * 1e3,
+            "p10": float(np.percentile(prefix_ms, 10)) * 1e3,
+            "p90": float(np.percentile(prefix_ms, 90)) * 1e3},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": _traffic_per_launch(args.workload),
-                     "kernel": "spec_attn_prefix (history pass)",
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": _traffic_per_launch(args.workload, roof_kernel),
+                     "kernel": ("spec_attn_verify (history pass, block and merge in one "
+                                "launch)" if single else "spec_attn_prefix (history pass)"),
                      "algorithmic_bytes_per_launch": kv_bytes,
-                     "mfma_busy_frac": (_counter_record(args.workload) or {}).get(
+                     "mfma_busy_frac": (_counter_record(args.workload, roof_kernel) or {}).get(
                          "mfma_busy_frac")},
         "mean_n_accept": float(np.mean(n_acc)),
         "graph_replay": graph,

@@ -16,7 +16,9 @@
  *      spec_attn_block   -- attention among the draft rows under the causal
  *                           or tree mask;
  *      lse_merge         -- log-sum-exp merge of all partials;
- *      spec_attn_block_merge -- the last two in one launch.
+ *      spec_attn_block_merge -- the last two in one launch;
+ *      spec_attn_verify  -- all three in one launch where the device holds
+ *                           the history pass at once.
  *    The LongSpec drafter's own attention (same summary, sections 2.1-2.2)
  *    uses spec_attn_prefix at n = 1 with lse_merge and no block for its
  *    cross-attention over the target's cache, and
@@ -60,10 +62,13 @@
  *   n_accept = -1 for that sequence; non-finite logits give unspecified
  *   tokens but never an out-of-bounds access.
  * - Results are bit-deterministic: every reduction has a fixed order; the
- *   one atomic (rapid_accept's per-sequence arrival counter) only decides
- *   which workgroup performs the draw, not what is drawn.
- * - Workspaces (rapid_accept, spec_attn_window) are caller-owned device
- *   scratch; they need no initial contents and hold nothing between calls.
+ *   atomics (the acceptance passes' per-sequence arrival counters,
+ *   spec_attn_verify's split masks) only decide which workgroup performs a
+ *   step, not what it computes.
+ * - Workspaces (rapid_accept, rapid_tree_accept, spec_attn_window) are
+ *   caller-owned device scratch; they need no initial contents and hold
+ *   nothing between calls.  spec_attn_verify's sync words are the exception:
+ *   zero before the first call, zero after every call.
  *   A workspace counts as an output: calls that may run at the same time
  *   (different streams) each need their own; calls on one stream may share
  *   one.
@@ -234,6 +239,60 @@ rv_status spec_attn_block_merge(const void* q, const void* k_blk, const void* v_
                                 const int32_t* parent_host, const float* o_part,
                                 const float* lse_part, int S, int B, int Hq, int Hkv, int n,
                                 int d, float sm_scale, void* out, float* lse_out, void* stream);
+
+/*
+ * spec_attn_verify -- the whole verify attention (spec_attn_prefix, then
+ * spec_attn_block_merge) in one launch where the device can hold it (LongSpec
+ * summary, section 2.3: an unmasked pass over the history, a masked pass over
+ * the draft block, their outputs combined by log-sum-exp).  Each workgroup of
+ * the history pass, once the other splits of its (sequence, kv head) are
+ * done, merges a share of that group's rows, so the merge needs no launch of
+ * its own.
+ *
+ *   q, k_cache, v_cache, seq_lens, max_seq_len, L_max, sm_scale, split_len,
+ *   num_splits, o_part, lse_part   as spec_attn_prefix (o_part and lse_part
+ *                                  are still written, then read back)
+ *   k_blk, v_blk, parent_host      as spec_attn_block
+ *   out, lse_out                   as spec_attn_block_merge
+ *   sync        device scratch of spec_attn_verify_sync_size(B, Hkv) bytes,
+ *               16-byte aligned, ZERO-FILLED by the caller before its first
+ *               use; every call leaves it zero again.  Unlike the other
+ *               workspaces it must not be shared by calls that may run at
+ *               the same time (different streams).
+ *   help_after_us  microseconds a workgroup whose split is done waits for
+ *               the rest before it computes a missing split itself (negative:
+ *               200; 0 makes every waiting workgroup help at once; at most
+ *               10^7, else RV_ERR_VALUE).  Results do not depend on it.
+ *   start_event, stop_event  hipEvent_t created by the caller, or NULL:
+ *               recorded on the first and last kernel's own dispatch.
+ * The single launch is taken when rv_verify_single_launch(B, Hq, Hkv, n, d,
+ * num_splits, number of compute units of the current device) is 1; otherwise
+ * the call runs the two launches of spec_attn_prefix and
+ * spec_attn_block_merge.  Either way out and lse_out equal those of the two
+ * calls up to fp32 rounding order (the single launch sums each row's
+ * partials in one ascending chain).
+ */
+size_t spec_attn_verify_sync_size(int B, int Hkv);
+
+/*
+ * 1 when spec_attn_verify runs as a single launch: the history pass takes the
+ * per-wave kernel (M = (Hq/Hkv)*n <= 64 rows per kv head, and <= 48 at
+ * d = 128), num_splits <= 64, ceil(M / num_splits) <= 4 (one merged row per
+ * wave), and its B*Hkv*num_splits workgroups number at most 64 and at most
+ * num_cus; else 0 (also for invalid sizes).  Small grids are where the one
+ * launch pays: on larger ones the exchange between workgroups on different
+ * XCDs costs more than the second launch.  Pure host arithmetic.
+ */
+int rv_verify_single_launch(int B, int Hq, int Hkv, int n, int d, int num_splits, int num_cus);
+
+rv_status spec_attn_verify(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* seq_lens, int64_t max_seq_len, int B, int Hq, int Hkv,
+                           int n, int d, int64_t L_max, float sm_scale, int64_t split_len,
+                           int num_splits, const void* k_blk, const void* v_blk,
+                           const int32_t* parent_host, float* o_part, float* lse_part,
+                           void* sync, size_t sync_bytes, void* out, float* lse_out,
+                           int help_after_us, void* stream, void* start_event,
+                           void* stop_event);
 
 /*
  * spec_attn_window -- the drafter's sliding-window self-attention with

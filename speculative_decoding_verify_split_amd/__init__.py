@@ -15,15 +15,21 @@ from .rapid_verify import (  # noqa: F401
     RV_ACCEPT_TAIL_PRESERVE,
     rapid_accept,
     rapid_accept_ex,
+    rapid_accept_noalloc,
     rapid_accept_workspace_size,
+    rapid_tree_accept,
+    rapid_tree_accept_workspace_size,
     rv_prefix_balanced_split,
     rv_prefix_default_split,
     rv_status_string,
+    rv_verify_single_launch,
     rv_version,
     spec_attn_block,
     spec_attn_block_merge,
     spec_attn_prefix,
     spec_attn_prefix_ev,
+    spec_attn_verify,
+    spec_attn_verify_sync_size,
     spec_attn_window,
     spec_attn_window_workspace_size,
 )

@@ -41,6 +41,8 @@
 
 #include <utility>
 
+#include "block_row.h"
+#include "merge_fold.h"
 #include "rv_device.h"
 #include "rv_internal.h"
 
@@ -176,13 +178,186 @@ struct TileRegs {
   i32x4 v[PrefixGeom<D>::VCH];
 };
 
-// History pass over split s of the cache (no mask).
-template <int D, int MT>
+// What the single-launch verify pass (attn_kernel<D, MT, true>) needs beyond
+// the history pass: the draft block, the merged outputs and one pair of
+// sync words per (sequence, kv head).
+template <bool FUSE>
+struct TailArgs {};
+template <>
+struct TailArgs<true> {
+  const uint16_t* k_blk;     // [B][Hkv][n][D] bf16
+  const uint16_t* v_blk;     // [B][Hkv][n][D] bf16
+  uint16_t* out;             // [B][Hq][n][D] bf16
+  float* lse_out;            // [B][Hq][n] or null
+  uint64_t* sync;            // [B][Hkv][2]: mask of published splits, finished count
+  uint32_t help_ticks;       // wait (100 MHz ticks) before computing a missing split
+  BlockMask mask;            // visibility bits of the block rows
+};
+
+// The fused tail: after its own split, a workgroup (b, kv head, s) waits for
+// the other splits of its (b, kv head) and then merges local rows
+// s, s + S, s + 2S, ... < M (LongSpec summary, section 2.3: the history part
+// and the masked block part are combined by log-sum-exp), so the merge needs
+// no launch of its own.  It is taken for small grids only (the host rule in
+// rv_verify_single_launch: at most 64 workgroups, at most one merged row per
+// wave), where it saves the second launch; on the full 8B-shaped layer the
+// cross-XCD publish and poll below cost more than a kernel boundary.
+//   * Publish: the split's partials are written with device-scope stores,
+//     which stay coherent across the XCDs' L2s without a writeback (plain
+//     stores behind an agent-scope release took ~20 us of L2 write-backs at
+//     256 workgroups); every wave waits for its stores to complete, then one
+//     thread sets the split's bit in the group's mask word.
+//   * Block part: then wave w computes the block attention of its first row
+//     (local row s + w S; block_row.h) while the other splits finish.
+//     (Before the split's first tiles, its time lands on every split;
+//     issuing its loads during the split's epilogue gained nothing.)
+//   * Wait: one thread polls the mask word.  The launch is used only when
+//     every workgroup of the grid fits on the device at once, but other work
+//     may hold compute units; so a workgroup that has waited help_ticks
+//     computes the first missing split after its own itself and publishes
+//     it.  A split computed twice is written twice with the same bits, and
+//     every wait ends: each help sets a bit, so after at most S helps the
+//     mask is full.
+//   * Merge: wave w merges rows s + w S, s + (w + 4) S, ...: the row's S
+//     partials (device-scope loads) in ascending split order against their
+//     maximum, then the block part, as in spec_attn_block_merge (one wave per
+//     row here, so the sums run in a different order: equal up to fp32
+//     rounding).
+//   * The finished count: each workgroup adds one once it needs the mask no
+//     more (after its own bits are set); the last of the S clears both
+//     words, so they are zero again for the next call (the caller zero-fills
+//     them once).
+
+// Wait until every vector-memory access this wave issued has completed
+// (stores acknowledged at their scope); also a compiler barrier.
+__device__ __forceinline__ void wait_vm_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int D, typename RunSplit>
+__device__ __forceinline__ void verify_tail(RunSplit& run_split, const TailArgs<true>& vt,
+                                            const uint16_t* __restrict__ q, int Hq, int Hkv,
+                                            int n, float scale_log2, int S,
+                                            const float* __restrict__ o_part,
+                                            const float* __restrict__ lse_part, int b, int kvh,
+                                            int s0, int M) {
+  constexpr int PER = D / 64;
+  __shared__ int sh_next;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int G = Hq / Hkv;
+  uint64_t* const mword = vt.sync + 2 * ((size_t)b * Hkv + kvh);
+  uint64_t* const fword = mword + 1;
+  const uint64_t full = S >= 64 ? ~0ull : ((1ull << S) - 1ull);
+  const size_t kv0 = ((size_t)b * Hkv + kvh) * (size_t)n * D;
+  auto grow_of = [&](int r) -> int64_t {  // (b, h, i) index of local row r
+    const int gq = r / n;
+    const int i = r - gq * n;
+    return ((int64_t)b * Hq + kvh * G + gq) * n + i;
+  };
+  auto block_part = [&](int r, float (&ob)[PER], float& lb2) {
+    block_row_attention<D>(q + grow_of(r) * D, vt.k_blk + kv0, vt.v_blk + kv0,
+                           vt.mask.bits[r % n], n, scale_log2, ob, lb2);
+  };
+  // (after this thread's own mask updates have completed)
+  auto finish = [&]() {
+    wait_vm_stores();
+    const uint64_t old =
+        __hip_atomic_fetch_add(fword, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == (uint64_t)(S - 1)) {
+      __hip_atomic_store(mword, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(fword, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  // Every wave's device-scope partial stores complete, then split sp is
+  // marked done.
+  auto publish = [&](int sp) {
+    wait_vm_stores();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_or(mword, 1ull << sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  // -1 once every split of the group is published (and this workgroup is
+  // counted out), else the split to compute on another's behalf.
+  auto wait = [&]() -> int {
+    if (threadIdx.x == 0) {
+      int next = -1;
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      for (;;) {
+        const uint64_t m = __hip_atomic_load(mword, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((m & full) == full) break;
+        if (__builtin_amdgcn_s_memrealtime() - t0 >= vt.help_ticks) {
+          for (int t = 1; t <= S; ++t) {  // first missing split after this one
+            const int u = (s0 + t) % S;
+            if (!((m >> u) & 1ull)) {
+              next = u;
+              break;
+            }
+          }
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (next < 0) finish();
+      sh_next = next;
+    }
+    __syncthreads();
+    return sh_next;
+  };
+
+  float ob[PER], lb2 = 0.f;
+  const int r_first = s0 + wave * S;  // this wave's first row
+  run_split(s0);
+  publish(s0);
+  if (s0 >= M) {  // no row to merge here
+    if (threadIdx.x == 0) finish();
+    return;
+  }
+  if (r_first < M) block_part(r_first, ob, lb2);
+  // (a split to help with: the barrier in wait() ended every LDS read of the
+  // last one, so run_split may reuse the LDS)
+  for (int u = wait(); u >= 0; u = wait()) {
+    run_split(u);
+    publish(u);
+  }
+
+  for (int j = wave;; j += NW) {
+    const int r = s0 + j * S;
+    if (r >= M) break;
+    if (j != wave) block_part(r, ob, lb2);
+    const int64_t grow = grow_of(r);
+    const float* lp = lse_part + grow * S;
+    const float* op = o_part + grow * S * D + lane * PER;
+    PartialFold<D, 1, 32, true> pf;
+    pf.load(op, lp, S, 0, 0);
+    float Ms = -INFINITY;
+    for (int t = lane; t < S; t += 64) Ms = fmaxf(Ms, partial_load<true>(lp + t));
+    Ms = wave_max(Ms);
+    float acc[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+    float wsum = 0.f;
+    if (Ms != -INFINITY) pf.fold(op, lp, S, 0, Ms, acc, wsum);
+    const float lb = lb2 * kLn2;  // finite: a row always sees itself
+    const float Mx = fmaxf(Ms, lb);
+    const float fs = (Ms == -INFINITY) ? 0.f : exp2_hw((Ms - Mx) * kLog2e);
+    const float fb = exp2_hw((lb - Mx) * kLog2e);
+    const float tot = fmaf(fs, wsum, fb);
+    const float inv = 1.0f / tot;  // tot >= fb = 1 or fs * wsum >= 1
+    uint16_t* dst = vt.out + grow * D + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) dst[e] = f32_to_bf16_bits(fmaf(fs, acc[e], fb * ob[e]) * inv);
+    if (vt.lse_out != nullptr && lane == 0) vt.lse_out[grow] = Mx + log2_hw(tot) * kLn2;
+  }
+}
+
+// History pass over split s of the cache (no mask).  With FUSE the same
+// launch also computes the draft-block part and merges the result (see the
+// notes at the fused tail below).
+template <int D, int MT, bool FUSE>
 __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
     const uint16_t* __restrict__ vc, const int32_t* __restrict__ seq_lens, int Hq, int Hkv,
     int n, int64_t L_max, float scale_log2, int64_t split_len, int S,
-    float* __restrict__ o_part, float* __restrict__ lse_part) {
+    float* __restrict__ o_part, float* __restrict__ lse_part, const TailArgs<FUSE> vt) {
   using Gm = PrefixGeom<D>;
   constexpr int KS = Gm::KS, NB = Gm::NB, VCH = Gm::VCH, VROW = Gm::VROW, OROW = Gm::OROW;
   constexpr int VBYTES = NW * Gm::VTILE;
@@ -202,7 +377,6 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
   __shared__ float l_lds[NW][MT * 16];
 
   const SplitItem item = split_item(seq_lens, (int)gridDim.z, Hkv, S, L_max, split_len);
-  const int s = item.s;
   const int kvh = item.kvh;
   const int b = item.b;
   const int lane = threadIdx.x & 63;
@@ -214,6 +388,9 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
 
   int64_t L = seq_lens[b];
   L = L < 0 ? 0 : (L > L_max ? L_max : L);
+
+  // The partial (O, LSE) of split s for every row of the group.
+  auto run_split = [&](const int s) {
   const int64_t kbeg = (int64_t)s * split_len;
   int64_t kend = kbeg + split_len;
   if (kend > L) kend = L;
@@ -456,7 +633,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
     const float inv = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) m_lds[w][row] = a[w] * inv;  // this row's weights
-    lse_part[out_row(row) * S + s] = l > 0.f ? (M + log2_hw(l)) * kLn2 : -INFINITY;
+    const float lse_s = l > 0.f ? (M + log2_hw(l)) * kLn2 : -INFINITY;
+    if constexpr (FUSE)  // device-scope store: read by other XCDs in this launch
+      __hip_atomic_store(lse_part + out_row(row) * S + s, lse_s, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    else
+      lse_part[out_row(row) * S + s] = lse_s;
   }
   __syncthreads();
 
@@ -473,9 +655,23 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
       for (int w = 0; w < NW; ++w)
         o += m_lds[w][row] * *reinterpret_cast<const f32x4*>(obuf + (w * MT * 16 + row) * OROW +
                                                              c4 * 4);
-      __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(o_part + (out_row(row) * S + s) * D +
-                                                          c4 * 4));
+      float* const dst = o_part + (out_row(row) * S + s) * D + c4 * 4;
+      if constexpr (FUSE) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __hip_atomic_store(dst + e, o[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(dst));
+      }
     }
+  }
+  };
+
+  if constexpr (!FUSE) {
+    run_split(item.s);
+  } else {
+    verify_tail<D>(run_split, vt, q, Hq, Hkv, n, scale_log2, S, o_part, lse_part, b, kvh, item.s,
+                   M);
   }
 }
 
@@ -888,12 +1084,13 @@ __global__ __launch_bounds__(NW * KP * 64, 1) void attn_wide_kernel(
 
 // With start/stop events the launch records them on the kernel's own
 // dispatch (hipExtLaunchKernel), so their elapsed time is the kernel's.
-template <typename Kernel>
+// (extra: the narrow kernel's tail arguments; none for the wide kernel)
+template <typename Kernel, typename... Extra>
 hipError_t launch_attn(Kernel kernel, int waves, const void* q, const void* k, const void* v,
                        const int32_t* seq_lens, int B, int Hq, int Hkv, int n, int64_t L_max,
                        float scale_log2, int64_t split_len, int S, float* o_part,
                        float* lse_part, hipStream_t stream, hipEvent_t ev_start,
-                       hipEvent_t ev_stop) {
+                       hipEvent_t ev_stop, const Extra&... extra) {
   dim3 grid((unsigned)S, (unsigned)Hkv, (unsigned)B);
   const dim3 block((unsigned)(waves * 64));
   const uint16_t* qq = static_cast<const uint16_t*>(q);
@@ -902,10 +1099,10 @@ hipError_t launch_attn(Kernel kernel, int waves, const void* q, const void* k, c
   if (ev_start != nullptr || ev_stop != nullptr)
     hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev_start, ev_stop, 0, qq, kk,
                           vv, seq_lens, Hq, Hkv, n, L_max, scale_log2, split_len, S, o_part,
-                          lse_part);
+                          lse_part, extra...);
   else
     hipLaunchKernelGGL(kernel, grid, block, 0, stream, qq, kk, vv, seq_lens, Hq, Hkv,
-                       n, L_max, scale_log2, split_len, S, o_part, lse_part);
+                       n, L_max, scale_log2, split_len, S, o_part, lse_part, extra...);
   return hipGetLastError();
 }
 
@@ -918,18 +1115,23 @@ rv_status dispatch_attn(int d, const RowPlan& rp, const void* q, const void* k, 
   if (d == DD && rp.MTW == MM)                                                                 \
     e = launch_attn(KERNEL, WAVES, q, k, v, seq_lens, B, Hq, Hkv, n, L_max, scale_log2,       \
                     split_len, S, o_part, lse_part, s, e0, e1);
+#define RV_NARROW_CASE(DD, MM)                                                                 \
+  if (d == DD && rp.MTW == MM)                                                                 \
+    e = launch_attn((attn_kernel<DD, MM, false>), NW, q, k, v, seq_lens, B, Hq, Hkv, n, L_max, \
+                    scale_log2, split_len, S, o_part, lse_part, s, e0, e1, none);
   // Up to 4 row tiles: the per-wave streaming kernel.  5..8 tiles: the
   // shared-stage kernel with two key phases (8 waves, 2 tiles each); wider
   // groups: one phase (4 waves, 3 or 4 tiles each).
+  const TailArgs<false> none{};
   if (!rp.wide) {
-    RV_ATTN_CASE(64, 1, (attn_kernel<64, 1>), NW)
-    else RV_ATTN_CASE(64, 2, (attn_kernel<64, 2>), NW)
-    else RV_ATTN_CASE(64, 3, (attn_kernel<64, 3>), NW)
-    else RV_ATTN_CASE(64, 4, (attn_kernel<64, 4>), NW)
-    else RV_ATTN_CASE(128, 1, (attn_kernel<128, 1>), NW)
-    else RV_ATTN_CASE(128, 2, (attn_kernel<128, 2>), NW)
-    else RV_ATTN_CASE(128, 3, (attn_kernel<128, 3>), NW)
-    else RV_ATTN_CASE(128, 4, (attn_kernel<128, 4>), NW)
+    RV_NARROW_CASE(64, 1)
+    else RV_NARROW_CASE(64, 2)
+    else RV_NARROW_CASE(64, 3)
+    else RV_NARROW_CASE(64, 4)
+    else RV_NARROW_CASE(128, 1)
+    else RV_NARROW_CASE(128, 2)
+    else RV_NARROW_CASE(128, 3)
+    else RV_NARROW_CASE(128, 4)
     else return RV_ERR_UNSUPPORTED;
   } else {
     RV_ATTN_CASE(64, 2, (attn_wide_kernel<64, 2, 2>), 2 * NW)
@@ -941,6 +1143,34 @@ rv_status dispatch_attn(int d, const RowPlan& rp, const void* q, const void* k, 
     else return RV_ERR_UNSUPPORTED;
   }
 #undef RV_ATTN_CASE
+#undef RV_NARROW_CASE
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return RV_ERR_HIP;
+  }
+  return RV_OK;
+}
+
+rv_status dispatch_verify(int d, const RowPlan& rp, const void* q, const void* k, const void* v,
+                          const int32_t* seq_lens, int B, int Hq, int Hkv, int n, int64_t L_max,
+                          float scale_log2, int64_t split_len, int S, float* o_part,
+                          float* lse_part, const TailArgs<true>& tail, hipStream_t s,
+                          hipEvent_t e0, hipEvent_t e1) {
+  hipError_t e;
+#define RV_VERIFY_CASE(DD, MM)                                                                 \
+  if (d == DD && rp.MTW == MM)                                                                 \
+    e = launch_attn((attn_kernel<DD, MM, true>), NW, q, k, v, seq_lens, B, Hq, Hkv, n, L_max,  \
+                    scale_log2, split_len, S, o_part, lse_part, s, e0, e1, tail);
+  if (rp.wide) return RV_ERR_UNSUPPORTED;
+  RV_VERIFY_CASE(64, 1)
+  else RV_VERIFY_CASE(64, 2)
+  else RV_VERIFY_CASE(64, 3)
+  else RV_VERIFY_CASE(64, 4)
+  else RV_VERIFY_CASE(128, 1)
+  else RV_VERIFY_CASE(128, 2)
+  else RV_VERIFY_CASE(128, 3)
+  else return RV_ERR_UNSUPPORTED;  // (d = 128 with 4 row tiles: two launches)
+#undef RV_VERIFY_CASE
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return RV_ERR_HIP;
@@ -982,4 +1212,51 @@ extern "C" rv_status spec_attn_prefix_ev(const void* q, const void* k_cache,
                            static_cast<hipStream_t>(stream),
                            static_cast<hipEvent_t>(start_event),
                            static_cast<hipEvent_t>(stop_event));
+}
+
+extern "C" rv_status spec_attn_verify(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* seq_lens, int64_t max_seq_len, int B,
+                                      int Hq, int Hkv, int n, int d, int64_t L_max,
+                                      float sm_scale, int64_t split_len, int num_splits,
+                                      const void* k_blk, const void* v_blk,
+                                      const int32_t* parent_host, float* o_part, float* lse_part,
+                                      void* sync, size_t sync_bytes, void* out, float* lse_out,
+                                      int help_after_us, void* stream, void* start_event,
+                                      void* stop_event) {
+  rv::BlockMask mask;
+  rv_status st = rv::check_verify(q, k_cache, v_cache, seq_lens, max_seq_len, B, Hq, Hkv, n, d,
+                                  L_max, sm_scale, split_len, num_splits, k_blk, v_blk,
+                                  parent_host, o_part, lse_part, sync, sync_bytes, out,
+                                  help_after_us, &mask);
+  if (st != RV_OK) return st;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return RV_ERR_HIP;
+  }
+  const rv::RowPlan rp = rv::row_plan(Hq, Hkv, n);
+  const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = static_cast<hipEvent_t>(start_event);
+  hipEvent_t e1 = static_cast<hipEvent_t>(stop_event);
+  if (rv_verify_single_launch(B, Hq, Hkv, n, d, num_splits, cus)) {
+    rv::TailArgs<true> tail;
+    tail.k_blk = static_cast<const uint16_t*>(k_blk);
+    tail.v_blk = static_cast<const uint16_t*>(v_blk);
+    tail.out = static_cast<uint16_t*>(out);
+    tail.lse_out = lse_out;
+    tail.sync = static_cast<uint64_t*>(sync);
+    const int us = help_after_us < 0 ? rv::kVerifyHelpDefaultUs : help_after_us;
+    tail.help_ticks = (uint32_t)us * 100u;  // 100 MHz constant clock
+    tail.mask = mask;
+    return rv::dispatch_verify(d, rp, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, n, L_max,
+                               scale_log2, split_len, num_splits, o_part, lse_part, tail, s, e0,
+                               e1);
+  }
+  st = rv::dispatch_attn(d, rp, q, k_cache, v_cache, seq_lens, B, Hq, Hkv, n, L_max, scale_log2,
+                         split_len, num_splits, o_part, lse_part, s, e0, nullptr);
+  if (st != RV_OK) return st;
+  return rv::block_merge_launch(q, k_blk, v_blk, mask, o_part, lse_part, num_splits, B, Hq, Hkv, n,
+                                d, scale_log2, out, lse_out, stream, stop_event);
 }

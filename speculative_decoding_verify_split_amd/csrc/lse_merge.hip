@@ -22,70 +22,15 @@
 // attention (block_row.h) while the history partials are in flight, which
 // saves the block pass its own launch and its round trip through memory.
 
+#include <hip/hip_ext.h>
+
 #include "block_row.h"
+#include "merge_fold.h"
 #include "rv_device.h"
 #include "rv_internal.h"
 
 namespace rv {
 namespace {
-
-// One wave's share of a row's history partials, s = wave, wave + NWV, ...,
-// batch b holding the FB of them from s = wave + b FB NWV.  op points at
-// this lane's PER columns of the row's first partial.
-template <int D, int NWV, int FB>
-struct PartialFold {
-  static constexpr int PER = D / 64;
-  float val[FB][PER];
-  float lse[FB];
-
-  // Issues every load of batch b; partials past S read as empty.
-  __device__ __forceinline__ void load(const float* __restrict__ op,
-                                       const float* __restrict__ lp, int S, int wave, int b) {
-#pragma unroll
-    for (int j = 0; j < FB; ++j) {
-      const int s = wave + (b * FB + j) * NWV;
-      lse[j] = s < S ? lp[s] : -INFINITY;
-#pragma unroll
-      for (int e = 0; e < PER; ++e) val[j][e] = s < S ? op[(size_t)s * D + e] : 0.f;
-    }
-  }
-
-  // acc += a_s O_s and wsum += a_s over batch b in ascending s, with
-  // a_s = exp(LSE_s - M) (0 for an empty split, whose O_s is 0).
-  __device__ __forceinline__ void add(int S, int wave, int b, float M, float (&acc)[PER],
-                                      float& wsum) const {
-#pragma unroll
-    for (int j = 0; j < FB; ++j) {
-      const int s = wave + (b * FB + j) * NWV;
-      if (s < S) {
-        const float a = exp2_hw((lse[j] - M) * kLog2e);
-        wsum += a;
-#pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] = fmaf(a, val[j][e], acc[e]);
-      }
-    }
-  }
-
-  // Every batch of this wave, the first already loaded.
-  __device__ __forceinline__ void fold(const float* __restrict__ op,
-                                       const float* __restrict__ lp, int S, int wave, float M,
-                                       float (&acc)[PER], float& wsum) {
-    add(S, wave, 0, M, acc, wsum);
-    for (int b = 1; wave + b * FB * NWV < S; ++b) {
-      load(op, lp, S, wave, b);
-      add(S, wave, b, M, acc, wsum);
-    }
-  }
-};
-
-// Fixed-order (left to right) sum of the NWV wave values.
-template <int NWV>
-__device__ __forceinline__ float wave_order_sum(const float* v, int stride) {
-  float t = v[0];
-#pragma unroll
-  for (int w = 1; w < NWV; ++w) t += v[w * stride];
-  return t;
-}
 
 template <int D, int FB, int NWV>
 __global__ __launch_bounds__(NWV * 64) void merge_kernel(const float* __restrict__ o_part,
@@ -204,13 +149,19 @@ __global__ __launch_bounds__(NWV * 64) void block_merge_kernel(
 // (FB) and waves per row (NWV); the index 0..3 selects one of the four.
 int fold_shape(int S) { return S <= 32 ? 0 : (S <= 64 ? 1 : (S <= 128 ? 2 : 3)); }
 
+// With a stop event the launch records it on the kernel's own dispatch.
 template <int D, int FB, int NWV>
-void launch_block_merge(dim3 grid, hipStream_t s, const uint16_t* q, const uint16_t* k,
-                        const uint16_t* v, const BlockMask& mask, int Hq, int G, int n,
-                        float scale_log2, const float* o_part, const float* lse_part, int S,
-                        uint16_t* out, float* lse_out) {
-  hipLaunchKernelGGL((block_merge_kernel<D, FB, NWV>), grid, dim3(NWV * 64), 0, s, q, k, v,
-                     mask, Hq, G, n, scale_log2, o_part, lse_part, S, out, lse_out);
+void launch_block_merge(dim3 grid, hipStream_t s, hipEvent_t ev_stop, const uint16_t* q,
+                        const uint16_t* k, const uint16_t* v, const BlockMask& mask, int Hq,
+                        int G, int n, float scale_log2, const float* o_part,
+                        const float* lse_part, int S, uint16_t* out, float* lse_out) {
+  if (ev_stop != nullptr)
+    hipExtLaunchKernelGGL((block_merge_kernel<D, FB, NWV>), grid, dim3(NWV * 64), 0, s, nullptr,
+                          ev_stop, 0, q, k, v, mask, Hq, G, n, scale_log2, o_part, lse_part, S,
+                          out, lse_out);
+  else
+    hipLaunchKernelGGL((block_merge_kernel<D, FB, NWV>), grid, dim3(NWV * 64), 0, s, q, k, v,
+                       mask, Hq, G, n, scale_log2, o_part, lse_part, S, out, lse_out);
 }
 
 template <int D, int FB, int NWV>
@@ -223,28 +174,25 @@ void launch_merge(dim3 grid, hipStream_t s, const float* o_part, const float* ls
 }  // namespace
 }  // namespace rv
 
-extern "C" rv_status spec_attn_block_merge(const void* q, const void* k_blk, const void* v_blk,
-                                           const int32_t* parent_host, const float* o_part,
-                                           const float* lse_part, int S, int B, int Hq, int Hkv,
-                                           int n, int d, float sm_scale, void* out,
-                                           float* lse_out, void* stream) {
-  rv::BlockMask mask;
-  rv_status st = rv::check_block_merge(q, k_blk, v_blk, parent_host, o_part, lse_part, S, B, Hq,
-                                       Hkv, n, d, sm_scale, out, &mask);
-  if (st != RV_OK) return st;
-  const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+namespace rv {
+
+rv_status block_merge_launch(const void* q, const void* k_blk, const void* v_blk,
+                             const BlockMask& mask, const float* o_part, const float* lse_part,
+                             int S, int B, int Hq, int Hkv, int n, int d, float scale_log2,
+                             void* out, float* lse_out, void* stream, void* stop_event) {
   hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t ev = static_cast<hipEvent_t>(stop_event);
   dim3 grid((unsigned)(B * Hq * n));
   const uint16_t* qq = static_cast<const uint16_t*>(q);
   const uint16_t* kk = static_cast<const uint16_t*>(k_blk);
   const uint16_t* vv = static_cast<const uint16_t*>(v_blk);
   uint16_t* o16 = static_cast<uint16_t*>(out);
   const int G = Hq / Hkv;
-  const int fs = rv::fold_shape(S);
+  const int fs = fold_shape(S);
 #define RV_BM_CASE(DD, F, FB, NWV)                                                           \
   if (d == DD && fs == F)                                                                    \
-    rv::launch_block_merge<DD, FB, NWV>(grid, s, qq, kk, vv, mask, Hq, G, n, scale_log2,     \
-                                        o_part, lse_part, S, o16, lse_out);
+    launch_block_merge<DD, FB, NWV>(grid, s, ev, qq, kk, vv, mask, Hq, G, n, scale_log2,     \
+                                    o_part, lse_part, S, o16, lse_out);
   RV_BM_CASE(64, 0, 8, 4)
   else RV_BM_CASE(64, 1, 16, 4)
   else RV_BM_CASE(64, 2, 32, 4)
@@ -256,6 +204,22 @@ extern "C" rv_status spec_attn_block_merge(const void* q, const void* k_blk, con
 #undef RV_BM_CASE
   if (hipGetLastError() != hipSuccess) return RV_ERR_HIP;
   return RV_OK;
+}
+
+}  // namespace rv
+
+extern "C" rv_status spec_attn_block_merge(const void* q, const void* k_blk, const void* v_blk,
+                                           const int32_t* parent_host, const float* o_part,
+                                           const float* lse_part, int S, int B, int Hq, int Hkv,
+                                           int n, int d, float sm_scale, void* out,
+                                           float* lse_out, void* stream) {
+  rv::BlockMask mask;
+  rv_status st = rv::check_block_merge(q, k_blk, v_blk, parent_host, o_part, lse_part, S, B, Hq,
+                                       Hkv, n, d, sm_scale, out, &mask);
+  if (st != RV_OK) return st;
+  const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  return rv::block_merge_launch(q, k_blk, v_blk, mask, o_part, lse_part, S, B, Hq, Hkv, n, d,
+                                scale_log2, out, lse_out, stream, nullptr);
 }
 
 extern "C" rv_status lse_merge(const float* o_part, const float* lse_part, int S,

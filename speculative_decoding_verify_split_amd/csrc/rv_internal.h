@@ -47,6 +47,39 @@ rv_status check_block_merge(const void* q, const void* k_blk, const void* v_blk,
                             const float* lse_part, int S, int B, int Hq, int Hkv, int n, int d,
                             float sm_scale, const void* out, BlockMask* mask);
 
+// The block + merge launch of spec_attn_block_merge with a prebuilt mask;
+// stop_event (a hipEvent_t or NULL) is recorded on the kernel's own dispatch.
+rv_status block_merge_launch(const void* q, const void* k_blk, const void* v_blk,
+                             const BlockMask& mask, const float* o_part, const float* lse_part,
+                             int S, int B, int Hq, int Hkv, int n, int d, float scale_log2,
+                             void* out, float* lse_out, void* stream, void* stop_event);
+
+// --- single-launch verify pass (spec_attn_verify) -----------------------------
+
+// The splits of one (sequence, kv head) are tracked in one 64-bit mask word.
+constexpr int kVerifyMaxSplits = 64;
+// The single launch pays where its grid is small: measured on MI355X at
+// 32/8 heads, n = 11, it took 13.5 us against 17.6-26 us for the two
+// launches at 16 workgroups (8/2 heads, 4K tokens), tied at 128, and lost at
+// 256 (97 against 89 us at 128K tokens): the cross-XCD publish and poll cost
+// grows with the grid, and a workgroup merging more than one row per wave
+// serialises them (32 workgroups of 11 rows each: 34 against 22 us).
+constexpr int kVerifySingleMaxGroups = 64;
+// Default wait before a workgroup computes a missing split itself: 200 us of
+// the 100 MHz constant clock (s_memrealtime).
+constexpr int kVerifyHelpDefaultUs = 200;
+constexpr int kVerifyHelpMaxUs = 10000000;
+// Sync words: per (sequence, kv head) the split mask and the finished count.
+inline size_t verify_sync_bytes(int B, int Hkv) { return (size_t)B * (size_t)Hkv * 16; }
+
+rv_status check_verify(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* seq_lens, int64_t max_seq_len, int B, int Hq, int Hkv,
+                       int n, int d, int64_t L_max, float sm_scale, int64_t split_len,
+                       int num_splits, const void* k_blk, const void* v_blk,
+                       const int32_t* parent_host, const float* o_part, const float* lse_part,
+                       const void* sync, size_t sync_bytes, const void* out, int help_after_us,
+                       BlockMask* mask);
+
 // Largest first-row position spec_attn_window accepts (device values above
 // it are clamped), so that positions of a block's rows stay in int range.
 constexpr int kMaxWindowPos = 1 << 30;

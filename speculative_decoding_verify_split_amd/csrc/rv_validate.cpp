@@ -108,6 +108,26 @@ rv_status check_block_merge(const void* q, const void* k_blk, const void* v_blk,
   return block_mask(parent_host, n, mask);
 }
 
+rv_status check_verify(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* seq_lens, int64_t max_seq_len, int B, int Hq, int Hkv,
+                       int n, int d, int64_t L_max, float sm_scale, int64_t split_len,
+                       int num_splits, const void* k_blk, const void* v_blk,
+                       const int32_t* parent_host, const float* o_part, const float* lse_part,
+                       const void* sync, size_t sync_bytes, const void* out, int help_after_us,
+                       BlockMask* mask) {
+  if (!sync) return RV_ERR_NULL;
+  rv_status st = check_prefix(q, k_cache, v_cache, seq_lens, max_seq_len, B, Hq, Hkv, n, d, L_max,
+                              sm_scale, split_len, num_splits, o_part, lse_part);
+  if (st != RV_OK) return st;
+  st = check_block_merge(q, k_blk, v_blk, parent_host, o_part, lse_part, num_splits, B, Hq, Hkv,
+                         n, d, sm_scale, out, mask);
+  if (st != RV_OK) return st;
+  if (!aligned16(sync)) return RV_ERR_ALIGNMENT;
+  if (sync_bytes < verify_sync_bytes(B, Hkv)) return RV_ERR_WORKSPACE;
+  if (help_after_us > kVerifyHelpMaxUs) return RV_ERR_VALUE;
+  return RV_OK;
+}
+
 rv_status check_window(const void* q, const void* k_ring, const void* v_ring,
                        const int32_t* pos, int B, int Hq, int Hkv, int n, int d, int cap,
                        int sink, int window, float sm_scale, const void* out,
@@ -358,6 +378,27 @@ rv_status rv_prefix_balanced_split(const int32_t* seq_lens_host, int B, int Hq, 
   *split_len = len;
   *num_splits = (int)S;
   return RV_OK;
+}
+
+size_t spec_attn_verify_sync_size(int B, int Hkv) {
+  if (B < 1 || Hkv < 1 || B > 65535 || Hkv > 65535) return 0;
+  return rv::verify_sync_bytes(B, Hkv);
+}
+
+int rv_verify_single_launch(int B, int Hq, int Hkv, int n, int d, int num_splits, int num_cus) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || n < 1 || Hq % Hkv != 0 || num_cus < 1) return 0;
+  if (n > RV_MAX_BLOCK_ROWS || (int64_t)(Hq / Hkv) * n > RV_MAX_GROUP_ROWS) return 0;
+  if (d != 64 && d != 128) return 0;
+  if (num_splits < 1 || num_splits > rv::kVerifyMaxSplits) return 0;
+  const rv::RowPlan rp = rv::row_plan(Hq, Hkv, n);
+  if (rp.wide) return 0;
+  // d = 128 with 4 row tiles: the fused kernel would exceed 512 registers
+  if (d == 128 && rp.MT == 4) return 0;
+  // at most one merged row per wave, a small grid, and every workgroup of it
+  // resident at once (one per compute unit)
+  if ((rp.M + num_splits - 1) / num_splits > rv::kWavesPerGroup) return 0;
+  const int64_t groups = (int64_t)B * Hkv * num_splits;
+  return groups <= rv::kVerifySingleMaxGroups && groups <= num_cus ? 1 : 0;
 }
 
 }  // extern "C"

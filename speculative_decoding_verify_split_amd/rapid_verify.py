@@ -59,6 +59,13 @@ def load_library():
     lib.spec_attn_block_merge.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                           f32, vp, vp, vp]
     lib.spec_attn_block_merge.restype = i32
+    lib.spec_attn_verify_sync_size.argtypes = [i32, i32]
+    lib.spec_attn_verify_sync_size.restype = sz
+    lib.rv_verify_single_launch.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.rv_verify_single_launch.restype = i32
+    lib.spec_attn_verify.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, i64, f32, i64,
+                                     i32, vp, vp, vp, vp, vp, vp, sz, vp, vp, i32, vp, vp, vp]
+    lib.spec_attn_verify.restype = i32
     lib.spec_attn_window_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.spec_attn_window_workspace_size.restype = sz
     lib.spec_attn_window.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32,
@@ -267,6 +274,63 @@ def spec_attn_block_merge(q, k_blk, v_blk, parent, o_part, lse_part, out, lse_ou
         _ptr(q), _ptr(k_blk), _ptr(v_blk), ctypes.cast(par, ctypes.c_void_p) if par else None,
         _ptr(o_part), _ptr(lse_part), S, B, Hq, Hkv, n, d, float(sm_scale), _ptr(out),
         _ptr(lse_out), _stream(stream)), "spec_attn_block_merge")
+
+
+def spec_attn_verify_sync_size(B, Hkv):
+    """Bytes of spec_attn_verify's sync words (0 for invalid sizes)."""
+    return int(load_library().spec_attn_verify_sync_size(B, Hkv))
+
+
+def rv_verify_single_launch(B, Hq, Hkv, n, d, num_splits, num_cus=None):
+    """True when spec_attn_verify takes the single launch; num_cus defaults
+    to the current device's compute-unit count."""
+    if num_cus is None:
+        import torch
+        num_cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    return bool(load_library().rv_verify_single_launch(B, Hq, Hkv, n, d, int(num_splits),
+                                                       int(num_cus)))
+
+
+def _event(ev):
+    return ctypes.c_void_p(ev) if isinstance(ev, int) else ev
+
+
+def spec_attn_verify(q, k_cache, v_cache, seq_lens, max_seq_len, split_len, num_splits, k_blk,
+                     v_blk, parent, o_part, lse_part, sync, out, lse_out=None, sm_scale=1.0,
+                     help_after_us=-1, stream=None, start_event=None, stop_event=None):
+    """History pass, block pass and merge, in one launch where the device
+    holds the history pass at once.  Shapes as spec_attn_prefix and
+    spec_attn_block_merge; sync: a uint8 GPU tensor of at least
+    spec_attn_verify_sync_size(B, Hkv) bytes, zero-filled before its first
+    use (every call leaves it zero)."""
+    import torch
+    _need(q, "q", torch.bfloat16)
+    B, Hq, n, d = q.shape
+    _need(k_cache, "k_cache", torch.bfloat16)
+    Hkv, L_max = k_cache.shape[1], k_cache.shape[2]
+    _need(k_cache, "k_cache", torch.bfloat16, (B, Hkv, L_max, d))
+    _need(v_cache, "v_cache", torch.bfloat16, (B, Hkv, L_max, d))
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    _need(k_blk, "k_blk", torch.bfloat16, (B, Hkv, n, d))
+    _need(v_blk, "v_blk", torch.bfloat16, (B, Hkv, n, d))
+    _need(o_part, "o_part", torch.float32, (B, Hq, n, num_splits, d))
+    _need(lse_part, "lse_part", torch.float32, (B, Hq, n, num_splits))
+    _need(sync, "sync", torch.uint8)
+    _need(out, "out", torch.bfloat16, (B, Hq, n, d))
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, (B, Hq, n))
+    par = None
+    if parent is not None:
+        vals = [int(x) for x in parent]
+        if len(vals) != n:
+            raise ValueError("parent must have n entries")
+        par = (ctypes.c_int32 * n)(*vals)
+    _check(load_library().spec_attn_verify(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), int(max_seq_len), B, Hq, Hkv, n, d,
+        L_max, float(sm_scale), int(split_len), int(num_splits), _ptr(k_blk), _ptr(v_blk),
+        ctypes.cast(par, ctypes.c_void_p) if par else None, _ptr(o_part), _ptr(lse_part),
+        _ptr(sync), sync.numel(), _ptr(out), _ptr(lse_out), int(help_after_us), _stream(stream),
+        _event(start_event), _event(stop_event)), "spec_attn_verify")
 
 
 def spec_attn_window_workspace_size(B, Hq, n, d, sink, window):

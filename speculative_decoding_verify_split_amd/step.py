@@ -61,6 +61,9 @@ class VerifyStep:
             self.lse_blk = torch.empty((B, Hq, n), dtype=f32, device=device)
             self.out = torch.empty((B, Hq, n, d), dtype=torch.bfloat16, device=device)
             self.lse_out = torch.empty((B, Hq, n), dtype=f32, device=device)
+            # spec_attn_verify's sync words: zero once, left zero by every call
+            self.sync = torch.zeros((rv.spec_attn_verify_sync_size(B, Hkv),), dtype=torch.uint8,
+                                    device=device)
         self.vocab = vocab
         self.flags = int(flags)
         if vocab is not None:
@@ -80,14 +83,23 @@ class VerifyStep:
             self.p_hat = (torch.empty((Bv, self.gamma, V), dtype=f32, device=device)
                           if want_p_hat else None)
 
-    def attention(self, k_cache=None, v_cache=None, stream=None, fused=False, block=True):
+    def attention(self, k_cache=None, v_cache=None, stream=None, fused=False, block=True,
+                  single=False, help_after_us=-1, events=(None, None)):
         """The attention calls; k_cache/v_cache override the resident cache
         (same shape), e.g. to rotate copies when timing.  fused: the block
         pass and the merge as one spec_attn_block_merge call (o_blk and
-        lse_blk are then left untouched).  block=False: no draft block, the
-        history partials are merged alone (a drafter's cross-attention)."""
+        lse_blk are then left untouched).  single: the whole attention as one
+        spec_attn_verify call (events: its start/stop hipEvent_t handles).
+        block=False: no draft block, the history partials are merged alone
+        (a drafter's cross-attention)."""
         kc = self.k_cache if k_cache is None else k_cache
         vc = self.v_cache if v_cache is None else v_cache
+        if single:
+            rv.spec_attn_verify(self.q, kc, vc, self.seq_lens, self.max_seq_len, self.split_len,
+                                self.num_splits, self.k_blk, self.v_blk, self.parent, self.o_part,
+                                self.lse_part, self.sync, self.out, self.lse_out, self.sm_scale,
+                                help_after_us, stream, events[0], events[1])
+            return
         rv.spec_attn_prefix(self.q, kc, vc, self.seq_lens, self.max_seq_len, self.split_len,
                             self.num_splits, self.o_part, self.lse_part, self.sm_scale, stream)
         if not block:
@@ -113,9 +125,9 @@ class VerifyStep:
             rv.rapid_accept(z, y, self.draft, self.r, self.u, self.T, self.eta, self.n_accept,
                             self.out_tokens, self.workspace, self.ratio, self.p_hat, stream)
 
-    def run(self, stream=None, fused=False):
+    def run(self, stream=None, fused=False, single=False):
         if self.attn is not None:
-            self.attention(stream=stream, fused=fused)
+            self.attention(stream=stream, fused=fused, single=single)
         if self.vocab is not None:
             self.accept(stream=stream)
 

@@ -38,7 +38,8 @@ def declared_functions():
 def test_header_declares_the_four_calls():
     names = declared_functions()
     for n in ("spec_attn_prefix", "spec_attn_prefix_ev", "spec_attn_block", "lse_merge",
-              "spec_attn_block_merge",
+              "spec_attn_block_merge", "spec_attn_verify", "spec_attn_verify_sync_size",
+              "rv_verify_single_launch",
               "spec_attn_window", "spec_attn_window_workspace_size",
               "rapid_accept", "rapid_accept_ex", "rapid_accept_workspace_size",
               "rv_status_string", "rv_prefix_default_split", "rv_prefix_balanced_split"):
@@ -103,6 +104,67 @@ def test_prefix_ev_validates_like_prefix(lib):
     bad = list(base)
     bad[11] = 0.0
     assert lib.spec_attn_prefix_ev(*bad, None, None) == RV_ERR_VALUE
+
+
+def _verify(lib, parent=None, **kw):
+    a = dict(q=P, k=P, v=P, lens=P, max_seq_len=4096, B=1, Hq=8, Hkv=2, n=5, d=64, L_max=4096,
+             scale=1.0, split_len=1024, S=4, kb=P, vb=P, o=P, lse=P, sync=P, sync_bytes=32,
+             out=P, lse_out=None, help=-1)
+    a.update(kw)
+    par = None
+    if parent is not None:
+        arr = (ctypes.c_int32 * len(parent))(*parent)
+        par = ctypes.cast(arr, ctypes.c_void_p)
+    return lib.spec_attn_verify(a["q"], a["k"], a["v"], a["lens"], a["max_seq_len"], a["B"],
+                                a["Hq"], a["Hkv"], a["n"], a["d"], a["L_max"], a["scale"],
+                                a["split_len"], a["S"], a["kb"], a["vb"], par, a["o"], a["lse"],
+                                a["sync"], a["sync_bytes"], a["out"], a["lse_out"], a["help"],
+                                None, None, None)
+
+
+def test_verify_validation(lib):
+    """spec_attn_verify checks everything spec_attn_prefix and
+    spec_attn_block_merge check, plus its sync words, before any HIP call."""
+    assert _verify(lib, q=None) == RV_ERR_NULL
+    assert _verify(lib, kb=None) == RV_ERR_NULL
+    assert _verify(lib, out=None) == RV_ERR_NULL
+    assert _verify(lib, sync=None) == RV_ERR_NULL
+    assert _verify(lib, d=96) == RV_ERR_UNSUPPORTED
+    assert _verify(lib, S=3) == RV_ERR_SHAPE
+    assert _verify(lib, split_len=1000) == RV_ERR_SHAPE
+    assert _verify(lib, scale=0.0) == RV_ERR_VALUE
+    assert _verify(lib, parent=[0, 0, 1, 2, 3]) == RV_ERR_VALUE  # root must be -1
+    assert _verify(lib, parent=[-1, 0, 2, 1, 3]) == RV_ERR_VALUE  # parent not earlier
+    assert _verify(lib, vb=MIS) == RV_ERR_ALIGNMENT
+    assert _verify(lib, sync=MIS) == RV_ERR_ALIGNMENT
+    assert _verify(lib, sync_bytes=31) == RV_ERR_WORKSPACE  # B * Hkv * 16 = 32
+    assert _verify(lib, B=2, lens=P, sync_bytes=32) == RV_ERR_WORKSPACE
+    assert _verify(lib, help=10 ** 7 + 1) == RV_ERR_VALUE
+
+
+def test_verify_sync_size_and_single_launch_rule(lib):
+    assert lib.spec_attn_verify_sync_size(1, 8) == 128
+    assert lib.spec_attn_verify_sync_size(3, 4) == 192
+    assert lib.spec_attn_verify_sync_size(0, 8) == 0
+    one = lib.rv_verify_single_launch
+    # the tiny workload: 8/2 heads, n = 5, 8 splits -> 16 workgroups, 3 rows each
+    assert one(1, 8, 2, 5, 64, 8, 256) == 1
+    assert one(1, 8, 2, 5, 64, 8, 15) == 0       # more workgroups than units
+    assert one(1, 8, 2, 5, 64, 4, 256) == 0      # 5 rows per workgroup
+    # the 8B shape: 8 kv heads x 32 splits = 256 workgroups, past the small grid
+    assert one(1, 32, 8, 11, 128, 32, 256) == 0
+    assert one(1, 32, 8, 11, 128, 8, 256) == 0   # 6 rows per workgroup
+    assert one(1, 32, 8, 1, 128, 8, 256) == 1    # n = 1: 4 rows, 64 workgroups
+    assert one(1, 32, 8, 1, 128, 9, 256) == 0    # 72 workgroups
+    assert one(2, 8, 2, 5, 64, 8, 256) == 1      # 32 workgroups
+    assert one(1, 64, 8, 11, 128, 8, 256) == 0   # 88 rows: the shared-stage kernel
+    assert one(1, 4, 1, 16, 128, 16, 256) == 0   # 64 rows at d = 128
+    assert one(1, 4, 1, 16, 64, 16, 256) == 1    # 64 rows at d = 64
+    assert one(1, 4, 1, 12, 128, 12, 256) == 1   # 48 rows at d = 128
+    assert one(1, 4, 1, 11, 128, 64, 256) == 1   # 64 splits, one row each
+    assert one(1, 4, 1, 11, 128, 65, 256) == 0   # more splits than mask bits
+    assert one(1, 7, 2, 5, 128, 4, 256) == 0     # Hq % Hkv != 0
+    assert one(1, 8, 2, 5, 96, 4, 256) == 0
 
 
 def _block(lib, parent=None, **kw):

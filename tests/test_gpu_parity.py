@@ -23,6 +23,7 @@ from workloads import (CONFIGS, config_attention, config_vocab, make_attention, 
                        tree_parents)
 from speculative_decoding_verify_split_amd.rapid_verify import (RV_ACCEPT_PRINTED_RESIDUAL,
                                                                 RV_ACCEPT_TAIL_PRESERVE)
+from speculative_decoding_verify_split_amd import rapid_verify as rv
 from speculative_decoding_verify_split_amd.step import VerifyStep
 
 pytestmark = pytest.mark.gpu
@@ -95,24 +96,42 @@ def test_attention_small(case):
     st = VerifyStep(ai, None, split=split)
     O_ref, L_ref = attn_ref(ai.q, ai.k_cache, ai.v_cache, ai.k_blk, ai.v_blk, ai.seq_lens,
                             ai.parent, ai.sm_scale)
+    B, Hq, n, d = ai.q.shape
+    single = rv.rv_verify_single_launch(B, Hq, ai.k_cache.shape[1], n, d, st.num_splits)
     res = {}
-    for fused in (False, True):
+    # block+merge, block_merge, then spec_attn_verify with the default wait
+    # and with help_after_us = 0 (every waiting workgroup computes missing
+    # splits itself at once: the help path)
+    for mode in ("split", "fused", "verify", "verify-help0"):
         st.out.zero_()
         st.lse_out.zero_()
-        st.attention(fused=fused)
+        if mode.startswith("verify"):
+            st.attention(single=True, help_after_us=0 if mode == "verify-help0" else -1)
+        else:
+            st.attention(fused=mode == "fused")
         out, lse = _attn_outputs(st)
         err = attn_row_errors(out, O_ref)
         dl = np.abs(lse - L_ref).max()
-        announce("  %s: max row rel err %.3e, max |dLSE| %.3e"
-                 % ("block_merge" if fused else "block+merge", err.max(), dl))
+        announce("  %s%s: max row rel err %.3e, max |dLSE| %.3e"
+                 % (mode, " (one launch)" if mode.startswith("verify") and single else "",
+                    err.max(), dl))
         assert err.max() <= ATTN_ROW_TOL
         assert dl <= _lse_tol(ai.q.shape[1], ai.k_cache.shape[1], ai.q.shape[2])
-        res[fused] = (out, lse)
-    # the fused call differs from the two calls only in fp32 rounding order,
+        res[mode] = (out, lse)
+    assert not st.sync.any()  # spec_attn_verify leaves its sync words zero
+    # the fused calls differ from the two calls only in fp32 rounding order,
     # so their bf16 outputs differ by at most one bf16 step (2^-7 of an
     # entry's binade): 7.8e-3 of the row's largest entry
-    assert attn_row_errors(res[True][0], res[False][0]).max() <= 1e-2
-    assert np.abs(res[True][1] - res[False][1]).max() <= 1e-4
+    for mode in ("fused", "verify"):
+        assert attn_row_errors(res[mode][0], res["split"][0]).max() <= 1e-2
+        assert np.abs(res[mode][1] - res["split"][1]).max() <= 1e-4
+    # a split computed on another's behalf has the same bits, so the help
+    # path changes nothing; without the single launch the call is the fused
+    # call's two launches
+    same = (("verify", "verify-help0"),) + ((("verify", "fused"),) if not single else ())
+    for a, b in same:
+        assert np.array_equal(res[a][0].view(np.uint32), res[b][0].view(np.uint32)), (a, b)
+        assert np.array_equal(res[a][1].view(np.uint32), res[b][1].view(np.uint32)), (a, b)
 
 
 # Batches of more than 64 sequences take the multi-chunk path of the history
@@ -610,18 +629,28 @@ def _config_attention_check(name):
     out, lse = _attn_outputs(st)
     lse_part = st.lse_part.cpu().numpy()
     lse_blk = st.lse_blk.cpu().numpy()
-    st.attention(fused=True)  # the benchmark's step runs the fused block + merge
+    st.attention(fused=True)  # the fused block + merge
     out_f, lse_f = _attn_outputs(st)
+    # the whole attention through spec_attn_verify (the benchmark's step),
+    # one launch where rv_verify_single_launch says so
+    single = rv.rv_verify_single_launch(B, Hq, Hkv, n, d, st.num_splits)
+    st.attention(single=True)
+    out_s, lse_s = _attn_outputs(st)
+    assert not st.sync.any()  # the sync words are left zero
     # properties at any size
-    for o, l in ((out, lse), (out_f, lse_f)):
+    for o, l in ((out, lse), (out_f, lse_f), (out_s, lse_s)):
         assert np.isfinite(o).all() and np.isfinite(l).all()
         assert np.all(l >= np.maximum(lse_part.max(axis=-1), lse_blk) - 1e-4)
-    assert attn_row_errors(out_f, out).max() <= 1e-2  # one bf16 step, as above
-    assert np.abs(lse_f - lse).max() <= 1e-4
+    for o, l in ((out_f, lse_f), (out_s, lse_s)):
+        assert attn_row_errors(o, out).max() <= 1e-2  # one bf16 step, as above
+        assert np.abs(l - lse).max() <= 1e-4
+    if not single:  # the same two launches as the fused call
+        assert np.array_equal(out_s.view(np.uint16), out_f.view(np.uint16))
+        assert np.array_equal(lse_s, lse_f)
     # every (sequence, query head, row) against the oracle, one kv head at a
     # time (the oracle's scores for a kv head are G*n rows by the history)
     tol = _lse_tol(Hq, Hkv, n)
-    worst = {False: (0.0, 0.0), True: (0.0, 0.0)}
+    worst = {False: (0.0, 0.0), True: (0.0, 0.0), "single": (0.0, 0.0)}
     G = Hq // Hkv
     for b in range(B):
         for g in range(Hkv):
@@ -630,17 +659,19 @@ def _config_attention_check(name):
                                     ai.v_cache[b:b + 1, g:g + 1], ai.k_blk[b:b + 1, g:g + 1],
                                     ai.v_blk[b:b + 1, g:g + 1], ai.seq_lens[b:b + 1], ai.parent,
                                     ai.sm_scale)
-            for fused, o, l in ((False, out, lse), (True, out_f, lse_f)):
+            for fused, o, l in ((False, out, lse), (True, out_f, lse_f),
+                                ("single", out_s, lse_s)):
                 err = attn_row_errors(o[b, heads], O_ref[0]).max()
                 dl = np.abs(l[b, heads] - L_ref[0]).max()
                 worst[fused] = (max(worst[fused][0], err), max(worst[fused][1], dl))
                 assert err <= ATTN_ROW_TOL, (b, g, fused, err)
                 assert dl <= tol, (b, g, fused, dl)
         announce("  b=%d: %d query heads x %d rows checked" % (b, Hq, n))
-    for fused in (False, True):
+    names = {False: "block+merge", True: "block_merge",
+             "single": "verify (%s)" % ("one launch" if single else "two launches")}
+    for fused in (False, True, "single"):
         announce("  %s: max row rel err %.3e, max |dLSE| %.3e over all %d rows"
-                 % ("block_merge" if fused else "block+merge", worst[fused][0], worst[fused][1],
-                    B * Hq * n))
+                 % (names[fused], worst[fused][0], worst[fused][1], B * Hq * n))
 
 
 # (llama8b_tp8: one GPU's share under 8-way head parallelism; its default
