@@ -59,3 +59,45 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for a, b in zip(ref, _outputs(st)):
             assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("single", [True, False], ids=["one-launch", "two-launches"])
+def test_graph_replay_of_spec_attn_verify(single):
+    """spec_attn_verify captured in a graph: the single launch (whose sync
+    words each call leaves zero) and the two launches replay to the eager
+    result, with eager calls between the replays."""
+    from speculative_decoding_verify_split_amd import rapid_verify as rv
+    # 8/2 heads, d = 64, n = 5 at 4096 tokens: 16 workgroups (one launch);
+    # at 40960 tokens the default split gives too many for one launch
+    L = 4096 if single else 40960
+    ai = make_attention(62, 1, 8, 2, 64, 5, [L])
+    st = VerifyStep(ai, None)
+    assert rv.rv_verify_single_launch(1, 8, 2, 5, 64, st.num_splits) == single
+    print("[gpu-case] graph replay of spec_attn_verify, %s" % ("one launch" if single else
+                                                             "two launches"), flush=True)
+    st.attention(single=True)
+    torch.cuda.synchronize()
+    ref = (st.out.view(torch.int16).clone(), st.lse_out.clone())
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        st.attention(single=True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.attention(single=True)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        st.out.fill_(float("nan"))
+        st.lse_out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st.out.view(torch.int16), ref[0]), "replay %d differs" % rep
+        assert torch.equal(st.lse_out, ref[1]), "replay %d differs" % rep
+        assert not st.sync.any()
+        st.attention(single=True)  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(st.out.view(torch.int16), ref[0])
