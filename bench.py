@@ -3,25 +3,28 @@
 
 One step is the whole hot path on one batch of synthetic inputs: the verify
 attention -- history pass over the KV cache, masked draft block and
-log-sum-exp merge -- as one spec_attn_verify call (a single launch at the
-default workload; --attention block_merge runs spec_attn_prefix then
-spec_attn_block_merge, --attention unfused spec_attn_prefix, spec_attn_block
-and lse_merge), and rapid_accept (RAPID's vocabulary pass), back to back on
-one stream.  Default workload: the
-LLaMA-3.1-8B-shaped verify layer
-(32 query / 8 kv heads, d=128, 131072-token bf16 KV cache, gamma=10, vocab
-128256, T=1, eta=0.5), inputs resident in HBM.  Three copies of the KV cache
-and of the logits rotate from step to step so that no step reads what the
-previous one left in the 256 MB last-level cache.
+log-sum-exp merge -- as one spec_attn_verify call (at the default workload
+its two launches, spec_attn_prefix's history kernel then the fused block +
+merge; a single launch on small grids), and rapid_accept (RAPID's
+vocabulary pass), back to back on one stream.  --attention block_merge makes
+the spec_attn_prefix and spec_attn_block_merge calls separately,
+--attention unfused spec_attn_prefix, spec_attn_block and lse_merge.
+Default workload: the LLaMA-3.1-8B-shaped verify layer (32 query / 8 kv
+heads, d=128, 131072-token bf16 KV cache, gamma=10, vocab 128256, T=1,
+eta=0.5), inputs resident in HBM.  Three copies of the KV cache and of the
+logits rotate from step to step so that no step reads what the previous one
+left in the 256 MB last-level cache.
 
 Prints one JSON line: steps/s (value: K steps timed with nothing else on the
-stream), per-kernel device times from HIP events recorded on the library's
-stream during a second, untimed pass over the same K steps (the attention's
-pair rides on its own dispatches), the KV-stream bandwidth, the roofline of
-the attention kernel, and the fp64 CPU oracle timed on the host as
-a reported baseline, which also checks one step of the library's outputs on
-the same inputs and reports their acceptance statistics.  A plain 2 GiB
-device copy is measured before the warm-up (context for the peak).
+stream); per-kernel device times from HIP events recorded during a second,
+untimed pass over the same K steps, the attention's pair riding on its own
+dispatches (KV-stream = K+V bytes over that span); the history kernel's own
+duration from a third untimed pass in which its events ride on its own
+dispatch (the roofline's kernel, when the attention takes two launches);
+and the fp64 CPU oracle timed on the host as a reported baseline, which
+also checks one step of the library's outputs on the same inputs and
+reports their acceptance statistics.  A plain 2 GiB device copy is measured
+before the warm-up (context for the peak).
 """
 
 import argparse
