@@ -16,7 +16,8 @@
  *      spec_attn_block   -- attention among the draft rows under the causal
  *                           or tree mask;
  *      lse_merge         -- log-sum-exp merge of all partials;
- *      spec_attn_block_merge -- the last two in one launch;
+ *      spec_attn_block_merge -- the last two in one launch (spec_attn_block_merge_ev
+ *                           also records timing events on its kernel);
  *      spec_attn_verify  -- all three in one launch where the device holds
  *                           the history pass at once.
  *    The LongSpec drafter's own attention (same summary, sections 2.1-2.2)
@@ -239,6 +240,17 @@ rv_status spec_attn_block_merge(const void* q, const void* k_blk, const void* v_
                                 const int32_t* parent_host, const float* o_part,
                                 const float* lse_part, int S, int B, int Hq, int Hkv, int n,
                                 int d, float sm_scale, void* out, float* lse_out, void* stream);
+
+/*
+ * spec_attn_block_merge_ev -- spec_attn_block_merge that also records two
+ * caller-created HIP events (either may be NULL) on its kernel's own
+ * dispatch, as spec_attn_prefix_ev does for the history kernel.
+ */
+rv_status spec_attn_block_merge_ev(const void* q, const void* k_blk, const void* v_blk,
+                                   const int32_t* parent_host, const float* o_part,
+                                   const float* lse_part, int S, int B, int Hq, int Hkv, int n,
+                                   int d, float sm_scale, void* out, float* lse_out,
+                                   void* stream, void* start_event, void* stop_event);
 
 /*
  * spec_attn_verify -- the whole verify attention (spec_attn_prefix, then

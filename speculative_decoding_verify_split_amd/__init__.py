@@ -26,6 +26,7 @@ from .rapid_verify import (  # noqa: F401
     rv_version,
     spec_attn_block,
     spec_attn_block_merge,
+    spec_attn_block_merge_ev,
     spec_attn_prefix,
     spec_attn_prefix_ev,
     spec_attn_verify,

@@ -1258,5 +1258,5 @@ extern "C" rv_status spec_attn_verify(const void* q, const void* k_cache, const 
                          split_len, num_splits, o_part, lse_part, s, e0, nullptr);
   if (st != RV_OK) return st;
   return rv::block_merge_launch(q, k_blk, v_blk, mask, o_part, lse_part, num_splits, B, Hq, Hkv, n,
-                                d, scale_log2, out, lse_out, stream, stop_event);
+                                d, scale_log2, out, lse_out, stream, nullptr, stop_event);
 }

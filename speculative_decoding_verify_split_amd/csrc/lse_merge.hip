@@ -149,14 +149,15 @@ __global__ __launch_bounds__(NWV * 64) void block_merge_kernel(
 // (FB) and waves per row (NWV); the index 0..3 selects one of the four.
 int fold_shape(int S) { return S <= 32 ? 0 : (S <= 64 ? 1 : (S <= 128 ? 2 : 3)); }
 
-// With a stop event the launch records it on the kernel's own dispatch.
+// With events the launch records them on the kernel's own dispatch.
 template <int D, int FB, int NWV>
-void launch_block_merge(dim3 grid, hipStream_t s, hipEvent_t ev_stop, const uint16_t* q,
-                        const uint16_t* k, const uint16_t* v, const BlockMask& mask, int Hq,
-                        int G, int n, float scale_log2, const float* o_part,
-                        const float* lse_part, int S, uint16_t* out, float* lse_out) {
-  if (ev_stop != nullptr)
-    hipExtLaunchKernelGGL((block_merge_kernel<D, FB, NWV>), grid, dim3(NWV * 64), 0, s, nullptr,
+void launch_block_merge(dim3 grid, hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop,
+                        const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const BlockMask& mask, int Hq, int G, int n, float scale_log2,
+                        const float* o_part, const float* lse_part, int S, uint16_t* out,
+                        float* lse_out) {
+  if (ev_start != nullptr || ev_stop != nullptr)
+    hipExtLaunchKernelGGL((block_merge_kernel<D, FB, NWV>), grid, dim3(NWV * 64), 0, s, ev_start,
                           ev_stop, 0, q, k, v, mask, Hq, G, n, scale_log2, o_part, lse_part, S,
                           out, lse_out);
   else
@@ -179,8 +180,10 @@ namespace rv {
 rv_status block_merge_launch(const void* q, const void* k_blk, const void* v_blk,
                              const BlockMask& mask, const float* o_part, const float* lse_part,
                              int S, int B, int Hq, int Hkv, int n, int d, float scale_log2,
-                             void* out, float* lse_out, void* stream, void* stop_event) {
+                             void* out, float* lse_out, void* stream, void* start_event,
+                             void* stop_event) {
   hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t ev0 = static_cast<hipEvent_t>(start_event);
   hipEvent_t ev = static_cast<hipEvent_t>(stop_event);
   dim3 grid((unsigned)(B * Hq * n));
   const uint16_t* qq = static_cast<const uint16_t*>(q);
@@ -191,7 +194,7 @@ rv_status block_merge_launch(const void* q, const void* k_blk, const void* v_blk
   const int fs = fold_shape(S);
 #define RV_BM_CASE(DD, F, FB, NWV)                                                           \
   if (d == DD && fs == F)                                                                    \
-    launch_block_merge<DD, FB, NWV>(grid, s, ev, qq, kk, vv, mask, Hq, G, n, scale_log2,     \
+    launch_block_merge<DD, FB, NWV>(grid, s, ev0, ev, qq, kk, vv, mask, Hq, G, n, scale_log2, \
                                     o_part, lse_part, S, o16, lse_out);
   RV_BM_CASE(64, 0, 8, 4)
   else RV_BM_CASE(64, 1, 16, 4)
@@ -219,7 +222,22 @@ extern "C" rv_status spec_attn_block_merge(const void* q, const void* k_blk, con
   if (st != RV_OK) return st;
   const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
   return rv::block_merge_launch(q, k_blk, v_blk, mask, o_part, lse_part, S, B, Hq, Hkv, n, d,
-                                scale_log2, out, lse_out, stream, nullptr);
+                                scale_log2, out, lse_out, stream, nullptr, nullptr);
+}
+
+extern "C" rv_status spec_attn_block_merge_ev(const void* q, const void* k_blk, const void* v_blk,
+                                              const int32_t* parent_host, const float* o_part,
+                                              const float* lse_part, int S, int B, int Hq,
+                                              int Hkv, int n, int d, float sm_scale, void* out,
+                                              float* lse_out, void* stream, void* start_event,
+                                              void* stop_event) {
+  rv::BlockMask mask;
+  rv_status st = rv::check_block_merge(q, k_blk, v_blk, parent_host, o_part, lse_part, S, B, Hq,
+                                       Hkv, n, d, sm_scale, out, &mask);
+  if (st != RV_OK) return st;
+  const float scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  return rv::block_merge_launch(q, k_blk, v_blk, mask, o_part, lse_part, S, B, Hq, Hkv, n, d,
+                                scale_log2, out, lse_out, stream, start_event, stop_event);
 }
 
 extern "C" rv_status lse_merge(const float* o_part, const float* lse_part, int S,

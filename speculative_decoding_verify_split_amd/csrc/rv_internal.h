@@ -48,11 +48,13 @@ rv_status check_block_merge(const void* q, const void* k_blk, const void* v_blk,
                             float sm_scale, const void* out, BlockMask* mask);
 
 // The block + merge launch of spec_attn_block_merge with a prebuilt mask;
-// stop_event (a hipEvent_t or NULL) is recorded on the kernel's own dispatch.
+// start_event and stop_event (hipEvent_t or NULL) are recorded on the
+// kernel's own dispatch.
 rv_status block_merge_launch(const void* q, const void* k_blk, const void* v_blk,
                              const BlockMask& mask, const float* o_part, const float* lse_part,
                              int S, int B, int Hq, int Hkv, int n, int d, float scale_log2,
-                             void* out, float* lse_out, void* stream, void* stop_event);
+                             void* out, float* lse_out, void* stream, void* start_event,
+                             void* stop_event);
 
 // --- single-launch verify pass (spec_attn_verify) -----------------------------
 

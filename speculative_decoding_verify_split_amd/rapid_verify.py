@@ -59,6 +59,9 @@ def load_library():
     lib.spec_attn_block_merge.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                           f32, vp, vp, vp]
     lib.spec_attn_block_merge.restype = i32
+    lib.spec_attn_block_merge_ev.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                             i32, f32, vp, vp, vp, vp, vp]
+    lib.spec_attn_block_merge_ev.restype = i32
     lib.spec_attn_verify_sync_size.argtypes = [i32, i32]
     lib.spec_attn_verify_sync_size.restype = sz
     lib.rv_verify_single_launch.argtypes = [i32, i32, i32, i32, i32, i32, i32]
@@ -331,6 +334,37 @@ def spec_attn_verify(q, k_cache, v_cache, seq_lens, max_seq_len, split_len, num_
         ctypes.cast(par, ctypes.c_void_p) if par else None, _ptr(o_part), _ptr(lse_part),
         _ptr(sync), sync.numel(), _ptr(out), _ptr(lse_out), int(help_after_us), _stream(stream),
         _event(start_event), _event(stop_event)), "spec_attn_verify")
+
+
+def spec_attn_block_merge_ev(q, k_blk, v_blk, parent, o_part, lse_part, out, start_event,
+                             stop_event, lse_out=None, sm_scale=1.0, stream=None):
+    """spec_attn_block_merge recording two caller-created hipEvent_t handles
+    (ints or ctypes pointers; None allowed) on its kernel's own dispatch."""
+    import torch
+    _need(q, "q", torch.bfloat16)
+    B, Hq, n, d = q.shape
+    _need(k_blk, "k_blk", torch.bfloat16)
+    Hkv = k_blk.shape[1]
+    _need(k_blk, "k_blk", torch.bfloat16, (B, Hkv, n, d))
+    _need(v_blk, "v_blk", torch.bfloat16, (B, Hkv, n, d))
+    _need(o_part, "o_part", torch.float32)
+    S = o_part.shape[3]
+    _need(o_part, "o_part", torch.float32, (B, Hq, n, S, d))
+    _need(lse_part, "lse_part", torch.float32, (B, Hq, n, S))
+    _need(out, "out", torch.bfloat16, (B, Hq, n, d))
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, (B, Hq, n))
+    par = None
+    if parent is not None:
+        vals = [int(x) for x in parent]
+        if len(vals) != n:
+            raise ValueError("parent must have n entries")
+        par = (ctypes.c_int32 * n)(*vals)
+    _check(load_library().spec_attn_block_merge_ev(
+        _ptr(q), _ptr(k_blk), _ptr(v_blk), ctypes.cast(par, ctypes.c_void_p) if par else None,
+        _ptr(o_part), _ptr(lse_part), S, B, Hq, Hkv, n, d, float(sm_scale), _ptr(out),
+        _ptr(lse_out), _stream(stream), _event(start_event), _event(stop_event)),
+        "spec_attn_block_merge_ev")
 
 
 def spec_attn_window_workspace_size(B, Hq, n, d, sink, window):

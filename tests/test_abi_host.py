@@ -38,7 +38,8 @@ def declared_functions():
 def test_header_declares_the_four_calls():
     names = declared_functions()
     for n in ("spec_attn_prefix", "spec_attn_prefix_ev", "spec_attn_block", "lse_merge",
-              "spec_attn_block_merge", "spec_attn_verify", "spec_attn_verify_sync_size",
+              "spec_attn_block_merge", "spec_attn_block_merge_ev", "spec_attn_verify",
+              "spec_attn_verify_sync_size",
               "rv_verify_single_launch",
               "spec_attn_window", "spec_attn_window_workspace_size",
               "rapid_accept", "rapid_accept_ex", "rapid_accept_workspace_size",
@@ -211,34 +212,39 @@ def test_merge_validation(lib):
     assert _merge(lib, ob=None, lb=None, S=0) == RV_ERR_SHAPE  # neither: accepted shape-wise
 
 
-def _block_merge(lib, parent=None, **kw):
+def _block_merge(lib, parent=None, ev=False, **kw):
     a = dict(q=P, k=P, v=P, o=P, l=P, S=4, B=1, Hq=8, Hkv=2, n=5, d=64, scale=1.0, out=P, lo=P)
     a.update(kw)
     par = None
     if parent is not None:
         arr = (ctypes.c_int32 * len(parent))(*parent)
         par = ctypes.cast(arr, ctypes.c_void_p)
-    return lib.spec_attn_block_merge(a["q"], a["k"], a["v"], par, a["o"], a["l"], a["S"], a["B"],
-                                     a["Hq"], a["Hkv"], a["n"], a["d"], a["scale"], a["out"],
-                                     a["lo"], None)
+    args = (a["q"], a["k"], a["v"], par, a["o"], a["l"], a["S"], a["B"], a["Hq"], a["Hkv"],
+            a["n"], a["d"], a["scale"], a["out"], a["lo"], None)
+    if ev:
+        return lib.spec_attn_block_merge_ev(*args, None, None)
+    return lib.spec_attn_block_merge(*args)
 
 
-def test_block_merge_validation(lib):
-    assert _block_merge(lib, q=None) == RV_ERR_NULL
-    assert _block_merge(lib, k=None) == RV_ERR_NULL
-    assert _block_merge(lib, o=None) == RV_ERR_NULL
-    assert _block_merge(lib, out=None) == RV_ERR_NULL
-    assert _block_merge(lib, S=0) == RV_ERR_SHAPE
-    assert _block_merge(lib, n=0) == RV_ERR_SHAPE
-    assert _block_merge(lib, Hq=7) == RV_ERR_SHAPE
-    assert _block_merge(lib, n=65) == RV_ERR_UNSUPPORTED
-    assert _block_merge(lib, d=96) == RV_ERR_UNSUPPORTED
-    assert _block_merge(lib, parent=[0, 0, 1, 2, 3]) == RV_ERR_VALUE
-    assert _block_merge(lib, parent=[-1, 0, 2, 1, 0]) == RV_ERR_VALUE
-    assert _block_merge(lib, scale=0.0) == RV_ERR_VALUE
-    assert _block_merge(lib, scale=float("inf")) == RV_ERR_VALUE
-    assert _block_merge(lib, l=MIS) == RV_ERR_ALIGNMENT
-    assert _block_merge(lib, out=MIS) == RV_ERR_ALIGNMENT
+@pytest.mark.parametrize("ev", [False, True], ids=["block_merge", "block_merge_ev"])
+def test_block_merge_validation(lib, ev):
+    def bm(_lib, **kw):
+        return _block_merge(_lib, ev=ev, **kw)
+    assert bm(lib, q=None) == RV_ERR_NULL
+    assert bm(lib, k=None) == RV_ERR_NULL
+    assert bm(lib, o=None) == RV_ERR_NULL
+    assert bm(lib, out=None) == RV_ERR_NULL
+    assert bm(lib, S=0) == RV_ERR_SHAPE
+    assert bm(lib, n=0) == RV_ERR_SHAPE
+    assert bm(lib, Hq=7) == RV_ERR_SHAPE
+    assert bm(lib, n=65) == RV_ERR_UNSUPPORTED
+    assert bm(lib, d=96) == RV_ERR_UNSUPPORTED
+    assert bm(lib, parent=[0, 0, 1, 2, 3]) == RV_ERR_VALUE
+    assert bm(lib, parent=[-1, 0, 2, 1, 0]) == RV_ERR_VALUE
+    assert bm(lib, scale=0.0) == RV_ERR_VALUE
+    assert bm(lib, scale=float("inf")) == RV_ERR_VALUE
+    assert bm(lib, l=MIS) == RV_ERR_ALIGNMENT
+    assert bm(lib, out=MIS) == RV_ERR_ALIGNMENT
 
 
 def _window(lib, **kw):

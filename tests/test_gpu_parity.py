@@ -375,6 +375,38 @@ def test_prefix_ev_matches_prefix_and_records_the_kernel():
     assert torch.equal(st.o_part, ref[0]) and torch.equal(st.lse_part, ref[1])
 
 
+def test_block_merge_ev_matches_block_merge_and_records_the_kernel():
+    """spec_attn_block_merge_ev writes the same output as
+    spec_attn_block_merge and its events bracket the kernel."""
+    import ctypes
+    from speculative_decoding_verify_split_amd import rapid_verify as rv
+    ai, split = _make_case(ATTN_CASES[0])
+    announce("spec_attn_block_merge_ev")
+    st = VerifyStep(ai, None, split=split)
+    st.attention(fused=True)
+    torch.cuda.synchronize()
+    ref = (st.out.clone(), st.lse_out.clone())
+    st.out.zero_()
+    st.lse_out.zero_()
+    hip = ctypes.CDLL("libamdhip64.so")
+    evs = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in evs:
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+    try:
+        rv.spec_attn_block_merge_ev(st.q, st.k_blk, st.v_blk, st.parent, st.o_part, st.lse_part,
+                                    st.out, evs[0], evs[1], st.lse_out, st.sm_scale)
+        torch.cuda.synchronize()
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), evs[0], evs[1]) == 0
+        announce("  kernel %.2f us" % (ms.value * 1e3))
+        assert ms.value > 0
+    finally:
+        for e in evs:
+            hip.hipEventDestroy(e)
+    assert torch.equal(st.out.view(torch.int16), ref[0].view(torch.int16))
+    assert torch.equal(st.lse_out, ref[1])
+
+
 def test_seq_lens_are_clamped_on_the_device():
     ai = make_attention(33, 3, 4, 2, 128, 4, [640, 640, 640], L_max=640)
     announce("seq_lens clamp")
