@@ -95,6 +95,19 @@ def test_tree_star_forced_rejections():
     assert np.all(ref["path"][:, 0] == 1)
 
 
+def test_tree_star_of_63_children():
+    """The widest tree: a root with 63 children (62 residual passes, 65
+    launches), uniforms near 1 so that rejections pile up, at V = 4096."""
+    n = 64
+    parent = np.array([-1] + [0] * 63, np.int32)
+    vi = make_tree_vocab(79, 3, parent, 4096, 3.0, 1.0, 1.0, 0.5)
+    vi.r[:] = np.float32(1.0 - 2 ** -24)
+    announce("rapid_tree_accept star of 63, forced rejections")
+    _check_tree(vi, "star63 reject")
+    vi.r[0, :] = 0.5
+    _check_tree(vi, "star63 mixed")
+
+
 def test_tree_workload_tree_full_vocab():
     """The 32-node tree of the 1M-token tree workload at V = 128256, eight
     sequences."""
