@@ -173,3 +173,34 @@ def test_verify_8b_shape_takes_two_launches():
     out, lse = _outputs(st)
     assert np.array_equal(_bits(out), _bits(out_f)) and np.array_equal(_bits(lse), _bits(lse_f))
     assert not st.sync.any()
+
+
+@pytest.mark.parametrize("L", [4096, 40960], ids=["one-launch", "two-launches"])
+def test_verify_events_bracket_the_attention(L):
+    """spec_attn_verify's start and stop events ride on its own dispatches:
+    positive elapsed time, and the output equals the call without events."""
+    import ctypes
+    ai = make_attention(63, 1, 8, 2, 64, 5, [L])
+    st = VerifyStep(ai, None)
+    announce("spec_attn_verify events, %d tokens, split %d x %d"
+             % (L, st.split_len, st.num_splits))
+    st.attention(single=True)
+    ref = _outputs(st)
+    hip = ctypes.CDLL("libamdhip64.so")
+    evs = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in evs:
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+    try:
+        st.out.zero_()
+        st.attention(single=True, events=(evs[0], evs[1]))
+        got = _outputs(st)
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), evs[0], evs[1]) == 0
+        announce("  %.2f us" % (ms.value * 1e3))
+        assert ms.value > 0
+    finally:
+        for e in evs:
+            hip.hipEventDestroy(e)
+    assert np.array_equal(_bits(got[0]), _bits(ref[0]))
+    assert np.array_equal(_bits(got[1]), _bits(ref[1]))
+    assert not st.sync.any()
