@@ -254,23 +254,24 @@ rv_status spec_attn_block_merge_ev(const void* q, const void* k_blk, const void*
 
 /*
  * spec_attn_verify -- the whole verify attention (spec_attn_prefix, then
- * spec_attn_block_merge) in one launch where the device can hold it (LongSpec
- * summary, section 2.3: an unmasked pass over the history, a masked pass over
- * the draft block, their outputs combined by log-sum-exp).  Each workgroup of
- * the history pass, once the other splits of its (sequence, kv head) are
- * done, merges a share of that group's rows, so the merge needs no launch of
- * its own.
+ * spec_attn_block_merge) in one call (LongSpec summary, section 2.3: an
+ * unmasked pass over the history, a masked pass over the draft block, their
+ * outputs combined by log-sum-exp).  On small grids it is one launch: each
+ * workgroup of the history pass, once the other splits of its (sequence,
+ * kv head) are done, merges a share of that group's rows, so the merge needs
+ * no launch of its own.  Otherwise it is the two launches.
  *
  *   q, k_cache, v_cache, seq_lens, max_seq_len, L_max, sm_scale, split_len,
  *   num_splits, o_part, lse_part   as spec_attn_prefix (o_part and lse_part
  *                                  are still written, then read back)
  *   k_blk, v_blk, parent_host      as spec_attn_block
  *   out, lse_out                   as spec_attn_block_merge
- *   sync        device scratch of spec_attn_verify_sync_size(B, Hkv) bytes,
- *               16-byte aligned, ZERO-FILLED by the caller before its first
- *               use; every call leaves it zero again.  Unlike the other
- *               workspaces it must not be shared by calls that may run at
- *               the same time (different streams).
+ *   sync        device scratch of spec_attn_verify_sync_size(B, Hkv) bytes
+ *               (sync_bytes smaller: RV_ERR_WORKSPACE), 16-byte aligned,
+ *               ZERO-FILLED by the caller before its first use; every call
+ *               leaves it zero again (the two-launch form does not touch
+ *               it).  Unlike the other workspaces it must not be shared by
+ *               calls that may run at the same time (different streams).
  *   help_after_us  microseconds a workgroup whose split is done waits for
  *               the rest before it computes a missing split itself (negative:
  *               200; 0 makes every waiting workgroup help at once; at most
