@@ -204,3 +204,56 @@ def test_verify_events_bracket_the_attention(L):
     assert np.array_equal(_bits(got[0]), _bits(ref[0]))
     assert np.array_equal(_bits(got[1]), _bits(ref[1]))
     assert not st.sync.any()
+
+
+def _random_single_launch_cases(seed=90, count=16):
+    """Seeded random shapes that take the single launch: d in {64, 128},
+    up to 64 rows per kv head (48 at d = 128), at most 64 workgroups, at most
+    4 rows per workgroup; ragged and empty lengths; chain, tree or star."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < count:
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.integers(1, 5))
+        G = int(rng.integers(1, 9))
+        n = int(rng.integers(1, 33))
+        M = G * n
+        if M > (48 if d == 128 else 64):
+            continue
+        B = int(rng.integers(1, 4))
+        S = int(rng.integers(-(-M // 4), 17))  # at least ceil(M / 4) splits
+        if B * Hkv * S > 64 or S > 64:
+            continue
+        split_len = 128 * int(rng.integers(1, 5))
+        lens = [int(x) for x in rng.integers(0, S * split_len + 1, size=B)]
+        parent = str(rng.choice(["chain", "tree", "star"])) if n > 1 else "chain"
+        cases.append((len(cases), B, G * Hkv, Hkv, d, n, lens, parent, (split_len, S)))
+    return cases
+
+
+RANDOM_SINGLE = _random_single_launch_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM_SINGLE, ids=["r%d" % c[0] for c in RANDOM_SINGLE])
+def test_verify_single_launch_random_shapes(case):
+    idx, B, Hq, Hkv, d, n, lens, kind, split = case
+    parent = None
+    if kind == "tree":
+        parent = tree_parents(np.random.SeedSequence(1000 + idx), n, min(5, n - 1))
+    elif kind == "star":
+        parent = np.array([-1] + [0] * (n - 1), np.int32)
+    L_max = max(max(lens), 1)
+    ai = make_attention(1000 + idx, B, Hq, Hkv, d, n, lens, L_max=L_max, parent=parent,
+                        pad_bits=0x7FC0)
+    assert rv.rv_verify_single_launch(B, Hq, Hkv, n, d, split[1])
+    announce("spec_attn_verify random r%d: B=%d Hq=%d Hkv=%d d=%d n=%d %s lens=%s split=%s"
+             % (idx, B, Hq, Hkv, d, n, kind, lens, split))
+    st = VerifyStep(ai, None, split=split)
+    st.attention(single=True)
+    out, lse = _outputs(st)
+    _check_oracle(ai, out, lse, "r%d" % idx)
+    st.out.zero_()
+    st.attention(single=True, help_after_us=0)
+    out0, lse0 = _outputs(st)
+    assert np.array_equal(_bits(out0), _bits(out)) and np.array_equal(_bits(lse0), _bits(lse))
+    assert not st.sync.any()
