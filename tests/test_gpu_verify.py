@@ -57,6 +57,7 @@ VERIFY_CASES = [
     ("s64-one-kv-head", 55, 1, 4, 1, 128, 11, [8192], None, (128, 64)),
     ("s1", 56, 2, 4, 2, 128, 2, [100, 128], None, (128, 1)),
     ("4-rows-per-group", 57, 1, 16, 4, 128, 4, [1024], None, (256, 4)),
+    ("all-empty-history", 58, 2, 4, 2, 64, 2, [0, 0], None, (128, 1)),
 ]
 
 
@@ -66,7 +67,9 @@ def _case(c):
         parent = tree_parents(np.random.SeedSequence(seed), n, 5)
     elif parent == "star":
         parent = np.array([-1] + [0] * (n - 1), np.int32)
-    return make_attention(seed, B, Hq, Hkv, d, n, lens, parent=parent, pad_bits=0x7FC0), split
+    L_max = max(max(lens), 128)  # (an empty cache still has a buffer)
+    return make_attention(seed, B, Hq, Hkv, d, n, lens, L_max=L_max, parent=parent,
+                          pad_bits=0x7FC0), split
 
 
 @pytest.mark.parametrize("case", VERIFY_CASES, ids=[c[0] for c in VERIFY_CASES])
