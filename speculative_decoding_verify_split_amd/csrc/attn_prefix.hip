@@ -203,21 +203,23 @@ struct TailArgs<true> {
 // wave), where it saves the second launch; on the full 8B-shaped layer the
 // cross-XCD publish and poll below cost more than a kernel boundary.
 //   * Publish: the split's partials are written with device-scope stores,
-//     which stay coherent across the XCDs' L2s without a writeback (plain
-//     stores behind an agent-scope release took ~20 us of L2 write-backs at
-//     256 workgroups); every wave waits for its stores to complete, then one
-//     thread sets the split's bit in the group's mask word.
+//     which leave no dirty lines in the XCD's L2 (plain stores made the
+//     release below write back ~20 us of L2 at 256 workgroups); every wave
+//     waits for its stores to complete, the workgroup meets at a barrier,
+//     and one thread sets the split's bit in the group's mask word with an
+//     agent-scope release.
 //   * Block part: then wave w computes the block attention of its first row
 //     (local row s + w S; block_row.h) while the other splits finish.
 //     (Before the split's first tiles, its time lands on every split;
 //     issuing its loads during the split's epilogue gained nothing.)
-//   * Wait: one thread polls the mask word.  The launch is used only when
-//     every workgroup of the grid fits on the device at once, but other work
-//     may hold compute units; so a workgroup that has waited help_ticks
-//     computes the first missing split after its own itself and publishes
-//     it.  A split computed twice is written twice with the same bits, and
-//     every wait ends: each help sets a bit, so after at most S helps the
-//     mask is full.
+//   * Wait: one thread polls the mask word, then takes an agent-scope
+//     acquire before the workgroup reads the partials.  The launch is used
+//     only when every workgroup of the grid fits on the device at once, but
+//     other work may hold compute units; so a workgroup that has waited
+//     help_ticks computes the first missing split after its own itself and
+//     publishes it.  A split computed twice is written twice with the same
+//     bits, and every wait ends: each help sets a bit, so after at most S
+//     helps the mask is full.
 //   * Merge: wave w merges rows s + w S, s + (w + 4) S, ...: the row's S
 //     partials (device-scope loads) in ascending split order against their
 //     maximum, then the block part, as in spec_attn_block_merge (one wave per
@@ -268,12 +270,13 @@ __device__ __forceinline__ void verify_tail(RunSplit& run_split, const TailArgs<
     }
   };
   // Every wave's device-scope partial stores complete, then split sp is
-  // marked done.
+  // marked done with a release: a workgroup that sees the bit and then
+  // acquires (wait() below) sees the partials.
   auto publish = [&](int sp) {
     wait_vm_stores();
     __syncthreads();
     if (threadIdx.x == 0)
-      __hip_atomic_fetch_or(mword, 1ull << sp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_or(mword, 1ull << sp, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   };
   // -1 once every split of the group is published (and this workgroup is
   // counted out), else the split to compute on another's behalf.
@@ -296,6 +299,9 @@ __device__ __forceinline__ void verify_tail(RunSplit& run_split, const TailArgs<
         }
         __builtin_amdgcn_s_sleep(2);
       }
+      // (pairs with the releases of the splits seen published; the barrier
+      // below passes the ordering on to the other waves)
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       if (next < 0) finish();
       sh_next = next;
     }

@@ -33,7 +33,8 @@
 //                  running total exceeds the target.
 // Every reduction and scan has a fixed order and the counter only decides
 // which workgroup runs the draw, so results are bit-exact run to run; no
-// workgroup ever waits for another.
+// workgroup waits for another to run (the drawing one waits at most for slot
+// stores already issued).
 
 #include <mutex>
 
@@ -53,12 +54,15 @@ __global__ __launch_bounds__(TPB) void stats_kernel(const float* __restrict__ z,
                                                     const float* __restrict__ y, int gamma, int V,
                                                     float invT2, int cs, float* __restrict__ zstat,
                                                     float* __restrict__ ystat,
-                                                    uint32_t* __restrict__ arrivals) {
+                                                    uint32_t* __restrict__ arrivals,
+                                                    uint64_t* __restrict__ slots, int cd) {
   constexpr int PER = kStatPer;
   const int c = blockIdx.x, r = blockIdx.y, b = blockIdx.z;
-  // The decide kernel counts chunk arrivals per sequence; start from zero on
-  // every call (the workspace is not assumed to be initialised).
+  // The decide kernel counts chunk arrivals per sequence and publishes its
+  // chunk weights in slots; start from zero and empty slots on every call
+  // (the workspace is not assumed to be initialised).
   if (c == 0 && r == 0 && threadIdx.x == 0) arrivals[(size_t)b * kArrivalStride] = 0u;
+  if (r == 0) clear_slots(slots + (size_t)b * cd, cd);
   const float* row;
   float* dst;
   if (r <= gamma) {
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(TPB) void decide_kernel(
     const float* __restrict__ z, const float* __restrict__ y, const int32_t* __restrict__ draft,
     const float* __restrict__ r, int gamma, int V, float invT2, float eta2, int cp, int cd,
     const float* __restrict__ sstat, const float* __restrict__ tstat, unsigned flags,
-    const float* __restrict__ rowtab, float* __restrict__ wsum,
+    const float* __restrict__ rowtab, uint64_t* __restrict__ wsum,
     uint32_t* __restrict__ arrivals, const float* __restrict__ u,
     int32_t* __restrict__ n_accept, int32_t* __restrict__ out_tokens,
     float* __restrict__ ratio_out, float* __restrict__ p_hat_out) {
@@ -363,29 +367,19 @@ __global__ __launch_bounds__(TPB) void decide_kernel(
     }
   }
   const float2 W = block_sum2(w0, w1);
-  // Publish this chunk's draw weights, then count its arrival.  The
-  // workgroup that arrives last draws the token: which workgroup that is
-  // does not change what is drawn, and nothing ever waits for another
-  // workgroup.  The weights are the only data another workgroup of this
-  // kernel reads, so they go out as device-scope atomic stores, and waiting
-  // for those stores to complete before the (device-scope) increment orders
-  // them ahead of it: the ordering of a release, without the write-back of
-  // the whole L2 that a release performs for ordinary stores.
+  // Publish this chunk's draw weights and count its arrival.  The workgroup
+  // that arrives last draws the token: which workgroup that is does not
+  // change what is drawn, and it waits only for stores already issued.
   __shared__ uint32_t sh_arrived;
-  if (threadIdx.x == 0) {
-    float* wc = wsum + ((size_t)b * cd + c) * 2;
-    __hip_atomic_store(wc, W.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(wc + 1, W.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    sh_arrived = __hip_atomic_fetch_add(arrivals + (size_t)b * kArrivalStride, 1u, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (threadIdx.x == 0)
+    sh_arrived = publish_and_arrive(wsum + (size_t)b * cd + c, W.x, W.y,
+                                    arrivals + (size_t)b * kArrivalStride);
   __syncthreads();
   if (sh_arrived != (uint32_t)(cd - 1)) return;  // uniform
   draw_from_chunks<VEC, kDrawPer>(
       z + ((size_t)b * (gamma + 1) + ts) * V,
       ts < gamma ? y + ((size_t)b * gamma + ts) * V : nullptr, u[(size_t)b * (gamma + 1) + ts], V,
-      cd, wsum + (size_t)b * cd * 2, out_tokens + (size_t)b * (gamma + 1) + ts,
+      cd, wsum + (size_t)b * cd, out_tokens + (size_t)b * (gamma + 1) + ts,
       [&](float zv, float yv, int kind) {
         return draw_weight(zv, yv, ts, gamma, kind, invT2, eta2, rc);
       });
@@ -402,10 +396,10 @@ hipError_t launch_accept(const float* z, const float* y, const int32_t* draft, c
   float* sstat = ws + L.sstat;
   float* rowtab = ws + L.rowtab;
   float* tstat = ws + L.tstat;
-  float* wsm = ws + L.wsum;
+  uint64_t* wsm = reinterpret_cast<uint64_t*>(ws + L.wsum);
   uint32_t* arrivals = reinterpret_cast<uint32_t*>(ws + L.arrivals);
   hipLaunchKernelGGL((stats_kernel<VEC>), dim3(L.cs, 2 * gamma + 1, B), dim3(TPB), 0, s, z, y,
-                     gamma, V, invT2, L.cs, zstat, ystat, arrivals);
+                     gamma, V, invT2, L.cs, zstat, ystat, arrivals, wsm, L.cd);
   hipLaunchKernelGGL((phat_kernel<VEC>), dim3(L.cp, gamma + 1, B), dim3(TPB), 0, s, z, y, draft,
                      gamma, V, invT2, eta2, L.cs, L.cp, zstat, ystat, sstat, rowtab);
   if (flags & RV_ACCEPT_TAIL_PRESERVE)

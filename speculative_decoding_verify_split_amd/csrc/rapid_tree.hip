@@ -42,11 +42,13 @@ __global__ __launch_bounds__(TPB) void tree_stats_kernel(const float* __restrict
                                                          int V, float invT2, int cs,
                                                          float* __restrict__ zstat,
                                                          float* __restrict__ ystat,
-                                                         uint32_t* __restrict__ arrivals) {
+                                                         uint32_t* __restrict__ arrivals,
+                                                         uint64_t* __restrict__ slots, int cd) {
   constexpr int PER = kStatPer;
   const int c = blockIdx.x, rr = blockIdx.y, b = blockIdx.z;
   const int n = tp.n;
   if (c == 0 && rr == 0 && threadIdx.x == 0) arrivals[(size_t)b * kArrivalStride] = 0u;
+  if (rr == 0) clear_slots(slots + (size_t)b * cd, cd);
   const float* row;
   float* dst;
   if (rr < n) {
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(TPB) void tree_decide_kernel(
     const float* __restrict__ z, const float* __restrict__ y, const int32_t* __restrict__ tokens,
     const float* __restrict__ r, const float* __restrict__ u, TreePlan tp, int V, float invT2,
     float eta2, int cp, int cd, const float* __restrict__ sstat,
-    const float* __restrict__ rowtab, const float* __restrict__ rstat, float* __restrict__ wsum,
+    const float* __restrict__ rowtab, const float* __restrict__ rstat, uint64_t* __restrict__ wsum,
     uint32_t* __restrict__ arrivals, int32_t* __restrict__ n_accept, int32_t* __restrict__ path,
     int32_t* __restrict__ out_tokens, float* __restrict__ ratio_out) {
   constexpr int PER = kDrawPer;
@@ -370,20 +372,15 @@ __global__ __launch_bounds__(TPB) void tree_decide_kernel(
     }
   }
   const float2 W = block_sum2(w0, w1);
-  // Publish, then count the arrival; the last workgroup to arrive draws (see
-  // decide_kernel of rapid_accept for the ordering).
+  // Publish and count the arrival; the last workgroup to arrive draws (as in
+  // decide_kernel of rapid_accept).
   __shared__ uint32_t sh_arrived;
-  if (threadIdx.x == 0) {
-    float* wc = wsum + ((size_t)b * cd + c) * 2;
-    __hip_atomic_store(wc, W.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(wc + 1, W.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    sh_arrived = __hip_atomic_fetch_add(arrivals + (size_t)b * kArrivalStride, 1u,
-                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (threadIdx.x == 0)
+    sh_arrived = publish_and_arrive(wsum + (size_t)b * cd + c, W.x, W.y,
+                                    arrivals + (size_t)b * kArrivalStride);
   __syncthreads();
   if (sh_arrived != (uint32_t)(cd - 1)) return;  // uniform
-  draw_from_chunks<VEC, PER>(zrow, yrow, u[(size_t)b * n + v], V, cd, wsum + (size_t)b * cd * 2,
+  draw_from_chunks<VEC, PER>(zrow, yrow, u[(size_t)b * n + v], V, cd, wsum + (size_t)b * cd,
                              out_tokens + (size_t)b * n + tc.m, wfun);
 }
 
@@ -397,10 +394,10 @@ hipError_t launch_tree(const float* z, const float* y, const int32_t* tokens, co
   float* sstat = ws + L.sstat;
   float* rowtab = ws + L.rowtab;
   float* rstat = ws + L.rstat;
-  float* wsm = ws + L.wsum;
+  uint64_t* wsm = reinterpret_cast<uint64_t*>(ws + L.wsum);
   uint32_t* arrivals = reinterpret_cast<uint32_t*>(ws + L.arrivals);
   hipLaunchKernelGGL((tree_stats_kernel<VEC>), dim3(L.cs, tp.n + tp.ni, B), dim3(TPB), 0, s, z,
-                     y, tp, V, invT2, L.cs, zstat, ystat, arrivals);
+                     y, tp, V, invT2, L.cs, zstat, ystat, arrivals, wsm, L.cd);
   hipLaunchKernelGGL((tree_phat_kernel<VEC>), dim3(L.cp, tp.ni + 1, B), dim3(TPB), 0, s, z, y, tp,
                      V, invT2, eta2, L.cs, L.cp, zstat, ystat, sstat, rowtab);
   for (int j = 1; j <= tp.npass; ++j)

@@ -140,7 +140,8 @@ struct AcceptLayout {
   size_t rowtab;       // [B][4][gamma+1]      base-2 LSE of z/T and y/T per row,
                        //                      then each draft token's z and y
   size_t tstat;        // [B][gamma][cp]       chunk sums of the tail-adjusted p_hat
-  size_t wsum;         // [B][cd][2]           residual and p_hat weight per chunk
+  size_t wsum;         // [B][cd] uint64       residual and p_hat weight per chunk
+                       //                      (one slot each, vocab_common.h)
   size_t arrivals;     // [B][kArrivalStride] uint32: chunks done with their draw weight
   size_t words;        // total
 };
@@ -179,7 +180,7 @@ struct TreeLayout {
   size_t sstat;        // [B][n][cp][2]  of s per internal slot
   size_t rowtab;       // [B][2][n]      base-2 LSE of z/T per node, of y/T per slot
   size_t rstat;        // [B][n][n][cp]  chunk sums of residual pass j per slot
-  size_t wsum;         // [B][cd][2]     draw weights per chunk
+  size_t wsum;         // [B][cd] uint64 draw weights per chunk (slots)
   size_t arrivals;     // [B][kArrivalStride]
   size_t words;
 };

@@ -13,6 +13,31 @@ namespace {
 
 constexpr int TPB = kVocabThreads;
 
+// Chunk draw-weight slots.  Each chunk of the decide pass publishes its two
+// weights as one 64-bit word with one device-scope atomic store; the pass's
+// first kernel sets every slot to kSlotEmpty, a bit pattern no published pair
+// takes, so the workgroup that draws can tell a slot whose store has not
+// landed yet and read it again.  A published slot holds (first weight, second
+// weight) in its (low, high) halves.
+constexpr uint64_t kSlotEmpty = ~0ull;
+
+__device__ __forceinline__ uint64_t pack_slot(float a, float b) {
+  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  // (only a NaN pair with every bit set can collide; publish it as another NaN)
+  return v == kSlotEmpty ? 0x7FC000007FC00000ull : v;
+}
+
+// Publishes one chunk's weights, then counts its arrival; returns the count
+// before this one.  The slot store is issued before the increment (the empty
+// asm keeps the compiler from moving it), so once the count shows every other
+// chunk arrived, every slot's store has been issued and will land.
+__device__ __forceinline__ uint32_t publish_and_arrive(uint64_t* slot, float a, float b,
+                                                       uint32_t* counter) {
+  __hip_atomic_store(slot, pack_slot(a, b), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("" ::: "memory");
+  return __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // x[e] = row[start + e] for e < N (zero at or past V).
 template <bool VEC, int N>
 __device__ __forceinline__ void load_run(const float* __restrict__ row, int V, int start,
@@ -101,6 +126,13 @@ __device__ float2 block_incl_scan2(float2 v, float2* total) {
   return make_float2(off.x + in.x, off.y + in.y);
 }
 
+// Sets the cd draw-weight slots of one sequence to kSlotEmpty, spread over
+// the workgroups of a grid's x dimension (the pass's first kernel).
+__device__ __forceinline__ void clear_slots(uint64_t* __restrict__ slots, int cd) {
+  for (int i = blockIdx.x * TPB + threadIdx.x; i < cd; i += gridDim.x * TPB)
+    slots[i] = kSlotEmpty;
+}
+
 // Index of the first thread with `hit` and of the last thread with `pos`
 // (-1 if none); every thread gets the same pair.
 __device__ int2 block_first_last(bool hit, bool pos) {
@@ -180,7 +212,7 @@ __device__ __forceinline__ void pq_s(float zv, float yv, float invT2, float eta2
 
 // Inverse CDF of one row with the caller's uniform, run by one whole
 // workgroup, over the cd chunks of TPB * PER elements whose weights (both
-// kinds) the pass has published at ws[2c], ws[2c + 1].  Chunk level: a scan
+// kinds) the pass has published in slots ws[c].  Chunk level: a scan
 // of the chunk weights (kind 1 only if the kind-0 weights have no mass at
 // all, which exact arithmetic rules out at a rejected row) picks the first
 // chunk of positive weight whose running total exceeds u * W; thread level:
@@ -192,19 +224,19 @@ __device__ __forceinline__ void pq_s(float zv, float yv, float invT2, float eta2
 // then 0); the chosen id goes to *out_slot.
 template <bool VEC, int PER, typename WF>
 __device__ void draw_from_chunks(const float* __restrict__ zrow, const float* __restrict__ yrow,
-                                 float u_val, int V, int cd, const float* __restrict__ ws,
+                                 float u_val, int V, int cd, const uint64_t* __restrict__ ws,
                                  int32_t* __restrict__ out_slot, WF wfun) {
   __shared__ float sh_base;
-  // The chunk weights were published by the other workgroups with
-  // device-scope atomic stores before their arrival was counted; read them
-  // with device-scope atomic loads, which do not return a stale copy from
-  // this workgroup's L2.
+  // Every chunk's slot store has been issued (publish_and_arrive); read each
+  // slot with device-scope atomic loads until its store has landed.
   auto chunk_w = [&](int i) {
-    return i < cd ? make_float2(
-                        __hip_atomic_load(ws + 2 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
-                        __hip_atomic_load(ws + 2 * i + 1, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT))
-                  : make_float2(0.f, 0.f);
+    if (i >= cd) return make_float2(0.f, 0.f);
+    uint64_t v = __hip_atomic_load(ws + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while (v == kSlotEmpty) {
+      __builtin_amdgcn_s_sleep(1);
+      v = __hip_atomic_load(ws + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
   };
   // Totals of both kinds, block of TPB chunks by block.  The last block's
   // values stay in registers (with cd <= TPB the only block).
