@@ -629,6 +629,37 @@ def test_accept_nonfinite_logits_stay_in_range(flags):
         assert np.all(tok[b, n + 1:] == -1)
 
 
+def test_accept_nan_with_every_bit_set_and_a_filled_workspace():
+    """A chunk's two draw weights travel as one 64-bit slot whose all-ones
+    pattern means "not yet written".  A bonus row of NaNs with every bit set
+    makes both weights that pattern; the pass publishes it as another NaN,
+    so the draw still ends with an id in [0, V).  The workspace starts
+    filled with 0xFF bytes (stale slots and counters), which the pass clears
+    itself."""
+    V, g = 5000, 4
+    vi = make_vocab(50, B=3, gamma=g, V=V, z_sigma=3.0, noise=1.0, T=1.0, eta=0.5)
+    vi.r[:] = 0.0                             # every draft accepted: the bonus row is drawn
+    zb = vi.z.view(np.uint32)
+    zb[0, g] = 0xFFFFFFFF                     # whole bonus row
+    zb[1, g, ::3] = 0xFFFFFFFF                # every third entry
+    announce("rapid_accept all-ones NaN bonus rows, 0xFF-filled workspace")
+    st = VerifyStep(None, vi, want_ratio=True)
+    for _ in range(2):
+        st.workspace.fill_(0xFF)
+        st.out_tokens.fill_(-7)
+        st.accept()
+        torch.cuda.synchronize()
+        n_g = st.n_accept.cpu().numpy()
+        tok = st.out_tokens.cpu().numpy()
+        assert list(n_g) == [g, g, g]
+        for b in range(3):
+            assert np.array_equal(tok[b, :g], vi.draft[b, :g])
+            assert 0 <= tok[b, g] < V, (b, tok[b])
+    ref = rapid_accept_ref(vi.z[2:], vi.y[2:], vi.draft[2:], vi.r[2:], vi.u[2:], 1.0, 0.5)
+    res = compare_accept(ref, n_g[2:], tok[2:], vi.r[2:], vi.u[2:], draft=vi.draft[2:])
+    assert not res["errors"]
+
+
 def test_step_is_bit_deterministic():
     ai = config_attention("tiny")
     vi = config_vocab("tiny")
