@@ -157,3 +157,33 @@ def test_tree_bad_token_sentinel():
     res = compare_tree_accept(ref, vi.parent, vi.tokens[:1], n_g[:1], path_g[:1], tok_g[:1],
                               vi.r[:1])
     assert not res["errors"], res["errors"]
+
+
+def test_tree_nan_with_every_bit_set_and_a_filled_workspace():
+    """The empty-slot pattern of the draw weights (every bit set) as the
+    leaves' target rows: with every first child accepted the walk ends at a
+    leaf and draws its bonus token from those NaNs, which must still give an
+    id in [0, V); the workspace starts filled with 0xFF bytes."""
+    parent = np.array([-1, 0, 0, 1, 1, 2], np.int32)
+    V = 3000
+    vi = make_tree_vocab(71, 2, parent, V, 3.0, 1.0, 1.0, 0.5)
+    vi.r[:] = 0.0
+    vi.z.view(np.uint32)[:, 3:] = 0xFFFFFFFF   # the leaves 3, 4, 5
+    B, n, _ = vi.z.shape
+    dev = {k: to_device(getattr(vi, k)) for k in ("z", "y", "tokens", "r", "u")}
+    n_acc = torch.empty((B,), dtype=torch.int32, device="cuda")
+    path = torch.empty((B, n), dtype=torch.int32, device="cuda")
+    tok = torch.empty((B, n), dtype=torch.int32, device="cuda")
+    ws = torch.full((rv.rapid_tree_accept_workspace_size(B, n, V),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    announce("rapid_tree_accept all-ones NaN leaves, 0xFF-filled workspace")
+    rv.rapid_tree_accept(dev["z"], dev["y"], dev["tokens"], list(parent), dev["r"], dev["u"],
+                         vi.T, vi.eta, n_acc, path, tok, ws)
+    torch.cuda.synchronize()
+    n_g, path_g, tok_g = n_acc.cpu().numpy(), path.cpu().numpy(), tok.cpu().numpy()
+    for b in range(B):
+        assert n_g[b] == 2 and list(path_g[b, :2]) == [1, 3], (n_g[b], path_g[b])
+        assert np.all(path_g[b, 2:] == -1)
+        assert list(tok_g[b, :2]) == [vi.tokens[b, 1], vi.tokens[b, 3]]
+        assert 0 <= tok_g[b, 2] < V, tok_g[b]
+        assert np.all(tok_g[b, 3:] == -1)
