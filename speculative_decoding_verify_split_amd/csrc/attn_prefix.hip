@@ -524,14 +524,16 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_kernel(
     bf16x8 pf[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      float mx = fmaxf(fmaxf(fmaxf(sacc[0][mt][0], sacc[0][mt][1]),
-                             fmaxf(sacc[0][mt][2], sacc[0][mt][3])),
-                       fmaxf(fmaxf(sacc[1][mt][0], sacc[1][mt][1]),
-                             fmaxf(sacc[1][mt][2], sacc[1][mt][3])));
-      mx = row_max4(mx);
-      const float m_tile = mx * scale_log2;
-      const bool raise = m_tile > m_run[mt] + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(raise)) {
+      // The lane's own 8 scores decide whether any row of the tile may
+      // raise (the row max exceeds the threshold exactly when one of its
+      // lanes' maxima does); only then is the row max formed.
+      const float lmx = fmaxf(fmaxf(fmaxf(sacc[0][mt][0], sacc[0][mt][1]),
+                                    fmaxf(sacc[0][mt][2], sacc[0][mt][3])),
+                              fmaxf(fmaxf(sacc[1][mt][0], sacc[1][mt][1]),
+                                    fmaxf(sacc[1][mt][2], sacc[1][mt][3])));
+      if (__builtin_amdgcn_ballot_w64(lmx * scale_log2 > m_run[mt] + kRescaleSlack)) {
+        const float m_tile = row_max4(lmx) * scale_log2;
+        const bool raise = m_tile > m_run[mt] + kRescaleSlack;
         const float m_new = raise ? m_tile : m_run[mt];
         const float alpha = exp2_hw(m_run[mt] - m_new);
         l_run[mt] *= alpha;
@@ -898,12 +900,13 @@ __global__ __launch_bounds__(NW * KP * 64, 1) void attn_wide_kernel(
   // row has seen no key), and the row sum as a 16-column MFMA accumulator
   // of P against a ones operand: every lane then holds its row's full sum,
   // taken over the same bf16-rounded p that multiply V.
-  float m_run[MTW], neg_m[MTW];
+  float m_run[MTW], neg_m[MTW], thr[MTW];  // thr = m_run + kRescaleSlack
   f32x4 lacc[MTW];
 #pragma unroll
   for (int j = 0; j < MTW; ++j) {
     m_run[j] = -INFINITY;
     neg_m[j] = 0.f;
+    thr[j] = -INFINITY;
     lacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   bf16x8 ones;
@@ -965,15 +968,16 @@ __global__ __launch_bounds__(NW * KP * 64, 1) void attn_wide_kernel(
     for (int j = 0; j < MTW; ++j) {
       if (j > 0 && j >= tcnt) break;
       bf16x8 pf;
-      float mx = fmaxf(fmaxf(fmaxf(sacc[0][j][0], sacc[0][j][1]),
-                             fmaxf(sacc[0][j][2], sacc[0][j][3])),
-                       fmaxf(fmaxf(sacc[1][j][0], sacc[1][j][1]),
-                             fmaxf(sacc[1][j][2], sacc[1][j][3])));
-      mx = row_max4(mx);
-      const float m_tile = mx * scale_log2;
-      const bool raise = m_tile > m_run[j] + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(raise)) {
+      // (the lanes' own maxima decide whether the row max is needed, as in
+      // the per-wave kernel above)
+      const float lmx = fmaxf(
+          fmaxf(fmaxf(fmaxf(sacc[0][j][0], sacc[0][j][1]), sacc[0][j][2]),
+                fmaxf(fmaxf(sacc[0][j][3], sacc[1][j][0]), sacc[1][j][1])),
+          fmaxf(sacc[1][j][2], sacc[1][j][3]));
+      if (__builtin_amdgcn_ballot_w64(lmx * scale_log2 > thr[j])) {
         // (a tile always holds a valid key, so m_tile and m_new are finite)
+        const float m_tile = row_max4(lmx) * scale_log2;
+        const bool raise = m_tile > thr[j];
         const float m_new = raise ? m_tile : m_run[j];
         const float alpha = exp2_hw(m_run[j] - m_new);
         lacc[j] *= alpha;
@@ -981,6 +985,7 @@ __global__ __launch_bounds__(NW * KP * 64, 1) void attn_wide_kernel(
         for (int nb = 0; nb < NB; ++nb) oacc[nb][j] *= alpha;
         m_run[j] = m_new;
         neg_m[j] = -m_new;
+        thr[j] = m_new + kRescaleSlack;
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
