@@ -35,7 +35,8 @@ namespace rv {
 namespace {
 
 // grid (cs, n + ni, B): rows < n are z rows of nodes, the rest y rows of
-// internal slots.  Also clears the sequence's arrival counter.
+// internal slots.  Also clears the sequence's arrival counter and empties its
+// draw-weight slots.
 template <bool VEC>
 __global__ __launch_bounds__(TPB) void tree_stats_kernel(const float* __restrict__ z,
                                                          const float* __restrict__ y, TreePlan tp,
