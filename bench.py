@@ -18,13 +18,16 @@ left in the 256 MB last-level cache.
 Prints one JSON line: steps/s (value: K steps timed with nothing else on the
 stream); per-kernel device times from HIP events recorded during a second,
 untimed pass over the same K steps, the attention's pair riding on its own
-dispatches (KV-stream = K+V bytes over that span); the history kernel's own
-duration from a third untimed pass in which its events ride on its own
-dispatch (the roofline's kernel, when the attention takes two launches);
-and the fp64 CPU oracle timed on the host as a reported baseline, which
-also checks one step of the library's outputs on the same inputs and
-reports their acceptance statistics.  A plain 2 GiB device copy is measured
-before the warm-up (context for the peak).
+dispatches (the KV-stream over that span is reported beside the main one);
+the history kernel's and the block + merge kernel's own durations from a
+third untimed pass in which each kernel's events ride on its own dispatch
+(KV-stream = K+V bytes over their sum; the history kernel is the
+roofline's kernel when the attention takes two launches); and the fp64 CPU
+oracle timed on the host as a reported baseline, which also checks one step
+of the library's outputs on the same inputs and reports their acceptance
+statistics.  A plain 2 GiB device copy is measured before the warm-up
+(context for the peak); its buffers stay in torch's cache, because a device
+free slows the streaming kernels for the rest of the process.
 """
 
 import argparse
