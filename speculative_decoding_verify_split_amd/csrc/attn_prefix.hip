@@ -26,8 +26,9 @@
 //     operand of the P V product, so P needs no shuffle.
 //   * Online softmax in fp32, base-2 units, with a lazily raised running
 //     max (raised only when a tile exceeds it by more than 8), so the fp32
-//     accumulators are rescaled only on rare tiles; row max/sum across the
-//     four lanes of a row use the gfx950 row-swap permutes.
+//     accumulators are rescaled only on rare tiles; each lane tests its own
+//     8 scores first, and only on those tiles is the row max taken across
+//     the four lanes of a row (gfx950 row-swap permutes, as the row sum).
 //   * V is staged per wave in LDS in its natural [key][d] layout (row pitch
 //     2d + 32 bytes) and read back transposed for the A operand of
 //     O^T += V^T P^T with ds_read_b64_tr_b16, two reads per 16 columns.
