@@ -20,6 +20,7 @@ constexpr int TPB = kVocabThreads;
 // landed yet and read it again.  A published slot holds (first weight, second
 // weight) in its (low, high) halves.
 constexpr uint64_t kSlotEmpty = ~0ull;
+constexpr uint64_t kSlotWaitTicks = 10000000;  // 100 ms of the 100 MHz clock
 
 __device__ __forceinline__ uint64_t pack_slot(float a, float b) {
   const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
@@ -228,13 +229,20 @@ __device__ void draw_from_chunks(const float* __restrict__ zrow, const float* __
                                  int32_t* __restrict__ out_slot, WF wfun) {
   __shared__ float sh_base;
   // Every chunk's slot store has been issued (publish_and_arrive); read each
-  // slot with device-scope atomic loads until its store has landed.
+  // slot with device-scope atomic loads until its store has landed.  The
+  // wait is also bounded in time (kSlotWaitTicks of the 100 MHz clock, far
+  // beyond any store's latency), so that the pass ends even if a store were
+  // ever lost; an empty slot then counts as no weight.
   auto chunk_w = [&](int i) {
     if (i >= cd) return make_float2(0.f, 0.f);
     uint64_t v = __hip_atomic_load(ws + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    while (v == kSlotEmpty) {
-      __builtin_amdgcn_s_sleep(1);
-      v = __hip_atomic_load(ws + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v == kSlotEmpty) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      do {
+        __builtin_amdgcn_s_sleep(1);
+        v = __hip_atomic_load(ws + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } while (v == kSlotEmpty && __builtin_amdgcn_s_memrealtime() - t0 < kSlotWaitTicks);
+      if (v == kSlotEmpty) v = 0;
     }
     return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
   };
