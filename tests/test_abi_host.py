@@ -490,3 +490,35 @@ def test_tree_accept_validation(lib):
     assert rv.rapid_tree_accept_workspace_size(1, 0, 1000) == 0
     # the size does not depend on the tree's shape, only on (B, n, V)
     assert rv.rapid_tree_accept_workspace_size(8, 32, 128256) > need
+
+
+def test_a_plain_c_program_builds_against_the_header_and_calls_the_library(tmp_path):
+    """The boundary is a C ABI: a C99 program that includes the header links
+    against the library and calls its host-only entry points (sizes, the
+    launch rule, status strings and a call that fails validation before any
+    HIP call), with no C++ or HIP headers involved."""
+    src = tmp_path / "abi.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <string.h>
+#include "rapid_verify.h"
+int main(void) {
+  if (rapid_accept_workspace_size(1, 10, 128256) == 0) return 1;
+  if (rapid_accept_workspace_size(0, 10, 128256) != 0) return 2;
+  if (spec_attn_verify_sync_size(2, 8) != 2 * 8 * 16) return 3;
+  if (rv_verify_single_launch(1, 8, 2, 5, 64, 8, 256) != 1) return 4;
+  if (rv_verify_single_launch(1, 32, 8, 11, 128, 32, 256) != 0) return 5;
+  if (strcmp(rv_status_string(RV_OK), rv_status_string(RV_ERR_NULL)) == 0) return 6;
+  if (rapid_accept(NULL, NULL, NULL, NULL, NULL, 1, 4, 100, 1.0f, 0.5f, NULL, NULL, NULL,
+                   NULL, NULL, 0, NULL) != RV_ERR_NULL) return 7;
+  printf("ok\n");
+  return 0;
+}
+''')
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(rv.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe), "-L", libdir, "-lrapid_verify",
+                    "-Wl,-rpath," + libdir], check=True, capture_output=True, text=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
