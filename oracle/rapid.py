@@ -71,12 +71,21 @@ def retrieval_augmented_target(z_row, y_row, T, eta):
     return p, q, softmax_ref(s)
 
 
-def tail_preserve_ref(p, p_hat, frac=0.1):
+def tail_preserve_ref(p, p_hat, frac=0.1, force=None):
     """Blog section 2.4's tail rule: p_hat_k := p_k where
-    p_hat_k < frac * max_j p_hat_j, then renormalise."""
+    p_hat_k < frac * max_j p_hat_j, then renormalise.
+
+    force: optional {entry id: keep} fixing the side of the threshold those
+    entries fall on.  The rule itself never needs it; a check of an
+    implementation in another precision uses it for entries that lie within
+    that precision's error of the threshold, where either side is correct.
+    """
     p = np.asarray(p, dtype=np.float64)
     p_hat = np.asarray(p_hat, dtype=np.float64)
     keep = p_hat >= frac * np.max(p_hat)
+    if force:
+        for k, v in force.items():
+            keep[int(k)] = bool(v)
     adj = np.where(keep, p_hat, p)
     return adj / np.sum(adj)
 
@@ -99,13 +108,16 @@ def inverse_cdf_ref(w, u):
     return k, C, W
 
 
-def rapid_accept_ref(z, y, draft, r, u, T, eta, tail_preserve=False, residual="p_hat"):
+def rapid_accept_ref(z, y, draft, r, u, T, eta, tail_preserve=False, residual="p_hat",
+                     tail_force=None):
     """One verify step of RAPID's acceptance, per sequence, step by step.
 
     tail_preserve  apply the tail rule to p_hat (and use it everywhere p_hat
                    is used: ratios, residual, p_hat output)
     residual       "p_hat": max(p_hat - q, 0) (the background rule with p
                    replaced by p_hat); "printed": max(p - min(p_hat, q), 0)
+    tail_force     optional {(b, t): {entry id: keep}}: the tail rule's
+                   classification of those entries, fixed (tail_preserve_ref)
 
     z     [B, gamma+1, V] target logits (row t scores the token after row t)
     y     [B, gamma, V]   draft logits; draft[b, t] was drawn from softmax(y[b,t]/T)
@@ -146,7 +158,8 @@ def rapid_accept_ref(z, y, draft, r, u, T, eta, tail_preserve=False, residual="p
                 raise ValueError("draft token id out of range")
             p, q, p_hat = retrieval_augmented_target(z[b, t], y[b, t], T, eta)
             if tail_preserve:
-                p_hat = tail_preserve_ref(p, p_hat)
+                force = tail_force.get((b, t)) if tail_force else None
+                p_hat = tail_preserve_ref(p, p_hat, force=force)
             p_hat_all[b, t] = p_hat
             q_rows.append(q)
             p_rows.append(p)

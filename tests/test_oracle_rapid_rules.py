@@ -48,6 +48,50 @@ def test_tail_rule_keeps_head_ratios_and_sums_to_one():
             np.testing.assert_allclose(s, s[0], rtol=1e-12)
 
 
+def test_tail_rule_forced_sides():
+    """The classification override: forcing each entry to the side the rule
+    puts it on changes nothing; moving one tail entry k into the head gives
+    p_hat_k (not p_k) for it, every other entry keeps its value relative to
+    the rest, and the row still sums to one (hand-checkable on 4 entries)."""
+    p = np.array([0.4, 0.3, 0.2, 0.1])
+    ph = np.array([0.70, 0.20, 0.06, 0.04])   # threshold 0.07: entries 2, 3 in the tail
+    base = tail_preserve_ref(p, ph)
+    np.testing.assert_array_equal(tail_preserve_ref(p, ph, force={0: True, 2: False}), base)
+    # by hand: kept (0.70, 0.20), tail from p (0.2, 0.1), sum 1.2
+    np.testing.assert_allclose(base, np.array([0.70, 0.20, 0.2, 0.1]) / 1.2, rtol=0, atol=1e-15)
+    moved = tail_preserve_ref(p, ph, force={2: True})
+    np.testing.assert_allclose(moved, np.array([0.70, 0.20, 0.06, 0.1]) / 1.06, rtol=0,
+                               atol=1e-15)
+    dropped = tail_preserve_ref(p, ph, force={1: False})
+    np.testing.assert_allclose(dropped, np.array([0.70, 0.3, 0.2, 0.1]) / 1.3, rtol=0, atol=1e-15)
+
+
+def test_tail_force_reaches_the_acceptance_step():
+    """rapid_accept_ref's tail_force is the same override, per (sequence,
+    row): an empty one leaves every output bit-identical, and forcing the
+    drafted token's entry changes that row's ratio exactly as the forced
+    rule says."""
+    g = np.random.default_rng(7)
+    V, gamma = 30, 3
+    z = g.standard_normal((1, gamma + 1, V)) * 3
+    y = z[:, :gamma] + g.standard_normal((1, gamma, V))
+    draft = g.integers(0, V, size=(1, gamma))
+    r = np.zeros((1, gamma))
+    u = g.random((1, gamma + 1))
+    a = rapid_accept_ref(z, y, draft, r, u, 1.0, 1.0, tail_preserve=True)
+    b = rapid_accept_ref(z, y, draft, r, u, 1.0, 1.0, tail_preserve=True, tail_force={})
+    for k in ("n_accept", "out_tokens", "ratio", "p_hat"):
+        np.testing.assert_array_equal(a[k], b[k])
+    x = int(draft[0, 1])
+    p, q, ph = retrieval_augmented_target(z[0, 1], y[0, 1], 1.0, 1.0)
+    side = bool(ph[x] >= 0.1 * ph.max())
+    c = rapid_accept_ref(z, y, draft, r, u, 1.0, 1.0, tail_preserve=True,
+                         tail_force={(0, 1): {x: not side}})
+    want = tail_preserve_ref(p, ph, force={x: not side})
+    assert c["ratio"][0, 1] == min(1.0, want[x] / q[x])
+    np.testing.assert_array_equal(c["ratio"][0, [0, 2]], a["ratio"][0, [0, 2]])
+
+
 def test_printed_residual_is_the_background_rule_when_eta_is_zero():
     """With eta = 0, p_hat = p and max(p - min(p, q), 0) = max(p - q, 0):
     the printed rule reduces to the background residual of section 2.1."""
