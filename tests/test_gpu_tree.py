@@ -78,6 +78,36 @@ def test_tree_random(case):
     _check_tree(vi, name)
 
 
+def _random_tree_cases(seed=4444, count=12):
+    """Seeded random draft trees within the library's limits: 1-64 nodes,
+    depth up to 12, V from 2 to 50257 (odd sizes take the scalar loads),
+    B up to 4, three temperatures and three eta."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for k in range(count):
+        n = int(rng.integers(1, 65))
+        depth = int(rng.integers(1, min(n, 12) + 1)) if n > 1 else 0
+        V = int(rng.choice([2, 3, 7, 1000, 4099, 32000, 50257]))
+        B = int(rng.integers(1, 5))
+        T = float(rng.choice([0.7, 1.0, 1.3]))
+        eta = float(rng.choice([0.0, 0.5, 1.5]))
+        cases.append((k, 5000 + k, B, n, depth, V, T, eta))
+    return cases
+
+
+RANDOM_TREES = _random_tree_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM_TREES, ids=["rt%d" % c[0] for c in RANDOM_TREES])
+def test_tree_random_shapes(case):
+    k, seed, B, n, depth, V, T, eta = case
+    parent = tree_parents(np.random.SeedSequence(seed), n, depth) if n > 1 else np.array([-1])
+    vi = make_tree_vocab(seed, B, parent, V, 3.0, 1.0, T, eta)
+    announce("rapid_tree_accept random rt%d: n=%d depth=%d V=%d B=%d T=%g eta=%g"
+             % (k, n, depth, V, B, T, eta))
+    _check_tree(vi, "rt%d" % k)
+
+
 def test_tree_star_forced_rejections():
     """A root with 12 children and uniforms near 1: children of ratio below 1
     are rejected in turn (11 residual passes); a sequence whose 12 children
