@@ -27,9 +27,9 @@ oracle timed on the host as a reported baseline, which also checks one step
 of the library's outputs on the same inputs and reports their acceptance
 statistics.  A plain 2 GiB device copy is measured before the warm-up
 (context for the peak); its buffers stay in torch's cache, because a device
-free slows the streaming kernels for the rest of the process.  For the same
-reason the HIP graphs reported beside the eager rate are captured without
-torch.cuda.graph(), which empties that cache first.
+free slows the streaming kernels by ~7% for about 30 ms per GiB freed.  For
+the same reason the HIP graphs reported beside the eager rate are captured
+without torch.cuda.graph(), which empties that cache first.
 """
 
 import argparse
@@ -282,8 +282,8 @@ def _copy_context(n_bytes=1 << 31, min_ms=0.0, reps=5):
     s = total_ms / 1e3 / done
     # The buffers go back to torch's cache, not to the driver: on this part
     # a device free (hipFree, as torch's empty_cache makes) leaves the
-    # streaming kernels ~6% slower for the rest of the process, so nothing is
-    # freed to the driver before the timed steps.
+    # streaming kernels ~7% slower for about 30 ms per GiB freed, so nothing
+    # is freed to the driver before the timed steps.
     del src, dst
     return {"bytes_copied": n_bytes, "copies": done, "GBps_read_plus_write": 2 * n_bytes / s / 1e9}
 
@@ -291,9 +291,9 @@ def _copy_context(n_bytes=1 << 31, min_ms=0.0, reps=5):
 def _capture_graph(fn):
     """fn's kernels captured into one HIP graph.  torch.cuda.graph() would
     first hand torch's cached device memory back to the driver
-    (empty_cache); a device free leaves the streaming kernels slower for the
-    rest of the process, so the capture is begun directly, on a side stream
-    of its own."""
+    (empty_cache); a device free leaves the streaming kernels slower for a
+    while (about 30 ms per GiB freed), so the capture is begun directly, on
+    a side stream of its own."""
     import torch
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
